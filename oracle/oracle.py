@@ -1,0 +1,358 @@
+"""Python face of the CPU oracle (prism_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: tests, the smoke check and the benchmark's
+CPU-baseline leg use this module; the product path never imports it.
+
+Every function follows one step of Prism's Algorithm 1 (paper.rainbus.top,
+section "方法步骤详情"; formulas as printed on xyznot.com/id, "Metode" 1-3):
+zone statistics -> indicator / volume / shape -> zone-aware re-layout and
+mean pooling -> block scores and Top-k U Top-p -> attention over the
+selected blocks.  Tensors are numpy arrays laid out [heads, T*H*W, D], with
+bf16 passed as its raw uint16 bit pattern.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "prism_oracle.c")
+
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C, no fast-math, no contraction)."""
+    if force or not os.path.exists(LIB_PATH) or (
+        os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH)
+    ):
+        tmp = LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, SRC_PATH, "-lm"])
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = ctypes.CDLL(LIB_PATH)
+        _lib.orc_exp2.restype = ctypes.c_float
+        _lib.orc_exp2.argtypes = [ctypes.c_float]
+        _lib.orc_nearest_shape.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        _lib.orc_lstar.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        _lib.orc_select_row.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p]
+        _lib.orc_shapes.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_float, ctypes.c_float, ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p]
+        _lib.orc_score_row.argtypes = [
+            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_void_p]
+        _lib.orc_quantize.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _dtype_code(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return 0
+    if x.dtype == np.uint16:
+        return 1
+    raise TypeError(f"oracle takes float32 or bf16-as-uint16 arrays, got {x.dtype}")
+
+
+# ---------------------------------------------------------------- shapes
+
+def candidates() -> np.ndarray:
+    """[16, 4] table of (bT, bH, bW, B): edges in {2,4,8}, product B."""
+    out = np.zeros((16, 4), np.int32)
+    n = lib().orc_candidates(_p(out))
+    return out[:n]
+
+
+def shape_id_of(bt: int, bh: int, bw: int) -> int:
+    for i, row in enumerate(candidates()):
+        if tuple(row[:3]) == (bt, bh, bw):
+            return i
+    raise ValueError(f"({bt},{bh},{bw}) is not a candidate shape")
+
+
+def lstar(g, B: int) -> np.ndarray:
+    g = np.ascontiguousarray(g, np.float32)
+    out = np.zeros(3, np.float64)
+    lib().orc_lstar(_p(g), B, _p(out))
+    return out
+
+
+def nearest_shape(g, B: int) -> int:
+    g = np.ascontiguousarray(g, np.float32)
+    return lib().orc_nearest_shape(_p(g), B)
+
+
+def exp2(x: float) -> float:
+    return lib().orc_exp2(float(x))
+
+
+# ---------------------------------------------------------------- config
+
+@dataclass
+class Config:
+    T: int
+    H: int
+    W: int
+    heads: int
+    head_dim: int
+    top_k: int = 16
+    top_k_frac: float = 0.0
+    top_p: float = 0.9
+    volume_mask: int = 7
+    fixed_shape: tuple = (0, 0, 0)
+    eps: float = 1e-4
+    tau128: float = 0.5
+    tau256: float = 0.25
+
+    @property
+    def N(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def Z(self) -> int:
+        return (self.T // 8) * (self.H // 8) * (self.W // 8)
+
+    def k_for(self, nblk: int) -> int:
+        """Top-k size: a block count, or ceil(frac * N_blk) when frac > 0."""
+        if self.top_k_frac > 0:
+            k = int(math.ceil(np.float64(np.float32(self.top_k_frac)) * nblk))
+        else:
+            k = self.top_k
+        return max(0, min(k, nblk))
+
+
+@dataclass
+class Plan:
+    cfg: Config
+    vstats: np.ndarray            # [heads, Z, 5]
+    astats: np.ndarray | None     # [Z, 4]
+    g: np.ndarray                 # [heads, Z, 3]
+    volume: np.ndarray            # [heads, Z]
+    shape_id: np.ndarray          # [heads, Z] uint8
+    blk_off: np.ndarray           # [heads + 1] int64
+    blk_start: np.ndarray         # [G] int32 (permuted row of the block's first token)
+    blk_len: np.ndarray           # [G] int32
+    perm: np.ndarray              # [heads, N] int32 permuted position -> token
+    qbar: np.ndarray              # [G, D] fp32
+    kbar: np.ndarray              # [G, D] fp32
+    qgrid: np.ndarray             # [G, D] fp32 (integers)
+    qexp: np.ndarray              # [G] int32
+    kgrid: np.ndarray
+    kexp: np.ndarray
+    rows: dict = field(default_factory=dict)   # (head, local block) -> selected local key ids
+
+    def nblk(self, h: int) -> int:
+        return int(self.blk_off[h + 1] - self.blk_off[h])
+
+
+def zone_stats(v: np.ndarray, cfg: Config) -> np.ndarray:
+    out = np.zeros((cfg.heads, cfg.Z, 5), np.float32)
+    rc = lib().orc_zone_stats(_p(v), _dtype_code(v), cfg.T, cfg.H, cfg.W, cfg.heads,
+                              cfg.head_dim, _p(out))
+    assert rc == 0
+    return out
+
+
+def audio_stats(a: np.ndarray, cfg: Config) -> np.ndarray:
+    a = np.ascontiguousarray(a, np.float32)
+    out = np.zeros((cfg.Z, 4), np.float32)
+    rc = lib().orc_audio_stats(_p(a), cfg.T, cfg.H, cfg.W, _p(out))
+    assert rc == 0
+    return out
+
+
+def shapes(vstats, astats, cfg: Config):
+    fixed = -1 if tuple(cfg.fixed_shape) == (0, 0, 0) else shape_id_of(*cfg.fixed_shape)
+    sid = np.zeros((cfg.heads, cfg.Z), np.uint8)
+    g = np.zeros((cfg.heads, cfg.Z, 3), np.float32)
+    vol = np.zeros((cfg.heads, cfg.Z), np.int32)
+    rc = lib().orc_shapes(_p(vstats), _p(astats), cfg.heads, cfg.Z, np.float32(cfg.eps),
+                          np.float32(cfg.tau128), np.float32(cfg.tau256), cfg.volume_mask,
+                          fixed, _p(sid), _p(g), _p(vol))
+    assert rc == 0
+    return sid, g, vol
+
+
+def block_table(shape_id: np.ndarray, cfg: Config):
+    cand = candidates()
+    G = int(sum(512 // cand[s, 3] for s in shape_id.reshape(-1)))
+    off = np.zeros(cfg.heads + 1, np.int64)
+    start = np.zeros(G, np.int32)
+    ln = np.zeros(G, np.int32)
+    lib().orc_block_table(_p(shape_id), cfg.heads, cfg.Z, _p(off), _p(start), _p(ln))
+    return off, start, ln
+
+
+def perm_map(shape_id: np.ndarray, cfg: Config) -> np.ndarray:
+    perm = np.zeros((cfg.heads, cfg.N), np.int32)
+    lib().orc_perm_map(_p(shape_id), cfg.T, cfg.H, cfg.W, cfg.heads, _p(perm))
+    return perm
+
+
+def pool(x: np.ndarray, shape_id, blk_off, cfg: Config) -> np.ndarray:
+    G = int(blk_off[-1])
+    out = np.zeros((G, cfg.head_dim), np.float32)
+    lib().orc_pool(_p(x), _dtype_code(x), cfg.T, cfg.H, cfg.W, cfg.heads, cfg.head_dim,
+                   _p(shape_id), _p(blk_off), _p(out))
+    return out
+
+
+def quantize(xbar: np.ndarray):
+    xbar = np.ascontiguousarray(xbar, np.float32)
+    q = np.zeros_like(xbar)
+    e = np.zeros(xbar.shape[0], np.int32)
+    lib().orc_quantize(_p(xbar), xbar.shape[0], xbar.shape[1], _p(q), _p(e))
+    return q, e
+
+
+def plan(q, k, v, av_norm, cfg: Config) -> Plan:
+    """Stages one to three up to the pooled, integer-grid block means."""
+    vs = zone_stats(v, cfg)
+    ast = None if av_norm is None else audio_stats(av_norm, cfg)
+    sid, g, vol = shapes(vs, ast, cfg)
+    off, start, ln = block_table(sid, cfg)
+    perm = perm_map(sid, cfg)
+    qbar = pool(q, sid, off, cfg)
+    kbar = pool(k, sid, off, cfg)
+    qg, qe = quantize(qbar)
+    kg, ke = quantize(kbar)
+    return Plan(cfg, vs, ast, g, vol, sid, off, start, ln, perm, qbar, kbar, qg, qe, kg, ke)
+
+
+def score_row(pl: Plan, h: int, i: int) -> np.ndarray:
+    """Block scores s_ij (fp32) of local query block i of head h."""
+    o, n = int(pl.blk_off[h]), pl.nblk(h)
+    s = np.zeros(n, np.float32)
+    qrow = np.ascontiguousarray(pl.qgrid[o + i])
+    kg = np.ascontiguousarray(pl.kgrid[o:o + n])
+    ke = np.ascontiguousarray(pl.kexp[o:o + n])
+    lib().orc_score_row(_p(qrow), int(pl.qexp[o + i]), _p(kg), _p(ke), n, pl.cfg.head_dim,
+                        _p(s))
+    return s
+
+
+def select_from_scores(s: np.ndarray, k: int, p: float) -> np.ndarray:
+    s = np.ascontiguousarray(s, np.float32)
+    out = np.zeros(max(1, s.shape[0]), np.int32)
+    cnt = lib().orc_select_row(_p(s), s.shape[0], k, np.float32(p), _p(out))
+    return out[:cnt].copy()
+
+
+def select_row(pl: Plan, h: int, i: int) -> np.ndarray:
+    key = (h, i)
+    if key not in pl.rows:
+        s = score_row(pl, h, i)
+        pl.rows[key] = select_from_scores(s, pl.cfg.k_for(pl.nblk(h)), pl.cfg.top_p)
+    return pl.rows[key]
+
+
+def select_all(pl: Plan, heads=None):
+    """Full CSR over the listed heads: (row_ptr [G+1] int64 over all blocks,
+    col_idx int32).  Rows of heads not listed are empty."""
+    heads = range(pl.cfg.heads) if heads is None else heads
+    G = int(pl.blk_off[-1])
+    counts = np.zeros(G, np.int64)
+    lists = {}
+    for h in heads:
+        for i in range(pl.nblk(h)):
+            r = select_row(pl, h, i)
+            lists[int(pl.blk_off[h]) + i] = r
+            counts[int(pl.blk_off[h]) + i] = len(r)
+    row_ptr = np.zeros(G + 1, np.int64)
+    np.cumsum(counts, out=row_ptr[1:])
+    col = np.zeros(int(row_ptr[-1]), np.int32)
+    for g, r in lists.items():
+        col[row_ptr[g]:row_ptr[g + 1]] = r
+    return row_ptr, col
+
+
+# ---------------------------------------------------------------- attention
+
+def _items(pl: Plan, items):
+    ih = np.array([h for h, _ in items], np.int32)
+    ib = np.array([b for _, b in items], np.int32)
+    sels = [select_row(pl, h, b) for h, b in items]
+    ptr = np.zeros(len(items) + 1, np.int64)
+    np.cumsum([len(s) for s in sels], out=ptr[1:])
+    idx = np.concatenate(sels).astype(np.int32) if sels else np.zeros(0, np.int32)
+    return ih, ib, ptr, np.ascontiguousarray(idx)
+
+
+def attn_fwd(q, k, v, pl: Plan, items):
+    """O and LSE for (head, local query block) items.
+    Returns o [n, 256, D] fp64 and lse [n, 256] (rows in permuted order)."""
+    cfg = pl.cfg
+    ih, ib, ptr, idx = _items(pl, items)
+    o = np.zeros((len(items), 256, cfg.head_dim), np.float64)
+    lse = np.zeros((len(items), 256), np.float64)
+    lib().orc_attn_fwd(_p(q), _p(k), _p(v), _dtype_code(q), ctypes.c_int64(cfg.N),
+                       cfg.head_dim, _p(pl.perm), _p(pl.blk_off), _p(pl.blk_start),
+                       _p(pl.blk_len), len(items), _p(ih), _p(ib), _p(ptr), _p(idx),
+                       _p(o), _p(lse))
+    return o, lse
+
+
+def attn_bwd_q(q, k, v, do, pl: Plan, items):
+    cfg = pl.cfg
+    ih, ib, ptr, idx = _items(pl, items)
+    dq = np.zeros((len(items), 256, cfg.head_dim), np.float64)
+    lib().orc_attn_bwd_q(_p(q), _p(k), _p(v), _p(do), _dtype_code(q), ctypes.c_int64(cfg.N),
+                         cfg.head_dim, _p(pl.perm), _p(pl.blk_off), _p(pl.blk_start),
+                         _p(pl.blk_len), len(items), _p(ih), _p(ib), _p(ptr), _p(idx),
+                         _p(dq))
+    return dq
+
+
+def attn_bwd_kv(q, k, v, do, pl: Plan, items):
+    """dK, dV for (head, local key block) items; needs every row of the
+    items' heads, so it selects those heads in full."""
+    cfg = pl.cfg
+    heads = sorted({h for h, _ in items})
+    row_ptr, col = select_all(pl, heads)
+    tq = []
+    for h, j in items:
+        o = int(pl.blk_off[h])
+        lst = [i for i in range(pl.nblk(h))
+               if np.any(col[row_ptr[o + i]:row_ptr[o + i + 1]] == j)]
+        tq.append(np.array(lst, np.int32))
+    tptr = np.zeros(len(items) + 1, np.int64)
+    np.cumsum([len(t) for t in tq], out=tptr[1:])
+    tidx = np.ascontiguousarray(np.concatenate(tq).astype(np.int32)) if tq else np.zeros(0, np.int32)
+    ih = np.array([h for h, _ in items], np.int32)
+    ib = np.array([b for _, b in items], np.int32)
+    dk = np.zeros((len(items), 256, cfg.head_dim), np.float64)
+    dv = np.zeros((len(items), 256, cfg.head_dim), np.float64)
+    lib().orc_attn_bwd_kv(_p(q), _p(k), _p(v), _p(do), _dtype_code(q), ctypes.c_int64(cfg.N),
+                          cfg.head_dim, _p(pl.perm), _p(pl.blk_off), _p(pl.blk_start),
+                          _p(pl.blk_len), _p(row_ptr), _p(col), len(items), _p(ih), _p(ib),
+                          _p(tptr), _p(tidx), _p(dk), _p(dv))
+    return dk, dv
+
+
+def tokens_of_block(pl: Plan, h: int, i: int) -> np.ndarray:
+    """Original token indices of local block i of head h, in permuted order."""
+    g = int(pl.blk_off[h]) + i
+    s, n = int(pl.blk_start[g]), int(pl.blk_len[g])
+    return pl.perm[h, s:s + n]

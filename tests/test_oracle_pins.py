@@ -1,0 +1,553 @@
+"""Pins of the CPU oracle against what the pages and plain mathematics fix,
+independently of the oracle's own code: closed forms, brute force with
+high-precision arithmetic, textbook attention, autograd and finite
+differences.  CPU only."""
+from decimal import Decimal, getcontext
+from fractions import Fraction
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------- candidate set
+
+def test_candidate_set_matches_pages(orc):
+    """paper.rainbus.top "核心方法": 16 candidates, each edge in {2,4,8},
+    product B in {64,128,256}."""
+    c = orc.candidates()
+    assert c.shape == (16, 4)
+    seen = set()
+    for bt, bh, bw, B in c:
+        assert {bt, bh, bw} <= {2, 4, 8}
+        assert bt * bh * bw == B
+        seen.add((bt, bh, bw))
+    assert len(seen) == 16
+    counts = {B: int((c[:, 3] == B).sum()) for B in (64, 128, 256)}
+    assert counts == {64: 7, 128: 6, 256: 3}
+    # every triple of edges with product in {64,128,256} is present
+    allt = {(a, b, d) for a in (2, 4, 8) for b in (2, 4, 8) for d in (2, 4, 8)
+            if a * b * d in (64, 128, 256)}
+    assert allt == seen
+    # id order: by volume, then lexicographic
+    keys = [(int(B), int(bt), int(bh), int(bw)) for bt, bh, bw, B in c]
+    assert keys == sorted(keys)
+
+
+# ----------------------------------------------------------- shape optimum
+
+def test_lstar_is_the_lagrange_optimum(orc):
+    """xyznot.com/id "Metode" 2: minimising sum_d g_d (b_d^2 - 1) under
+    prod b_d = B gives b*_d ~ g_d^(-1/2); l* is that optimum in log2 space."""
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        g = rng.uniform(1e-4, 2.0, 3).astype(np.float32)
+        for B in (64, 128, 256):
+            l = orc.lstar(g, B)
+            b = 2.0 ** l
+            assert abs(l.sum() - math.log2(B)) < 1e-12          # prod b = B
+            lag = g.astype(np.float64) * b * b                   # g_d b_d^2 equal
+            assert np.ptp(lag) < 1e-9 * lag.max()
+            # and it is a minimum of J on the constraint surface
+            J0 = float((g * (b * b - 1)).sum())
+            for _ in range(5):
+                dl = rng.normal(0, 0.05, 3)
+                dl -= dl.mean()
+                bb = 2.0 ** (l + dl)
+                assert float((g * (bb * bb - 1)).sum()) >= J0 - 1e-9
+
+
+def _nearest_decimal(g, B):
+    getcontext().prec = 60
+    ln2 = Decimal(2).ln()
+    lg = [Decimal(float(x)).ln() / ln2 for x in g]
+    S = Decimal(int(math.log2(B)))
+    c = (S + (lg[0] + lg[1] + lg[2]) / 2) / 3
+    ls = [-lg[d] / 2 + c for d in range(3)]
+    best, bestd = None, None
+    from oracle import oracle as O
+    for i, (bt, bh, bw, BB) in enumerate(O.candidates()):
+        if BB != B:
+            continue
+        e = [Decimal(int(math.log2(x))) for x in (bt, bh, bw)]
+        dist = sum((ls[d] - e[d]) ** 2 for d in range(3))
+        if bestd is None or dist < bestd - Decimal(10) ** -40:
+            best, bestd = i, dist
+    return best
+
+
+def test_nearest_shape_brute_force_high_precision(orc):
+    """Nearest candidate to l* by Euclidean distance, computed with 60-digit
+    decimal logarithms, against the oracle's exact product-form test."""
+    rng = np.random.default_rng(1)
+    gs = [rng.uniform(1e-4, 2.0, 3) for _ in range(300)]
+    gs += [np.exp(rng.uniform(-9, 0.7, 3)) for _ in range(300)]
+    for g in gs:
+        g = np.asarray(g, np.float32)
+        for B in (64, 128, 256):
+            assert orc.nearest_shape(g, B) == _nearest_decimal(g, B), (g, B)
+
+
+def test_golden_shape_examples(orc):
+    path = os.path.join(GOLDEN, "shape_examples.txt")
+    n = 0
+    for line in open(path):
+        if not line.strip() or line.startswith("#"):
+            continue
+        f = line.split()
+        g = np.array([float(Fraction(x)) for x in f[:3]], np.float32)
+        B = int(f[3])
+        want = tuple(int(x) for x in f[4:7])
+        got = tuple(int(x) for x in orc.candidates()[orc.nearest_shape(g, B)][:3])
+        assert got == want, line
+        n += 1
+    assert n >= 8
+
+
+# ----------------------------------------------------------- zone statistics
+
+def _ref_stats64(x):
+    """fp64 plain definitions for one zone x[t][y][w][c]."""
+    x = x.astype(np.float64)
+    out = []
+    for ax in range(3):
+        other = tuple(a for a in range(3) if a != ax)
+        prof = x.mean(axis=other)                     # [8, C]
+        out.append(((prof - prof.mean(axis=0)) ** 2).mean(axis=0).mean())
+    sv = x.var(axis=(1, 2)).mean(axis=0).mean()       # per-frame spatial variance
+    d = x[1:] - x[:-1]                                # [7, 8, 8, C]
+    tv = d.reshape(-1, x.shape[-1]).var(axis=0).mean()
+    out += [sv, tv]
+    return np.array(out)
+
+
+def _zone_tensor(x_zone, D, heads=1):
+    """place one 8x8x8xD zone into a [heads, 512, D] tensor (T=H=W=8)."""
+    v = np.zeros((heads, 512, D), np.float32)
+    for h in range(heads):
+        v[h] = x_zone.reshape(512, D)
+    return v
+
+
+def _cfg(orc, T, H, W, heads, D, **kw):
+    return orc.Config(T=T, H=H, W=W, heads=heads, head_dim=D, **kw)
+
+
+def test_zone_stats_against_plain_definitions(orc):
+    rng = np.random.default_rng(2)
+    for D in (64, 128):
+        x = rng.normal(size=(8, 8, 8, D)).astype(np.float32)
+        x += np.sin(np.arange(8) * 0.9)[:, None, None, None].astype(np.float32)
+        st = orc.zone_stats(_zone_tensor(x, D), _cfg(orc, 8, 8, 8, 1, D))[0, 0]
+        ref = _ref_stats64(x)
+        np.testing.assert_allclose(st, ref, rtol=2e-5, atol=1e-7)
+
+
+def test_zone_stats_axis_only_variation(orc):
+    """V varying along one axis only: the other two directional variances
+    vanish, r = unit vector; V varying only in time has zero spatial variance."""
+    D = 64
+    rng = np.random.default_rng(3)
+    # dyadic values with few bits: every partial sum below is exact
+    prof = (np.round(rng.normal(size=(8, D)) * 256) / 256).astype(np.float32)
+    for ax in range(3):
+        shape = [1, 1, 1, D]
+        shape[ax] = 8
+        x = np.broadcast_to(prof.reshape(shape), (8, 8, 8, D)).copy()
+        st = orc.zone_stats(_zone_tensor(x, D), _cfg(orc, 8, 8, 8, 1, D))[0, 0]
+        for other in range(3):
+            if other != ax:
+                assert st[other] == 0.0
+        assert st[ax] > 0
+        sid, g, _ = orc.shapes(st.reshape(1, 1, 5), None, _cfg(orc, 8, 8, 8, 1, D))
+        r = g[0, 0] - np.float32(1e-4)
+        np.testing.assert_allclose(r, np.eye(3)[ax], atol=1e-7)
+        if ax == 0:
+            assert st[3] == 0.0      # each frame constant: no spatial variance
+        else:
+            assert st[4] == 0.0      # nothing changes in time
+
+
+def test_zone_stats_constant_zone(orc):
+    D = 128
+    x = np.full((8, 8, 8, D), 0.37, np.float32)
+    st = orc.zone_stats(_zone_tensor(x, D), _cfg(orc, 8, 8, 8, 1, D))[0, 0]
+    assert np.all(st == 0.0)
+    _, g, _ = orc.shapes(st.reshape(1, 1, 5), None, _cfg(orc, 8, 8, 8, 1, D))
+    np.testing.assert_array_equal(g[0, 0], np.float32(1 / 3) + np.float32(1e-4))
+
+
+def test_zone_stats_linear_motion(orc):
+    """x = a*t + b(y,w): frame differences are constant, so their variance is 0."""
+    D = 64
+    rng = np.random.default_rng(4)
+    b = rng.normal(size=(1, 8, 8, D)).astype(np.float32)
+    a = np.float32(0.5)
+    x = (a * np.arange(8, dtype=np.float32)[:, None, None, None] + b).astype(np.float32)
+    st = orc.zone_stats(_zone_tensor(x, D), _cfg(orc, 8, 8, 8, 1, D))[0, 0]
+    assert st[4] < 1e-10
+    np.testing.assert_allclose(st[3], b.astype(np.float64).var(axis=(1, 2)).mean(), rtol=1e-5)
+
+
+def test_zone_stats_bf16_matches_f32_of_same_values(orc):
+    """The bf16 load path is exact: stats of bf16 bits == stats of their fp32 value."""
+    rng = np.random.default_rng(5)
+    x = torch.from_numpy(rng.normal(size=(2, 1024, 128)).astype(np.float32)).bfloat16()
+    cfg = _cfg(orc, 8, 8, 16, 2, 128)
+    a = orc.zone_stats(x.view(torch.int16).numpy().view(np.uint16), cfg)
+    b = orc.zone_stats(x.float().numpy(), cfg)
+    np.testing.assert_array_equal(a, b)
+
+
+# ----------------------------------------------------------- audio, g, volume
+
+def test_audio_terms(orc):
+    """xyznot.com/id "Metode" 1: g_d = r_d + abar * vhat_d + eps, abar in [0,1]
+    (zone mean over max zone mean); a silent zone contributes nothing and the
+    first layer (no cached norms) uses g = r + eps."""
+    T, H, W, D = 8, 8, 16, 64
+    cfg = _cfg(orc, T, H, W, 1, D)
+    rng = np.random.default_rng(6)
+    v = rng.normal(size=(1, T * H * W, D)).astype(np.float32)
+    vs = orc.zone_stats(v, cfg)
+    a = np.zeros((T, H, W), np.float32)
+    a[:, :, 8:] = (np.arange(1, 9, dtype=np.float32) / 16)[:, None, None]  # zone 1: T only
+    ast = orc.audio_stats(a.reshape(-1), cfg)
+    assert ast[0, 3] == 0.0
+    assert ast[1, 3] == 0.28125
+    assert ast[1, 1] == 0.0 and ast[1, 2] == 0.0 and ast[1, 0] > 0
+    _, g_first, _ = orc.shapes(vs, None, cfg)
+    _, g, _ = orc.shapes(vs, ast, cfg)
+    np.testing.assert_array_equal(g[0, 0], g_first[0, 0])          # silent zone
+    r = g_first[0, 1] - np.float32(1e-4)
+    want = (r + np.float32(1.0) * np.array([1, 0, 0], np.float32)) + np.float32(1e-4)
+    np.testing.assert_allclose(g[0, 1], want, rtol=1e-6)
+    assert g[0, 1, 0] > g_first[0, 1, 0]
+
+
+def _vstats_with_rho(rhos):
+    vs = np.zeros((1, len(rhos), 5), np.float32)
+    vs[0, :, 0] = 1.0
+    vs[0, :, 3] = np.asarray(rhos, np.float32)
+    return vs
+
+
+def test_volume_tiers(orc):
+    """paper.rainbus.top stage one: rho = (spatial + frame-difference variance)
+    normalised by its maximum; tau_128 = 0.5, tau_256 = 0.25: dense zones get
+    small blocks."""
+    rh = [1.0, 0.5, 0.49, 0.25, 0.2499, 0.0]
+    vs = _vstats_with_rho(rh)
+    cfg = _cfg(orc, 8, 8, 8 * len(rh), 1, 64)
+    _, _, vol = orc.shapes(vs, None, cfg)
+    assert list(vol[0]) == [64, 64, 128, 128, 256, 256]
+    _, _, vol = orc.shapes(_vstats_with_rho([0.0] * 3), None, _cfg(orc, 8, 8, 24, 1, 64))
+    assert list(vol[0]) == [256] * 3
+    cfg1 = _cfg(orc, 8, 8, 8 * len(rh), 1, 64, volume_mask=1)
+    _, _, vol = orc.shapes(vs, None, cfg1)
+    assert list(vol[0]) == [64] * len(rh)
+    cfg5 = _cfg(orc, 8, 8, 8 * len(rh), 1, 64, volume_mask=5)      # 64 and 256 only
+    _, _, vol = orc.shapes(vs, None, cfg5)
+    assert list(vol[0]) == [64, 64, 64, 64, 256, 256]
+
+
+def test_fixed_shape_override(orc):
+    rng = np.random.default_rng(7)
+    cfg = _cfg(orc, 8, 16, 16, 2, 64, fixed_shape=(4, 4, 8))
+    v = rng.normal(size=(2, cfg.N, 64)).astype(np.float32)
+    sid, _, vol = orc.shapes(orc.zone_stats(v, cfg), None, cfg)
+    assert np.all(sid == orc.shape_id_of(4, 4, 8)) and np.all(vol == 128)
+
+
+# ----------------------------------------------------------- permutation, pooling
+
+def test_permutation_is_zone_block_contiguous(orc):
+    rng = np.random.default_rng(8)
+    cfg = _cfg(orc, 16, 16, 24, 2, 64)
+    sid = rng.integers(0, 16, size=(cfg.heads, cfg.Z)).astype(np.uint8)
+    perm = orc.perm_map(sid, cfg)
+    off, start, ln = orc.block_table(sid, cfg)
+    cand = orc.candidates()
+    for h in range(cfg.heads):
+        assert np.array_equal(np.sort(perm[h]), np.arange(cfg.N))         # bijection
+        t = perm[h] // (cfg.H * cfg.W)
+        y = (perm[h] // cfg.W) % cfg.H
+        w = perm[h] % cfg.W
+        zone = (t // 8) * (cfg.H // 8) * (cfg.W // 8) + (y // 8) * (cfg.W // 8) + w // 8
+        assert np.array_equal(zone, np.repeat(np.arange(cfg.Z), 512))    # zone m -> rows 512m..
+        for g in range(int(off[h]), int(off[h + 1])):
+            s, n = start[g], ln[g]
+            m = s // 512
+            bt, bh, bw, B = cand[sid[h, m]]
+            assert n == B
+            tt, yy, ww = t[s:s + n], y[s:s + n], w[s:s + n]
+            # an axis-aligned box of the zone's shape, in raster order
+            assert (tt.max() - tt.min() + 1, yy.max() - yy.min() + 1,
+                    ww.max() - ww.min() + 1) == (bt, bh, bw)
+            assert tt.min() % bt == 0 and yy.min() % bh == 0 and ww.min() % bw == 0
+            assert np.all(np.diff(tt * 10000 + yy * 100 + ww) > 0)
+    assert int(off[-1]) == sum(512 // cand[s, 3] for s in sid.reshape(-1))
+
+
+def test_pooling_is_block_mean(orc):
+    rng = np.random.default_rng(9)
+    cfg = _cfg(orc, 8, 16, 16, 2, 128)
+    x = rng.normal(size=(2, cfg.N, 128)).astype(np.float32)
+    sid = rng.integers(0, 16, size=(2, cfg.Z)).astype(np.uint8)
+    off, start, ln = orc.block_table(sid, cfg)
+    perm = orc.perm_map(sid, cfg)
+    xb = orc.pool(x, sid, off, cfg)
+    for h in range(2):
+        for g in range(int(off[h]), int(off[h + 1])):
+            toks = perm[h, start[g]:start[g] + ln[g]]
+            ref = x[h, toks].astype(np.float64).mean(axis=0)
+            np.testing.assert_allclose(xb[g], ref, rtol=1e-5, atol=2e-6)
+
+
+def test_integer_grid_quantisation(orc):
+    rng = np.random.default_rng(10)
+    x = (rng.normal(size=(50, 128)) * np.exp(rng.uniform(-8, 3, (50, 1)))).astype(np.float32)
+    x[3] = 0
+    q, e = orc.quantize(x)
+    assert np.all(q == np.round(q)) and np.abs(q).max() <= 256
+    for i in range(50):
+        if i == 3:
+            assert e[i] == 0 and np.all(q[i] == 0)
+            continue
+        assert 128 <= np.abs(q[i]).max() <= 256
+        err = np.abs(x[i].astype(np.float64) - q[i] * 2.0 ** e[i])
+        assert err.max() <= 2.0 ** (e[i] - 1)
+
+
+def test_block_scores(orc):
+    """s_ij = Qbar_i . Kbar_j / sqrt(D) (paper.rainbus.top stage three), on
+    the integer grid: within the grid's rounding of the fp64 product."""
+    rng = np.random.default_rng(11)
+    D = 128
+    qb = rng.normal(size=(1, D)).astype(np.float32)
+    kb = rng.normal(size=(40, D)).astype(np.float32)
+    qg, qe = orc.quantize(qb)
+    kg, ke = orc.quantize(kb)
+    from oracle.oracle import _p, lib
+    s = np.zeros(40, np.float32)
+    lib().orc_score_row(_p(np.ascontiguousarray(qg[0])), int(qe[0]), _p(kg), _p(ke), 40, D, _p(s))
+    ref = (kb.astype(np.float64) @ qb[0].astype(np.float64)) / math.sqrt(D)
+    bound = (np.abs(qb).max() * 2.0 ** -8 * np.abs(kb).sum(1) +
+             np.abs(kb).max(1) * 2.0 ** -8 * np.abs(qb).sum()) / math.sqrt(D)
+    assert np.all(np.abs(s - ref) <= bound * 1.01 + 1e-6)
+
+
+# ----------------------------------------------------------- selection
+
+def test_exp2_accuracy(orc):
+    xs = np.linspace(-40, 0, 4001, dtype=np.float32)
+    for x in xs:
+        y = orc.exp2(float(x))
+        ref = 2.0 ** float(x)
+        assert abs(y - ref) <= 3 * np.spacing(np.float32(ref)), (x, y, ref)
+    assert orc.exp2(0.0) == 1.0
+
+
+def _select_ref(s, k, p):
+    """fp64 reference of TopK U TopP with ties by lower index; returns the set
+    and whether the Top-p cut is within 1e-9 of p (ambiguous in fixed point)."""
+    n = len(s)
+    order = sorted(range(n), key=lambda j: (-float(s[j]), j))
+    k = min(max(k, 0), n)
+    if p >= 1:
+        return set(range(n)), False
+    if p <= 0:
+        return set(order[:k]), False
+    sd = np.array([float(s[j]) for j in order])
+    w = np.exp(sd - sd[0])
+    cum = np.cumsum(w) / w.sum()
+    L = int(np.searchsorted(cum, p - 1e-15) + 1)
+    ambiguous = np.any(np.abs(cum - p) < 1e-9)
+    return set(order[:max(k, L)]), ambiguous
+
+
+def test_selection_brute_force(orc):
+    rng = np.random.default_rng(12)
+    checked = 0
+    for trial in range(400):
+        n = int(rng.integers(1, 300))
+        s = (rng.normal(size=n) * rng.uniform(0.1, 8)).astype(np.float32)
+        if trial % 5 == 0:
+            s = np.round(s * 2) / 2           # many exact ties
+        k = int(rng.integers(0, 20))
+        p = float(np.float32(rng.choice([0.0, 0.2, 0.5, 0.9, 0.99, 1.0, rng.uniform()])))
+        got = orc.select_from_scores(s, k, p)
+        assert np.all(np.diff(got) > 0)               # ascending, unique
+        want, amb = _select_ref(s, k, p)
+        if not amb:
+            assert set(got.tolist()) == want
+            checked += 1
+        # invariants that hold regardless
+        kk = min(k, n)
+        order = sorted(range(n), key=lambda j: (-float(s[j]), j))
+        assert set(order[:kk]) <= set(got.tolist())   # Top-k contained
+        if 0 < p < 1:
+            sd = np.array([float(x) for x in s], np.float64)
+            P = np.exp(sd - sd.max())
+            P /= P.sum()
+            assert P[got].sum() >= p - 1e-6          # mass >= p
+            # prefix property: selected = first |S| of the order
+            assert set(order[:len(got)]) == set(got.tolist())
+    assert checked > 300
+
+
+def test_selection_p1_selects_all_and_p0_is_topk(orc):
+    s = np.array([0.3, -1.0, 2.0, 2.0, 0.1], np.float32)
+    assert orc.select_from_scores(s, 2, 1.0).tolist() == [0, 1, 2, 3, 4]
+    assert orc.select_from_scores(s, 2, 0.0).tolist() == [2, 3]
+    assert orc.select_from_scores(s, 1, 0.0).tolist() == [2]     # tie -> lower index
+    assert orc.select_from_scores(s, 99, 0.0).tolist() == [0, 1, 2, 3, 4]
+
+
+# ----------------------------------------------------------- attention
+
+def _tiny(orc, T=8, H=8, W=16, heads=2, D=64, seed=13, **kw):
+    rng = np.random.default_rng(seed)
+    cfg = _cfg(orc, T, H, W, heads, D, **kw)
+    q = rng.normal(size=(heads, cfg.N, D)).astype(np.float32)
+    k = rng.normal(size=(heads, cfg.N, D)).astype(np.float32)
+    v = rng.normal(size=(heads, cfg.N, D)).astype(np.float32)
+    do = rng.normal(size=(heads, cfg.N, D)).astype(np.float32)
+    a = rng.uniform(size=cfg.N).astype(np.float32)
+    pl = orc.plan(q, k, v, a, cfg)
+    return cfg, q, k, v, do, pl
+
+
+def _all_items(pl):
+    return [(h, i) for h in range(pl.cfg.heads) for i in range(pl.nblk(h))]
+
+
+def _scatter(pl, items, arr):
+    """rows of per-item outputs [n, 256, ...] back to [heads, N, ...]."""
+    from oracle import oracle as O
+    out = np.zeros((pl.cfg.heads, pl.cfg.N) + arr.shape[2:], arr.dtype)
+    for it, (h, i) in enumerate(items):
+        toks = O.tokens_of_block(pl, h, i)
+        out[h, toks] = arr[it, :len(toks)]
+    return out
+
+
+def test_dense_limit_equals_textbook_attention(orc):
+    """Top-p = 1 selects every block: the result is plain softmax attention."""
+    cfg, q, k, v, _, pl = _tiny(orc, top_p=1.0, top_k=1)
+    items = _all_items(pl)
+    o, lse = orc.attn_fwd(q, k, v, pl, items)
+    O = _scatter(pl, items, o)
+    L = _scatter(pl, items, lse)
+    for h in range(cfg.heads):
+        s = q[h].astype(np.float64) @ k[h].astype(np.float64).T / math.sqrt(cfg.head_dim)
+        ref = torch.softmax(torch.from_numpy(s), dim=-1).numpy() @ v[h].astype(np.float64)
+        np.testing.assert_allclose(O[h], ref, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(L[h], np.log(np.exp(s - s.max(1, keepdims=True)).sum(1))
+                                   + s.max(1), rtol=1e-12)
+
+
+def test_sparse_equals_masked_dense_attention(orc):
+    """Attention over S_i equals dense softmax attention with every key outside
+    the selected blocks masked out (explicit N x N token mask)."""
+    cfg, q, k, v, _, pl = _tiny(orc, top_k=2, top_p=0.3)
+    items = _all_items(pl)
+    o, _ = orc.attn_fwd(q, k, v, pl, items)
+    O = _scatter(pl, items, o)
+    for h in range(cfg.heads):
+        mask = np.zeros((cfg.N, cfg.N), bool)
+        for i in range(pl.nblk(h)):
+            qt = orc.tokens_of_block(pl, h, i)
+            for j in orc.select_row(pl, h, i):
+                mask[np.ix_(qt, orc.tokens_of_block(pl, h, j))] = True
+        assert mask.mean() < 0.9
+        s = q[h].astype(np.float64) @ k[h].astype(np.float64).T / math.sqrt(cfg.head_dim)
+        s[~mask] = -np.inf
+        ref = torch.softmax(torch.from_numpy(s), dim=-1).numpy() @ v[h].astype(np.float64)
+        np.testing.assert_allclose(O[h], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_rows_sum_to_one(orc):
+    cfg, q, k, _, _, pl = _tiny(orc, top_k=3, top_p=0.5)
+    ones = np.ones_like(q)
+    items = _all_items(pl)
+    o, _ = orc.attn_fwd(q, k, ones, pl, items)
+    for it, (h, i) in enumerate(items):
+        n = len(orc.tokens_of_block(pl, h, i))
+        np.testing.assert_allclose(o[it, :n], 1.0, rtol=1e-12)
+
+
+def _loss_grads_torch(q, k, v, do, pl, cfg):
+    """Masked dense attention in fp64 torch autograd: L = sum(O * dO)."""
+    grads = []
+    for h in range(cfg.heads):
+        mask = np.zeros((cfg.N, cfg.N), bool)
+        from oracle import oracle as O
+        for i in range(pl.nblk(h)):
+            qt = O.tokens_of_block(pl, h, i)
+            for j in O.select_row(pl, h, i):
+                mask[np.ix_(qt, O.tokens_of_block(pl, h, j))] = True
+        Q = torch.tensor(q[h], dtype=torch.float64, requires_grad=True)
+        K = torch.tensor(k[h], dtype=torch.float64, requires_grad=True)
+        V = torch.tensor(v[h], dtype=torch.float64, requires_grad=True)
+        s = Q @ K.T / math.sqrt(cfg.head_dim)
+        s = s.masked_fill(~torch.from_numpy(mask), float("-inf"))
+        out = torch.softmax(s, -1) @ V
+        (out * torch.tensor(do[h], dtype=torch.float64)).sum().backward()
+        grads.append((Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()))
+    return grads
+
+
+def test_backward_matches_autograd_and_invariants(orc):
+    """paper.rainbus.top "技术新颖性": the plan is detached, gradients flow only
+    through attention on the selected blocks."""
+    cfg, q, k, v, do, pl = _tiny(orc, top_k=2, top_p=0.3)
+    items = _all_items(pl)
+    dq = _scatter(pl, items, orc.attn_bwd_q(q, k, v, do, pl, items))
+    dk_i, dv_i = orc.attn_bwd_kv(q, k, v, do, pl, items)
+    dk = _scatter(pl, items, dk_i)
+    dv = _scatter(pl, items, dv_i)
+    ref = _loss_grads_torch(q, k, v, do, pl, cfg)
+    for h in range(cfg.heads):
+        np.testing.assert_allclose(dq[h], ref[h][0], rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(dk[h], ref[h][1], rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(dv[h], ref[h][2], rtol=1e-9, atol=1e-11)
+        assert np.abs(dk[h].sum(axis=0)).max() < 1e-9      # sum_m dK_m = 0
+    # key blocks nobody selected get exactly zero gradient
+    for h in range(cfg.heads):
+        chosen = set()
+        for i in range(pl.nblk(h)):
+            chosen |= set(orc.select_row(pl, h, i).tolist())
+        for j in set(range(pl.nblk(h))) - chosen:
+            toks = orc.tokens_of_block(pl, h, j)
+            assert np.all(dk[h, toks] == 0) and np.all(dv[h, toks] == 0)
+
+
+def test_backward_finite_differences(orc):
+    cfg, q, k, v, do, pl = _tiny(orc, T=8, H=8, W=8, heads=1, D=64, top_k=2, top_p=0.4,
+                                 seed=21)
+    items = _all_items(pl)
+    dq = _scatter(pl, items, orc.attn_bwd_q(q, k, v, do, pl, items))
+    dk_i, dv_i = orc.attn_bwd_kv(q, k, v, do, pl, items)
+    dk, dv = _scatter(pl, items, dk_i), _scatter(pl, items, dv_i)
+
+    def loss(qq, kk, vv):
+        o, _ = orc.attn_fwd(qq, kk, vv, pl, items)
+        return float((_scatter(pl, items, o) * do.astype(np.float64)).sum())
+
+    rng = np.random.default_rng(22)
+    hstep = 1e-2
+    for which, grad in (("q", dq), ("k", dk), ("v", dv)):
+        for _ in range(4):
+            n, c = int(rng.integers(cfg.N)), int(rng.integers(cfg.head_dim))
+            args = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+            args[which][0, n, c] += hstep
+            lp = loss(args["q"], args["k"], args["v"])
+            args[which][0, n, c] -= 2 * hstep
+            lm = loss(args["q"], args["k"], args["v"])
+            fd = (lp - lm) / (2 * hstep)
+            assert abs(fd - grad[0, n, c]) <= 2e-3 * max(1.0, abs(fd)), (which, n, c)
