@@ -1,0 +1,9 @@
+"""MI355X (gfx950) implementation of Prism's dynamic block-sparse video
+self-attention: zone statistics, content-adaptive block shapes, zone-aware
+re-layout, Top-k U Top-p block selection and sparse attention forward and
+backward, behind the C ABI of include/prism.h."""
+from .api import (Plan, attn_bwd, attn_fwd, block_scores, candidate, make_config, plan,
+                  workspace_bytes)
+
+__all__ = ["Plan", "plan", "attn_fwd", "attn_bwd", "block_scores", "candidate",
+           "make_config", "workspace_bytes"]

@@ -1,0 +1,182 @@
+"""Python binding of the Prism sparse-attention library (include/prism.h).
+
+Argument marshalling only: torch tensors supply device memory and the HIP
+stream; every step of the plan and of attention runs in libprism.so.
+
+    plan = prism.plan(q, k, v, av_norm, T=..., H=..., W=..., top_k=16, top_p=0.9)
+    o, lse = prism.attn_fwd(plan, q, k, v)
+    dq, dk, dv = prism.attn_bwd(plan, q, k, v, o, lse, do)
+
+Tensors are [heads, T*H*W, head_dim] (token n = (t*H + h)*W + w), bf16 or fp32,
+contiguous, on one GPU; av_norm is [T*H*W] float32 or None (first layer).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _native as nat
+
+_NP = {
+    "zone_stats": np.float32, "audio_stats": np.float32, "shape_id": np.uint8,
+    "blk_off": np.int64, "blk_start": np.int32, "qbar": np.float32, "kbar": np.float32,
+    "qexp": np.int32, "kexp": np.int32, "row_ptr": np.int64, "col_idx": np.int32,
+    "colt_ptr": np.int64, "colt_idx": np.int32, "perm": np.int32, "qgrid": np.uint16,
+    "kgrid": np.uint16,
+}
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def make_config(T, H, W, heads, head_dim, dtype, *, top_k=16, top_k_frac=0.0, top_p=0.9,
+                volume_mask=7, fixed_shape=(0, 0, 0), eps=1e-4, tau128=0.5, tau256=0.25,
+                need_backward=True) -> nat.PrismConfig:
+    c = nat.PrismConfig()
+    nat.lib().prism_config_default(ctypes.byref(c))
+    c.T, c.H, c.W, c.heads, c.head_dim = T, H, W, heads, head_dim
+    c.dtype = nat.PRISM_BF16 if dtype == torch.bfloat16 else nat.PRISM_F32
+    c.top_k, c.top_k_frac, c.top_p = int(top_k), float(top_k_frac), float(top_p)
+    c.volume_mask = int(volume_mask)
+    for i in range(3):
+        c.fixed_shape[i] = int(fixed_shape[i])
+    c.eps, c.tau128, c.tau256 = float(eps), float(tau128), float(tau256)
+    c.need_backward = 1 if need_backward else 0
+    return c
+
+
+def workspace_bytes(cfg: nat.PrismConfig, nnz_capacity: int) -> int:
+    n = ctypes.c_size_t()
+    nat.check(nat.lib().prism_plan_workspace_size(ctypes.byref(cfg), int(nnz_capacity),
+                                                  ctypes.byref(n)), "prism_plan_workspace_size")
+    return n.value
+
+
+class Plan:
+    """Owns the plan handle and the device workspace it points into."""
+
+    def __init__(self, handle, cfg, workspace, nnz, q, k, v):
+        self.handle = handle
+        self.cfg = cfg
+        self.workspace = workspace
+        self.nnz = nnz
+        self.device = q.device
+        self._k, self._v = k, v  # kept alive: the plan holds their permuted copies
+
+    def close(self):
+        if self.handle:
+            nat.lib().prism_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def export(self, name: str) -> np.ndarray:
+        which = nat.ARRAYS[name]
+        n = ctypes.c_size_t()
+        nat.check(nat.lib().prism_plan_array_bytes(self.handle, which, ctypes.byref(n)),
+                  "prism_plan_array_bytes")
+        out = np.empty(max(1, n.value // np.dtype(_NP[name]).itemsize), _NP[name])
+        nat.check(nat.lib().prism_plan_export(self.handle, which, out.ctypes.data_as(
+            ctypes.c_void_p), out.nbytes, _stream(self.device)), "prism_plan_export")
+        return out[: n.value // np.dtype(_NP[name]).itemsize]
+
+    def info(self) -> dict:
+        inf = nat.PrismPlanInfo()
+        nat.check(nat.lib().prism_plan_info(self.handle, ctypes.byref(inf),
+                                            _stream(self.device)), "prism_plan_info")
+        return {"total_blocks": inf.total_blocks, "nnz": inf.nnz,
+                "max_blocks_per_head": inf.max_blocks_per_head,
+                "pair_tokens": inf.pair_tokens, "shape_hist": list(inf.shape_hist)}
+
+
+def plan(q, k, v, av_norm=None, *, T, H, W, top_k=16, top_k_frac=0.0, top_p=0.9,
+         volume_mask=7, fixed_shape=(0, 0, 0), eps=1e-4, tau128=0.5, tau256=0.25,
+         need_backward=True, nnz_capacity=None, workspace=None) -> Plan:
+    """Stages one to three (shapes, re-layout, pooling, selection)."""
+    heads, N, D = q.shape
+    assert N == T * H * W and k.shape == q.shape and v.shape == q.shape
+    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+    assert q.dtype == k.dtype == v.dtype
+    if av_norm is not None:
+        assert av_norm.dtype == torch.float32 and av_norm.numel() == N and av_norm.is_contiguous()
+    cfg = make_config(T, H, W, heads, D, q.dtype, top_k=top_k, top_k_frac=top_k_frac,
+                      top_p=top_p, volume_mask=volume_mask, fixed_shape=fixed_shape, eps=eps,
+                      tau128=tau128, tau256=tau256, need_backward=need_backward)
+    nat.check(nat.lib().prism_config_check(ctypes.byref(cfg)), "prism_config_check")
+    Z = (T // 8) * (H // 8) * (W // 8)
+    worst = heads * (8 * Z) ** 2
+    cap = int(nnz_capacity) if nnz_capacity is not None else min(worst, max(heads * 8 * Z * 64,
+                                                                            worst // 8))
+    for _ in range(2):
+        nbytes = workspace_bytes(cfg, cap)
+        if workspace is None or workspace.numel() < nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        h = ctypes.c_void_p()
+        nnz = ctypes.c_int64()
+        st = nat.lib().prism_plan_create(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(av_norm), _ptr(workspace), workspace.numel(),
+                                         _stream(q.device), ctypes.byref(h), ctypes.byref(nnz))
+        if st == nat.PRISM_ENOMEM_WORKSPACE and nnz.value > cap:
+            cap = int(nnz.value)
+            workspace = None
+            continue
+        nat.check(st, "prism_plan_create")
+        return Plan(h, cfg, workspace, int(nnz.value), q, k, v)
+    raise nat.PrismError(nat.PRISM_ENOMEM_WORKSPACE, "prism_plan_create")
+
+
+def attn_fwd(pl: Plan, q, k, v, o=None, lse=None):
+    """Sparse attention forward; returns (o, lse) in the original token order."""
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    nat.check(nat.lib().prism_attn_fwd(pl.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       _stream(q.device)), "prism_attn_fwd")
+    return o, lse
+
+
+def attn_bwd_workspace_bytes(pl: Plan) -> int:
+    n = ctypes.c_size_t()
+    nat.check(nat.lib().prism_attn_bwd_workspace_size(ctypes.byref(pl.cfg), ctypes.byref(n)),
+              "prism_attn_bwd_workspace_size")
+    return n.value
+
+
+def attn_bwd(pl: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None):
+    """Backward with the plan held constant; returns (dq, dk, dv)."""
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_bytes(pl)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nat.check(nat.lib().prism_attn_bwd(pl.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                       workspace.numel(), _stream(q.device)), "prism_attn_bwd")
+    return dq, dk, dv
+
+
+def block_scores(pl: Plan, head: int) -> torch.Tensor:
+    nblk = int(pl.export("blk_off")[head + 1] - pl.export("blk_off")[head])
+    out = torch.empty((nblk, nblk), dtype=torch.float32, device=pl.device)
+    nat.check(nat.lib().prism_block_scores(pl.handle, int(head), _ptr(out), _stream(pl.device)),
+              "prism_block_scores")
+    return out
+
+
+def candidate(i: int) -> tuple:
+    a = (ctypes.c_int32 * 4)()
+    nat.check(nat.lib().prism_candidate(int(i), a), "prism_candidate")
+    return tuple(a)

@@ -1,0 +1,399 @@
+// Host side of the C ABI declared in include/prism.h: validation, workspace
+// carving and the order of the kernel launches.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "prism_common.h"
+#include "prism_kernels.h"
+
+using namespace prism;
+
+struct prism_plan_s {
+  prism_config cfg;
+  PlanDev P;
+  std::vector<int64_t> blk_off;  // host copy, heads + 1
+  int64_t nnz;
+  int64_t max_blocks;
+  const void* k;
+  const void* v;
+  int32_t* perm;  // device [heads][N], written on export
+};
+
+namespace {
+
+int64_t zones_of(const prism_config& c) {
+  return (int64_t)(c.T / 8) * (c.H / 8) * (c.W / 8);
+}
+
+int fixed_id_of(const prism_config& c) {
+  if (c.fixed_shape[0] == 0 && c.fixed_shape[1] == 0 && c.fixed_shape[2] == 0) return -1;
+  for (int i = 0; i < kNumShapes; i++)
+    if (h_shapes[i].bt == c.fixed_shape[0] && h_shapes[i].bh == c.fixed_shape[1] &&
+        h_shapes[i].bw == c.fixed_shape[2])
+      return i;
+  return -2;
+}
+
+// Sequential sub-allocator over the caller's workspace (256-byte aligned);
+// with a null base it only measures.
+struct Arena {
+  char* base;
+  size_t off = 0;
+  template <class T>
+  T* take(int64_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += (size_t)count * sizeof(T);
+    return p;
+  }
+};
+
+// Carves the plan arrays; returns bytes used for a given pair capacity.
+size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t** perm) {
+  Arena A{base};
+  const int64_t Z = zones_of(c);
+  const int64_t N = (int64_t)c.T * c.H * c.W;
+  const int64_t maxblk = 8 * Z;
+  const int64_t G = (int64_t)c.heads * maxblk;
+  const int D = c.head_dim;
+  const int es = c.dtype == PRISM_BF16 ? 2 : 4;
+  P->T = c.T;
+  P->H = c.H;
+  P->W = c.W;
+  P->heads = c.heads;
+  P->D = D;
+  P->dtype = c.dtype;
+  P->Z = (int)Z;
+  P->N = N;
+  P->vstats = A.take<float>((int64_t)c.heads * Z * 5);
+  P->astats = A.take<float>(Z * 4);
+  P->shape_id = A.take<uint8_t>((int64_t)c.heads * Z);
+  P->zone_base = A.take<int32_t>((int64_t)c.heads * Z);
+  P->nblk = A.take<int32_t>(c.heads);
+  P->blk_off = A.take<int64_t>(c.heads + 1);
+  P->blk_start = A.take<int32_t>(G);
+  P->blk_shape = A.take<uint8_t>(G);
+  P->blk_head = A.take<int32_t>(G);
+  P->qbar = A.take<float>(G * D);
+  P->kbar = A.take<float>(G * D);
+  P->qgrid = A.take<uint16_t>(G * D);
+  P->kgrid = A.take<uint16_t>(G * D);
+  P->qexp = A.take<int32_t>(G);
+  P->kexp = A.take<int32_t>(G);
+  P->kp = A.take<char>((int64_t)c.heads * N * D * es);
+  P->vp = A.take<char>((int64_t)c.heads * N * D * es);
+  P->scores = A.take<float>(maxblk * maxblk);
+  P->row_cnt = A.take<int32_t>(G);
+  P->row_key = A.take<uint32_t>(G);
+  P->row_tie = A.take<int32_t>(G);
+  P->row_ptr = A.take<int64_t>(G + 1);
+  P->row_cost = A.take<int64_t>(G);
+  P->counters = A.take<int64_t>(8);
+  int32_t* pm = A.take<int32_t>((int64_t)c.heads * N);
+  if (perm) *perm = pm;
+  if (c.need_backward) {
+    P->colt_ptr = A.take<int64_t>(G + 1);
+    P->colt_cnt = A.take<int32_t>(G);
+    P->chunk_cnt = A.take<int32_t>((maxblk / 64 + 1) * maxblk);
+  } else {
+    P->colt_ptr = nullptr;
+    P->colt_cnt = nullptr;
+    P->chunk_cnt = nullptr;
+  }
+  P->col_idx = A.take<int32_t>(cap);
+  P->colt_idx = c.need_backward ? A.take<int32_t>(cap) : nullptr;
+  P->cap = cap;
+  return A.off + 256;
+}
+
+size_t per_pair_bytes(const prism_config& c) { return c.need_backward ? 8 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+void prism_config_default(prism_config* c) {
+  if (!c) return;
+  memset(c, 0, sizeof(*c));
+  c->T = c->H = c->W = 8;
+  c->heads = 1;
+  c->head_dim = 128;
+  c->dtype = PRISM_BF16;
+  c->top_k = 16;
+  c->top_k_frac = 0.0f;
+  c->top_p = 0.9f;
+  c->volume_mask = 7u;
+  c->eps = 1e-4f;
+  c->tau128 = 0.5f;
+  c->tau256 = 0.25f;
+  c->need_backward = 1;
+}
+
+prism_status prism_config_check(const prism_config* c) {
+  if (!c) return PRISM_EINVAL;
+  if (c->T <= 0 || c->H <= 0 || c->W <= 0 || c->T % 8 || c->H % 8 || c->W % 8)
+    return PRISM_EINVAL;
+  if (c->heads <= 0) return PRISM_EINVAL;
+  if ((int64_t)c->T * c->H * c->W > (int64_t)0x7fffffff) return PRISM_EUNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return PRISM_EUNSUPPORTED;
+  if (c->dtype != PRISM_F32 && c->dtype != PRISM_BF16) return PRISM_EINVAL;
+  if (c->top_k < 0) return PRISM_EINVAL;
+  if (!(c->top_k_frac >= 0.0f) || !isfinite(c->top_k_frac)) return PRISM_EINVAL;
+  if (!(c->top_p >= 0.0f)) return PRISM_EINVAL;  // also rejects NaN
+  if ((c->volume_mask & 7u) == 0 || (c->volume_mask & ~7u)) return PRISM_EINVAL;
+  if (fixed_id_of(*c) == -2) return PRISM_EINVAL;
+  if (!(c->eps > 0.0f) || !isfinite(c->eps)) return PRISM_EINVAL;
+  if (!(c->tau256 >= 0.0f) || !(c->tau128 >= c->tau256) || !isfinite(c->tau128))
+    return PRISM_EINVAL;
+  return PRISM_OK;
+}
+
+prism_status prism_plan_workspace_size(const prism_config* c, int64_t nnz_capacity,
+                                       size_t* bytes) {
+  prism_status s = prism_config_check(c);
+  if (s != PRISM_OK) return s;
+  if (!bytes) return PRISM_EINVAL;
+  if (nnz_capacity < 0) {
+    int64_t mb = 8 * zones_of(*c);
+    nnz_capacity = (int64_t)c->heads * mb * mb;
+  }
+  PlanDev P;
+  *bytes = carve(*c, nnz_capacity, nullptr, &P, nullptr);
+  return PRISM_OK;
+}
+
+prism_status prism_plan_create(const prism_config* c, const void* q, const void* k,
+                               const void* v, const float* av_norm, void* workspace,
+                               size_t workspace_bytes, void* stream, prism_plan_t** plan_out,
+                               int64_t* nnz_out) {
+  prism_status s = prism_config_check(c);
+  if (s != PRISM_OK) return s;
+  if (!q || !k || !v || !workspace || !plan_out) return PRISM_EINVAL;
+  *plan_out = nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  PlanDev P;
+  size_t fixed = carve(*c, 0, nullptr, &P, nullptr);
+  if (workspace_bytes < fixed) {
+    if (nnz_out) *nnz_out = -1;
+    return PRISM_ENOMEM_WORKSPACE;
+  }
+  int64_t cap = (int64_t)((workspace_bytes - fixed) / per_pair_bytes(*c));
+  int32_t* perm = nullptr;
+  carve(*c, cap, (char*)workspace, &P, &perm);
+  const int fixed_id = fixed_id_of(*c);
+
+  PRISM_HIP(hipGetLastError());
+  bool ok = launch_zone_stats(v, c->dtype, c->head_dim, c->H, c->W, P.Z, c->heads, P.N,
+                              P.vstats, st);
+  if (av_norm)
+    ok = ok && launch_audio_stats(av_norm, c->H, c->W, P.Z, P.astats, st);
+  else
+    PRISM_HIP(hipMemsetAsync(P.astats, 0, sizeof(float) * 4 * P.Z, st));
+  ok = ok && launch_shapes(P, av_norm != nullptr, *c, fixed_id, st);
+  ok = ok && launch_blk_off(P, st);
+  if (!ok) return PRISM_EDEVICE;
+  std::vector<int64_t> off(c->heads + 1);
+  PRISM_HIP(hipMemcpyAsync(off.data(), P.blk_off, sizeof(int64_t) * (c->heads + 1),
+                           hipMemcpyDeviceToHost, st));
+  PRISM_HIP(hipStreamSynchronize(st));
+  int64_t maxb = 0;
+  for (int h = 0; h < c->heads; h++) maxb = std::max(maxb, off[h + 1] - off[h]);
+
+  ok = launch_permute_pool(P, q, k, v, st);
+  PRISM_HIP(hipMemsetAsync(P.counters, 0, sizeof(int64_t) * 8, st));
+  for (int h = 0; h < c->heads && ok; h++) {
+    int n = (int)(off[h + 1] - off[h]);
+    ok = launch_block_scores(P, off[h], n, P.scores, st);
+    ok = ok && launch_select(P, off[h], n, *c, h == c->heads - 1, st);
+  }
+  if (!ok) return PRISM_EDEVICE;
+  int64_t nnz = 0;
+  PRISM_HIP(hipMemcpyAsync(&nnz, P.counters, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+  PRISM_HIP(hipStreamSynchronize(st));
+  if (nnz_out) *nnz_out = nnz;
+  if (nnz > cap) return PRISM_ENOMEM_WORKSPACE;
+  if (c->need_backward) {
+    for (int h = 0; h < c->heads && ok; h++) {
+      int n = (int)(off[h + 1] - off[h]);
+      ok = launch_transpose(P, off[h], n, h == c->heads - 1, st);
+    }
+    if (!ok) return PRISM_EDEVICE;
+  }
+  PRISM_HIP(hipGetLastError());
+  prism_plan_s* pl = new prism_plan_s;
+  pl->cfg = *c;
+  pl->P = P;
+  pl->blk_off = off;
+  pl->nnz = nnz;
+  pl->max_blocks = maxb;
+  pl->k = k;
+  pl->v = v;
+  pl->perm = perm;
+  *plan_out = pl;
+  return PRISM_OK;
+}
+
+void prism_plan_destroy(prism_plan_t* plan) { delete plan; }
+
+prism_status prism_attn_fwd(const prism_plan_t* plan, const void* q, const void* k,
+                            const void* v, void* o, float* lse, void* stream) {
+  if (!plan || !q || !k || !v || !o || !lse) return PRISM_EINVAL;
+  if (k != plan->k || v != plan->v) return PRISM_ESTATE;
+  const prism_config& c = plan->cfg;
+  if (!((c.dtype == PRISM_BF16 && c.head_dim == 128) || c.dtype == PRISM_F32))
+    return PRISM_EUNSUPPORTED;
+  PRISM_HIP(hipGetLastError());
+  if (!launch_attn_fwd(plan->P, q, o, lse, (hipStream_t)stream)) return PRISM_EDEVICE;
+  return PRISM_OK;
+}
+
+prism_status prism_attn_bwd_workspace_size(const prism_config* c, size_t* bytes) {
+  prism_status s = prism_config_check(c);
+  if (s != PRISM_OK) return s;
+  if (!bytes) return PRISM_EINVAL;
+  const int64_t N = (int64_t)c->T * c->H * c->W;
+  Arena A{nullptr};
+  A.take<float>((int64_t)c->heads * N);
+  A.take<float>((int64_t)c->heads * N);
+  A.take<uint16_t>((int64_t)c->heads * N * c->head_dim);
+  A.take<uint16_t>((int64_t)c->heads * N * c->head_dim);
+  *bytes = A.off + 256;
+  return PRISM_OK;
+}
+
+prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void* k,
+                            const void* v, const void* o, const float* lse, const void* d_o,
+                            void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!plan || !q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv || !workspace)
+    return PRISM_EINVAL;
+  if (k != plan->k || v != plan->v) return PRISM_ESTATE;
+  const prism_config& c = plan->cfg;
+  if (!c.need_backward) return PRISM_ESTATE;
+  if (!(c.dtype == PRISM_BF16 && c.head_dim == 128)) return PRISM_EUNSUPPORTED;
+  size_t need = 0;
+  prism_attn_bwd_workspace_size(&c, &need);
+  if (workspace_bytes < need) return PRISM_ENOMEM_WORKSPACE;
+  const int64_t N = plan->P.N;
+  Arena A{(char*)workspace};
+  BwdDev B;
+  B.delta = A.take<float>((int64_t)c.heads * N);
+  B.lse_p = A.take<float>((int64_t)c.heads * N);
+  B.qp = A.take<uint16_t>((int64_t)c.heads * N * c.head_dim);
+  B.dop = A.take<uint16_t>((int64_t)c.heads * N * c.head_dim);
+  PRISM_HIP(hipGetLastError());
+  if (!launch_attn_bwd(plan->P, B, q, o, lse, d_o, dq, dk, dv, (hipStream_t)stream))
+    return PRISM_EDEVICE;
+  return PRISM_OK;
+}
+
+prism_status prism_block_scores(const prism_plan_t* plan, int32_t head, float* out,
+                                void* stream) {
+  if (!plan || !out || head < 0 || head >= plan->cfg.heads) return PRISM_EINVAL;
+  int n = (int)(plan->blk_off[head + 1] - plan->blk_off[head]);
+  PRISM_HIP(hipGetLastError());
+  if (!launch_block_scores(plan->P, plan->blk_off[head], n, out, (hipStream_t)stream))
+    return PRISM_EDEVICE;
+  return PRISM_OK;
+}
+
+static const void* array_ptr(const prism_plan_t* pl, int which, size_t* bytes) {
+  const PlanDev& P = pl->P;
+  const prism_config& c = pl->cfg;
+  const int64_t G = pl->blk_off[c.heads];
+  const int64_t Z = P.Z;
+  switch (which) {
+    case PRISM_ARR_ZONE_STATS: *bytes = sizeof(float) * c.heads * Z * 5; return P.vstats;
+    case PRISM_ARR_AUDIO_STATS: *bytes = sizeof(float) * Z * 4; return P.astats;
+    case PRISM_ARR_SHAPE_ID: *bytes = (size_t)c.heads * Z; return P.shape_id;
+    case PRISM_ARR_BLK_OFF: *bytes = sizeof(int64_t) * (c.heads + 1); return P.blk_off;
+    case PRISM_ARR_BLK_START: *bytes = sizeof(int32_t) * G; return P.blk_start;
+    case PRISM_ARR_QBAR: *bytes = sizeof(float) * G * c.head_dim; return P.qbar;
+    case PRISM_ARR_KBAR: *bytes = sizeof(float) * G * c.head_dim; return P.kbar;
+    case PRISM_ARR_QEXP: *bytes = sizeof(int32_t) * G; return P.qexp;
+    case PRISM_ARR_KEXP: *bytes = sizeof(int32_t) * G; return P.kexp;
+    case PRISM_ARR_ROW_PTR: *bytes = sizeof(int64_t) * (G + 1); return P.row_ptr;
+    case PRISM_ARR_COL_IDX: *bytes = sizeof(int32_t) * pl->nnz; return P.col_idx;
+    case PRISM_ARR_COLT_PTR:
+      *bytes = c.need_backward ? sizeof(int64_t) * (G + 1) : 0;
+      return P.colt_ptr;
+    case PRISM_ARR_COLT_IDX:
+      *bytes = c.need_backward ? sizeof(int32_t) * pl->nnz : 0;
+      return P.colt_idx;
+    case PRISM_ARR_PERM: *bytes = sizeof(int32_t) * c.heads * P.N; return pl->perm;
+    case PRISM_ARR_QGRID: *bytes = sizeof(uint16_t) * G * c.head_dim; return P.qgrid;
+    case PRISM_ARR_KGRID: *bytes = sizeof(uint16_t) * G * c.head_dim; return P.kgrid;
+    default: *bytes = 0; return nullptr;
+  }
+}
+
+prism_status prism_plan_array_bytes(const prism_plan_t* plan, int32_t which, size_t* bytes) {
+  if (!plan || !bytes) return PRISM_EINVAL;
+  const void* p = array_ptr(plan, which, bytes);
+  if (!p && *bytes) return PRISM_EINVAL;
+  if (which < 0 || which > PRISM_ARR_KGRID) return PRISM_EINVAL;
+  return PRISM_OK;
+}
+
+prism_status prism_plan_export(const prism_plan_t* plan, int32_t which, void* dst,
+                               size_t dst_bytes, void* stream) {
+  if (!plan || !dst || which < 0 || which > PRISM_ARR_KGRID) return PRISM_EINVAL;
+  size_t bytes = 0;
+  const void* p = array_ptr(plan, which, &bytes);
+  if (dst_bytes < bytes) return PRISM_EINVAL;
+  if (bytes == 0) return PRISM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  PRISM_HIP(hipGetLastError());
+  if (which == PRISM_ARR_PERM && !launch_perm_map(plan->P, plan->perm, st)) return PRISM_EDEVICE;
+  PRISM_HIP(hipMemcpyAsync(dst, p, bytes, hipMemcpyDeviceToHost, st));
+  PRISM_HIP(hipStreamSynchronize(st));
+  return PRISM_OK;
+}
+
+prism_status prism_plan_info(const prism_plan_t* plan, prism_plan_info_t* info, void* stream) {
+  if (!plan || !info) return PRISM_EINVAL;
+  const prism_config& c = plan->cfg;
+  const int64_t G = plan->blk_off[c.heads];
+  hipStream_t st = (hipStream_t)stream;
+  memset(info, 0, sizeof(*info));
+  info->total_blocks = G;
+  info->nnz = plan->nnz;
+  info->max_blocks_per_head = plan->max_blocks;
+  PRISM_HIP(hipGetLastError());
+  if (!launch_sum_i64(plan->P.row_cost, G, plan->P.counters + 4, st)) return PRISM_EDEVICE;
+  int64_t pt = 0;
+  PRISM_HIP(hipMemcpyAsync(&pt, plan->P.counters + 4, sizeof(int64_t), hipMemcpyDeviceToHost,
+                           st));
+  std::vector<uint8_t> sid((size_t)c.heads * plan->P.Z);
+  PRISM_HIP(hipMemcpyAsync(sid.data(), plan->P.shape_id, sid.size(), hipMemcpyDeviceToHost, st));
+  PRISM_HIP(hipStreamSynchronize(st));
+  info->pair_tokens = (double)pt;
+  for (uint8_t s : sid) info->shape_hist[s < 16 ? s : 0]++;
+  return PRISM_OK;
+}
+
+prism_status prism_candidate(int32_t id, int32_t* out4) {
+  if (id < 0 || id >= kNumShapes || !out4) return PRISM_EINVAL;
+  out4[0] = h_shapes[id].bt;
+  out4[1] = h_shapes[id].bh;
+  out4[2] = h_shapes[id].bw;
+  out4[3] = h_shapes[id].volume;
+  return PRISM_OK;
+}
+
+const char* prism_status_str(prism_status s) {
+  switch (s) {
+    case PRISM_OK: return "ok";
+    case PRISM_EINVAL: return "invalid argument";
+    case PRISM_EUNSUPPORTED: return "unsupported configuration";
+    case PRISM_ENOMEM_WORKSPACE: return "workspace too small";
+    case PRISM_EDEVICE: return "HIP runtime error";
+    case PRISM_ESTATE: return "arguments do not match the plan";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,1212 @@
+// Plan stages of Prism's dynamic sparse attention on gfx950 (paper.rainbus.top,
+// "方法步骤详情", stages one to three; formulas of xyznot.com/id, "Metode" 1-3):
+// zone statistics, indicator / volume / shape, re-layout and pooling, block
+// scores, Top-k U Top-p selection and the key-major transpose of the lists.
+//
+// Every quantity that decides a shape or a selected block is computed in fp32
+// in one fixed order (compiled with -ffp-contract=off; fused multiply-add
+// only where written as fmaf), so the plan is reproducible bit for bit.
+#include "prism_common.h"
+#include "prism_kernels.h"
+
+namespace prism {
+
+// ============================================================ K1: zone stats
+// One wave per (head, zone).  Lane l owns channels [l*CPL, l*CPL + CPL).
+// Token rows are read 64 lanes wide (one row per load instruction).
+
+template <int DT, int CPL>
+struct RowVal;  // one lane's CPL channels of one token row, kept packed
+
+template <>
+struct RowVal<1, 2> {  // bf16 x2
+  uint32_t v;
+  __device__ static RowVal load(const void* base, int64_t e) {
+    RowVal r;
+    r.v = __builtin_nontemporal_load((const uint32_t*)((const uint16_t*)base + e));
+    return r;
+  }
+  __device__ float get(int k) const {
+    return k ? __uint_as_float(v & 0xffff0000u) : __uint_as_float(v << 16);
+  }
+};
+template <>
+struct RowVal<1, 1> {
+  uint32_t v;
+  __device__ static RowVal load(const void* base, int64_t e) {
+    RowVal r;
+    r.v = ((const uint16_t*)base)[e];
+    return r;
+  }
+  __device__ float get(int) const { return __uint_as_float(v << 16); }
+};
+template <>
+struct RowVal<0, 1> {
+  float v;
+  __device__ static RowVal load(const void* base, int64_t e) {
+    RowVal r;
+    r.v = ((const float*)base)[e];
+    return r;
+  }
+  __device__ float get(int) const { return v; }
+};
+template <>
+struct RowVal<0, 2> {
+  float2 v;
+  __device__ static RowVal load(const void* base, int64_t e) {
+    RowVal r;
+    r.v = *(const float2*)((const float*)base + e);
+    return r;
+  }
+  __device__ float get(int k) const { return k ? v.y : v.x; }
+};
+
+__device__ inline float var8(const float* p) {
+  float mu = p[0];
+#pragma unroll
+  for (int i = 1; i < 8; i++) mu = mu + p[i];
+  mu = mu * 0.125f;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    float d = p[i] - mu;
+    acc = __builtin_fmaf(d, d, acc);
+  }
+  return acc * 0.125f;
+}
+
+// sum over the 64 lanes: for offsets 32..1 each lane adds the value of lane^offset
+__device__ inline float lane_butterfly_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = x + __shfl_xor(x, off, 64);
+  return x;
+}
+
+template <int DT, int CPL>
+__global__ __launch_bounds__(64) void k_zone_stats(const void* __restrict__ v, int H, int W,
+                                                   int Z, int64_t N, float* __restrict__ out) {
+  constexpr int D = 64 * CPL;
+  const int lane = threadIdx.x;
+  const int hm = blockIdx.x;
+  const int h = hm / Z, m = hm - h * Z;
+  const int zH = H >> 3, zW = W >> 3;
+  const int mt = m / (zH * zW), rem = m - mt * (zH * zW);
+  const int mh = rem / zW, mw = rem - mh * zW;
+  const int64_t base = (int64_t)h * N * D + (int64_t)lane * CPL;
+
+  // per-frame profile means and frame-difference means, one slot per lane
+  __shared__ float sPT[8][CPL][64], sDM[7][CPL][64];
+  RowVal<DT, CPL> cur[64], nxt[64];
+  float PH[8][CPL], PW[8][CPL], sv[CPL], within[CPL];
+
+  auto load_slice = [&](int t, RowVal<DT, CPL>* dst) {
+#pragma unroll
+    for (int y = 0; y < 8; y++) {
+      int64_t n0 = ((int64_t)((mt << 3) + t) * H + ((mh << 3) + y)) * W + (mw << 3);
+#pragma unroll
+      for (int w = 0; w < 8; w++) dst[y * 8 + w] = RowVal<DT, CPL>::load(v, base + (n0 + w) * D);
+    }
+  };
+
+  load_slice(0, cur);
+#pragma unroll 1
+  for (int t = 0; t < 8; t++) {
+    const bool more = t < 7;
+    if (more) load_slice(t + 1, nxt);
+#pragma unroll
+    for (int k = 0; k < CPL; k++) {
+      float Lw[8], Cy[8];
+#pragma unroll
+      for (int y = 0; y < 8; y++) {
+        float a = cur[y * 8].get(k);
+#pragma unroll
+        for (int w = 1; w < 8; w++) a = a + cur[y * 8 + w].get(k);
+        Lw[y] = a;
+      }
+#pragma unroll
+      for (int w = 0; w < 8; w++) {
+        float a = cur[w].get(k);
+#pragma unroll
+        for (int y = 1; y < 8; y++) a = a + cur[y * 8 + w].get(k);
+        Cy[w] = a;
+      }
+      float ss = Lw[0];
+#pragma unroll
+      for (int y = 1; y < 8; y++) ss = ss + Lw[y];
+      const float mref = ss * 0.015625f;
+      sPT[t][k][lane] = mref;
+#pragma unroll
+      for (int y = 0; y < 8; y++) PH[y][k] = (t == 0) ? Lw[y] : PH[y][k] + Lw[y];
+#pragma unroll
+      for (int w = 0; w < 8; w++) PW[w][k] = (t == 0) ? Cy[w] : PW[w][k] + Cy[w];
+      // spatial variance of frame t
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 64; i++) {
+        float d = cur[i].get(k) - mref;
+        acc = __builtin_fmaf(d, d, acc);
+      }
+      float vt = acc * 0.015625f;
+      sv[k] = (t == 0) ? vt : sv[k] + vt;
+      // frame difference t -> t+1
+      if (more) {
+        float s = nxt[0].get(k) - cur[0].get(k);
+#pragma unroll
+        for (int i = 1; i < 64; i++) s = s + (nxt[i].get(k) - cur[i].get(k));
+        float dmt = s * 0.015625f;
+        sDM[t][k][lane] = dmt;
+        float a2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 64; i++) {
+          float e = (nxt[i].get(k) - cur[i].get(k)) - dmt;
+          a2 = __builtin_fmaf(e, e, a2);
+        }
+        float dv = a2 * 0.015625f;
+        within[k] = (t == 0) ? dv : within[k] + dv;
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 64; i++) cur[i] = nxt[i];
+    }
+  }
+  float PT[8][CPL], dm[7][CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; k++) {
+#pragma unroll
+    for (int t = 0; t < 8; t++) PT[t][k] = sPT[t][k][lane];
+#pragma unroll
+    for (int t = 0; t < 7; t++) dm[t][k] = sDM[t][k][lane];
+  }
+
+  float st[5][CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; k++) {
+    float ph[8], pw[8], pt[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      pt[i] = PT[i][k];
+      ph[i] = PH[i][k] * 0.015625f;
+      pw[i] = PW[i][k] * 0.015625f;
+    }
+    st[0][k] = var8(pt);
+    st[1][k] = var8(ph);
+    st[2][k] = var8(pw);
+    st[3][k] = sv[k] * 0.125f;
+    float wv = within[k] / 7.0f;
+    float mu = dm[0][k];
+#pragma unroll
+    for (int i = 1; i < 7; i++) mu = mu + dm[i][k];
+    mu = mu / 7.0f;
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 7; i++) {
+      float e = dm[i][k] - mu;
+      a = __builtin_fmaf(e, e, a);
+    }
+    st[4][k] = wv + a / 7.0f;
+  }
+  const float invD = 1.0f / (float)D;
+#pragma unroll
+  for (int s = 0; s < 5; s++) {
+    float x = st[s][0];
+#pragma unroll
+    for (int k = 1; k < CPL; k++) x = x + st[s][k];
+    x = lane_butterfly_sum(x);
+    if (lane == 0) out[(int64_t)hm * 5 + s] = x * invD;
+  }
+}
+
+// ============================================================ K1b: audio stats
+// One thread per zone over the [N] float32 map: axis-profile variances and the
+// zone mean, with the same fixed order as the video statistics (D = 1).
+__global__ __launch_bounds__(64) void k_audio_stats(const float* __restrict__ a, int H, int W,
+                                                    int Z, float* __restrict__ out) {
+  int m = blockIdx.x * 64 + threadIdx.x;
+  if (m >= Z) return;
+  const int zH = H >> 3, zW = W >> 3;
+  const int mt = m / (zH * zW), rem = m - mt * (zH * zW);
+  const int mh = rem / zW, mw = rem - mh * zW;
+  auto X = [&](int t, int y, int w) {
+    return a[((int64_t)((mt << 3) + t) * H + ((mh << 3) + y)) * W + ((mw << 3) + w)];
+  };
+  float PT[8], PH[8], PW[8];
+  for (int t = 0; t < 8; t++) {
+    float ss = 0.0f;
+    for (int y = 0; y < 8; y++) {
+      float l = X(t, y, 0);
+      for (int w = 1; w < 8; w++) l = l + X(t, y, w);
+      ss = (y == 0) ? l : ss + l;
+      PH[y] = (t == 0) ? l : PH[y] + l;
+    }
+    for (int w = 0; w < 8; w++) {
+      float c = X(t, 0, w);
+      for (int y = 1; y < 8; y++) c = c + X(t, y, w);
+      PW[w] = (t == 0) ? c : PW[w] + c;
+    }
+    PT[t] = ss * 0.015625f;
+  }
+  for (int i = 0; i < 8; i++) {
+    PH[i] = PH[i] * 0.015625f;
+    PW[i] = PW[i] * 0.015625f;
+  }
+  float mu = PT[0];
+  for (int i = 1; i < 8; i++) mu = mu + PT[i];
+  out[m * 4 + 0] = var8(PT);
+  out[m * 4 + 1] = var8(PH);
+  out[m * 4 + 2] = var8(PW);
+  out[m * 4 + 3] = mu * 0.125f;
+}
+
+// ============================================================ K2: shapes
+__device__ inline void ratio3(const float* x, float* r) {
+  float s = (x[0] + x[1]) + x[2];
+  if (s > 0.0f) {
+    r[0] = x[0] / s;
+    r[1] = x[1] / s;
+    r[2] = x[2] / s;
+  } else {
+    r[0] = r[1] = r[2] = 1.0f / 3.0f;
+  }
+}
+
+// Candidate a strictly nearer than b to l*(g) in log2 space.  Since the
+// coordinates of l* and of every candidate (log2 of its edges) sum to log2 B,
+// |l* - e|^2 = const + sum e_d^2 + sum e_d log2 g_d; "a nearer" is therefore
+// prod g_d^(ea_d - eb_d) < 2^(|eb|^2 - |ea|^2).  Each side is a product of at
+// most two fp32 values times a power of two, exact in fp64.
+__device__ inline bool shape_nearer(const float* g, int a, int b) {
+  const Shape& A = d_shapes[a];
+  const Shape& Bs = d_shapes[b];
+  int ea[3] = {A.log2_bt, A.log2_bh, A.log2_bw};
+  int eb[3] = {Bs.log2_bt, Bs.log2_bh, Bs.log2_bw};
+  int qa = ea[0] * ea[0] + ea[1] * ea[1] + ea[2] * ea[2];
+  int qb = eb[0] * eb[0] + eb[1] * eb[1] + eb[2] * eb[2];
+  double lhs = 1.0, rhs = 1.0;
+#pragma unroll
+  for (int d = 0; d < 3; d++) {
+    int k = ea[d] - eb[d];
+    double gd = (double)g[d];
+    if (k >= 1) lhs = lhs * gd;
+    if (k >= 2) lhs = lhs * gd;
+    if (k <= -1) rhs = rhs * gd;
+    if (k <= -2) rhs = rhs * gd;
+  }
+  rhs = ldexp(rhs, qb - qa);
+  return lhs < rhs;
+}
+
+__device__ inline int volume_tier(float rr, float rmax, float tau128, float tau256,
+                                  uint32_t mask) {
+  int B;
+  if (!(rmax > 0.0f)) {
+    B = 256;
+  } else {
+    float rho = rr / rmax;
+    B = (rho >= tau128) ? 64 : (rho >= tau256) ? 128 : 256;
+  }
+  int bit = B == 64 ? 0 : B == 128 ? 1 : 2;
+  if (mask & (1u << bit)) return B;
+  for (int dist = 1; dist <= 2; dist++) {
+    if (bit - dist >= 0 && (mask & (1u << (bit - dist)))) return 64 << (bit - dist);
+    if (bit + dist <= 2 && (mask & (1u << (bit + dist)))) return 64 << (bit + dist);
+  }
+  return B;
+}
+
+__device__ inline float block_max(float v, float* sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  float r = sh[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); i++) r = fmaxf(r, sh[i]);
+  return r;
+}
+
+// One block of 256 threads per head.
+__global__ __launch_bounds__(256) void k_shapes(const float* __restrict__ vstats,
+                                                const float* __restrict__ astats, int have_audio,
+                                                int Z, float eps, float tau128, float tau256,
+                                                uint32_t vmask, int fixed_id,
+                                                uint8_t* __restrict__ shape_id,
+                                                int32_t* __restrict__ zone_base,
+                                                int32_t* __restrict__ nblk) {
+  __shared__ float sh[8];
+  __shared__ int scan[256];
+  const int h = blockIdx.x;
+  float am = 0.0f, rm = 0.0f;
+  for (int m = threadIdx.x; m < Z; m += 256) {
+    if (have_audio) am = fmaxf(am, astats[m * 4 + 3]);
+    const float* s = vstats + ((int64_t)h * Z + m) * 5;
+    rm = fmaxf(rm, s[3] + s[4]);
+  }
+  const float amax = block_max(am, sh);
+  const float rmax = block_max(rm, sh);
+  int carry = 0;
+  for (int m0 = 0; m0 < Z; m0 += 256) {
+    int m = m0 + threadIdx.x;
+    int nb = 0;
+    if (m < Z) {
+      const float* s = vstats + ((int64_t)h * Z + m) * 5;
+      int id, B;
+      if (fixed_id >= 0) {
+        id = fixed_id;
+        B = d_shapes[id].volume;
+      } else {
+        float r[3], g[3];
+        ratio3(s, r);
+        if (have_audio && amax > 0.0f) {
+          float abar = astats[m * 4 + 3] / amax;
+          float va[3];
+          ratio3(astats + m * 4, va);
+#pragma unroll
+          for (int d = 0; d < 3; d++) {
+            float c = abar * va[d];
+            g[d] = (r[d] + c) + eps;
+          }
+        } else {
+#pragma unroll
+          for (int d = 0; d < 3; d++) g[d] = r[d] + eps;
+        }
+        B = volume_tier(s[3] + s[4], rmax, tau128, tau256, vmask);
+        int first = shape_first(B), cnt = shape_count(B);
+        id = first;
+        for (int c = first + 1; c < first + cnt; c++)
+          if (shape_nearer(g, c, id)) id = c;
+      }
+      shape_id[(int64_t)h * Z + m] = (uint8_t)id;
+      nb = 512 / B;
+    }
+    // exclusive block scan of nb
+    scan[threadIdx.x] = nb;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      int v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (m < Z) zone_base[(int64_t)h * Z + m] = carry + scan[threadIdx.x] - nb;
+    carry += scan[255];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) nblk[h] = carry;
+}
+
+// ============================================================ K4: re-layout + pooling
+// One block of 512 threads (8 waves) per (head, zone); wave w owns permuted
+// rows [64w, 64w+64) of the zone.  K and V rows are copied to the permuted
+// buffers; Q and K are summed per 64-row tile (rows in permuted order), then
+// per block (tiles in order), scaled by 1/B and written with their integer
+// grid: q_c = rint(x_c 2^-E), E = exponent(max_c |x_c|) - 8.
+template <int DT, int CPL, bool SWZ>
+__global__ __launch_bounds__(512) void k_permute_pool(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, int H,
+    int W, int Z, int64_t N, const uint8_t* __restrict__ shape_id,
+    const int32_t* __restrict__ zone_base, const int64_t* __restrict__ blk_off,
+    void* __restrict__ kp, void* __restrict__ vp, int32_t* __restrict__ blk_start,
+    uint8_t* __restrict__ blk_shape, int32_t* __restrict__ blk_head, float* __restrict__ qbar,
+    float* __restrict__ kbar, uint16_t* __restrict__ qgrid, uint16_t* __restrict__ kgrid,
+    int32_t* __restrict__ qexp, int32_t* __restrict__ kexp) {
+  constexpr int D = 64 * CPL;
+  constexpr int ES = DT == 1 ? 2 : 4;  // element size
+  __shared__ float tsum[2][8][D];
+  const int hm = blockIdx.x;
+  const int h = hm / Z, m = hm - h * Z;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sid = shape_id[hm];
+  const Shape sh = d_shapes[sid];
+  const int B = sh.volume;
+  const int64_t hb = (int64_t)h * N;
+  float aq[CPL], ak[CPL];
+  for (int i = 0; i < 64; i++) {
+    const int r = wv * 64 + i;
+    const int64_t n = token_of(sh, m, r, H, W);
+    const int64_t src = (hb + n) * D + lane * CPL;
+    RowVal<DT, CPL> rq = RowVal<DT, CPL>::load(q, src);
+    RowVal<DT, CPL> rk = RowVal<DT, CPL>::load(k, src);
+    RowVal<DT, CPL> rv = RowVal<DT, CPL>::load(v, src);
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+      aq[c] = (i == 0) ? rq.get(c) : aq[c] + rq.get(c);
+      ak[c] = (i == 0) ? rk.get(c) : ak[c] + rk.get(c);
+    }
+    const int64_t p = (int64_t)m * 512 + r;  // permuted row within the head
+    int64_t dst_byte;
+    if (SWZ) {  // bf16, D = 128: 4 bytes per lane inside chunk lane/4
+      int rho = (int)(p & 63);
+      int chunk = (lane >> 2) ^ chunk_swizzle(rho);
+      dst_byte = ((hb + p) * D) * 2 + chunk * 16 + (lane & 3) * 4;
+    } else {
+      dst_byte = ((hb + p) * D + lane * CPL) * ES;
+    }
+    constexpr int VB = CPL * ES;  // bytes per lane
+    if (VB == 4) {
+      *(uint32_t*)((char*)kp + dst_byte) = *(const uint32_t*)((const char*)k + src * ES);
+      *(uint32_t*)((char*)vp + dst_byte) = *(const uint32_t*)((const char*)v + src * ES);
+    } else if (VB == 2) {
+      *(uint16_t*)((char*)kp + dst_byte) = *(const uint16_t*)((const char*)k + src * ES);
+      *(uint16_t*)((char*)vp + dst_byte) = *(const uint16_t*)((const char*)v + src * ES);
+    } else {
+      *(uint2*)((char*)kp + dst_byte) = *(const uint2*)((const char*)k + src * ES);
+      *(uint2*)((char*)vp + dst_byte) = *(const uint2*)((const char*)v + src * ES);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+    tsum[0][wv][lane * CPL + c] = aq[c];
+    tsum[1][wv][lane * CPL + c] = ak[c];
+  }
+  __syncthreads();
+  const int nb = 512 / B;
+  if (wv < nb) {
+    const int tpb = B / 64;
+    const int64_t g = blk_off[h] + zone_base[hm] + wv;
+    if (lane == 0) {
+      blk_start[g] = m * 512 + wv * B;
+      blk_shape[g] = (uint8_t)sid;
+      blk_head[g] = h;
+    }
+    const float invB = 1.0f / (float)B;
+#pragma unroll
+    for (int which = 0; which < 2; which++) {
+      float x[CPL];
+      float mx = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPL; c++) {
+        float s = tsum[which][wv * tpb][lane * CPL + c];
+        for (int t = 1; t < tpb; t++) s = s + tsum[which][wv * tpb + t][lane * CPL + c];
+        x[c] = s * invB;
+        mx = fmaxf(mx, fabsf(x[c]));
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      int e = 0;
+      if (mx > 0.0f) {
+        frexpf(mx, &e);
+        e -= 8;
+      }
+      float* xb = which ? kbar : qbar;
+      uint16_t* gr = which ? kgrid : qgrid;
+#pragma unroll
+      for (int c = 0; c < CPL; c++) {
+        xb[g * D + lane * CPL + c] = x[c];
+        float qv = mx > 0.0f ? rintf(ldexpf(x[c], -e)) : 0.0f;
+        gr[g * D + lane * CPL + c] = (uint16_t)(__float_as_uint(qv) >> 16);  // exact: |qv| <= 256
+      }
+      if (lane == 0) (which ? kexp : qexp)[g] = e;
+    }
+  }
+}
+
+// ============================================================ K5: block scores
+// s_ij = ldexp(I_ij, Ei + Ej) * fl(1/sqrt D), I_ij = integer dot product of the
+// grid rows, exact in fp32 on the bf16 MFMA (|I| <= 2^23).
+// Block of 256 threads covers 128 x 128 scores; each wave 64 x 64.
+template <int D>
+__global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict__ qgrid,
+                                                      const uint16_t* __restrict__ kgrid,
+                                                      const int32_t* __restrict__ qexp,
+                                                      const int32_t* __restrict__ kexp,
+                                                      int64_t g0, int n, float cD,
+                                                      float* __restrict__ scores) {
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i0 = blockIdx.y * 128 + (wv >> 1) * 64;
+  const int j0 = blockIdx.x * 128 + (wv & 1) * 64;
+  const int hl = lane >> 5, l32 = lane & 31;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[a][b][r] = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; kk++) {
+    bf16x8 af[2], bfr[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++) {
+      int i = i0 + rb * 32 + l32;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (i < n) u = *(const uint4*)(qgrid + (g0 + i) * D + kk * 16 + hl * 8);
+      af[rb] = __builtin_bit_cast(bf16x8, u);
+      int j = j0 + rb * 32 + l32;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (j < n) w = *(const uint4*)(kgrid + (g0 + j) * D + kk * 16 + hl * 8);
+      bfr[rb] = __builtin_bit_cast(bf16x8, w);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+      for (int b = 0; b < 2; b++)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+  }
+#pragma unroll
+  for (int a = 0; a < 2; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+      int j = j0 + b * 32 + l32;
+      if (j >= n) continue;
+      int ej = kexp[g0 + j];
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        int i = i0 + a * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+        if (i < n) {
+          float s = ldexpf(acc[a][b][r], qexp[g0 + i] + ej) * cD;
+          scores[(int64_t)i * n + j] = (s == 0.0f) ? 0.0f : s;
+        }
+      }
+    }
+}
+
+// ============================================================ K6: selection
+// Order-preserving map of fp32 to uint32 (larger float -> larger key).
+__device__ inline uint32_t f2key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float key2f(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// 2^x for x <= 0: x = k + f with k = rint(x), |f| <= 1/2, 2^f from its
+// degree-7 Taylor series in f ln 2 (Horner, fused multiply-add); the
+// coefficients are (ln 2)^n / n! rounded to fp32.
+__device__ inline float exp2_taylor(float x) {
+  if (!(x > -100.0f)) return 0.0f;
+  float kf = rintf(x);
+  float f = x - kf;
+  float p = 0.000015252733804059840280f;
+  p = __builtin_fmaf(p, f, 0.00015403530393381609954f);
+  p = __builtin_fmaf(p, f, 0.0013333558146428443423f);
+  p = __builtin_fmaf(p, f, 0.0096181291076284771620f);
+  p = __builtin_fmaf(p, f, 0.055504108664821579953f);
+  p = __builtin_fmaf(p, f, 0.24022650695910071233f);
+  p = __builtin_fmaf(p, f, 0.69314718055994530942f);
+  p = __builtin_fmaf(p, f, 1.0f);
+  return ldexpf(p, (int)kf);
+}
+
+// softmax weight of a score in 2^-32 units relative to the row maximum
+__device__ inline uint64_t weight_of(float s, float smax) {
+  const float LOG2E = 1.44269504088896340736f;
+  float x = (s - smax) * LOG2E;
+  float y = exp2_taylor(x);
+  return (uint64_t)(y * 4294967296.0f);
+}
+
+__device__ inline int bucket_of(float s, float smax) {
+  const float LOG2E = 1.44269504088896340736f;
+  float x = (s - smax) * LOG2E;  // same rounding as weight_of: monotone in s
+  float b = -x * 8.0f;
+  return b >= 255.0f ? 255 : (int)b;
+}
+
+template <typename T>
+__device__ inline T block_sum(T v, T* sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  T r = sh[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); i++) r += sh[i];
+  __syncthreads();
+  return r;
+}
+
+constexpr int kSelThreads = 256;
+constexpr int kSortCap = 2048;
+
+struct SelShared {
+  uint32_t cnt[4][256];
+  unsigned long long wt[4][256];
+  unsigned long long list[kSortCap];  // (key << 32) | ~index
+  uint32_t lcount;
+  unsigned long long red64[8];
+  uint32_t red32[8];
+  float redf[8];
+  int bsel[4];
+  unsigned long long above_w[2];
+  uint32_t above_c[2];
+};
+
+// Sort the collected (key, index) pairs descending by key, ascending by index.
+__device__ void sort_desc(unsigned long long* a, int n) {
+  int P = 1;
+  while (P < n) P <<= 1;
+  for (int i = n + threadIdx.x; i < P; i += blockDim.x) a[i] = 0ull;  // sorts last
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        int ixj = i ^ j;
+        if (ixj > i) {
+          unsigned long long x = a[i], y = a[ixj];
+          bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            a[i] = y;
+            a[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// inclusive scan over the block (256 threads) of one u64 per thread
+__device__ inline unsigned long long block_incl_scan(unsigned long long v,
+                                                     unsigned long long* sh,
+                                                     unsigned long long* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    unsigned long long u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  __syncthreads();
+  if (lane == 63) sh[wv] = v;
+  __syncthreads();
+  unsigned long long before = 0, tot = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); w++) {
+    if (w < wv) before += sh[w];
+    tot += sh[w];
+  }
+  *total = tot;
+  return before + v;
+}
+
+// smallest position of the sorted list whose prefix weight reaches `need`
+__device__ int first_crossing(const unsigned long long* list, int tot, unsigned long long need,
+                              float smax, SelShared& S) {
+  unsigned long long carry = 0;
+  if (threadIdx.x == 0) S.bsel[3] = tot - 1;
+  __syncthreads();
+  for (int c0 = 0; c0 < tot; c0 += blockDim.x) {
+    int i = c0 + threadIdx.x;
+    unsigned long long w = i < tot ? weight_of(key2f((uint32_t)(list[i] >> 32)), smax) : 0ull;
+    unsigned long long chunk_total;
+    unsigned long long incl = block_incl_scan(w, S.red64, &chunk_total);
+    if (i < tot && carry + incl >= need) atomicMin(&S.bsel[3], i);
+    __syncthreads();
+    if (S.bsel[3] < c0 + (int)blockDim.x && S.bsel[3] < tot - 1) break;
+    carry += chunk_total;
+    __syncthreads();
+  }
+  int r = S.bsel[3];
+  __syncthreads();
+  return r;
+}
+
+// Exact position search inside one bucket: returns in *out_key the key of the
+// element at 0-based order position `pos` among the elements of bucket b
+// (order: key desc, index asc) and in *out_ties the number of elements at
+// positions <= pos holding that same key.  Uses the shared list when the
+// bucket fits, else a bitwise search over keys.
+__device__ void bucket_position(const float* __restrict__ row, int n, float smax, int b,
+                                int64_t pos, SelShared& S, uint32_t* out_key,
+                                int64_t* out_ties) {
+  if (threadIdx.x == 0) S.lcount = 0;
+  __syncthreads();
+  // count first
+  uint32_t c = 0;
+  for (int j = threadIdx.x; j < n; j += blockDim.x)
+    if (bucket_of(row[j], smax) == b) c++;
+  uint32_t tot = block_sum<uint32_t>(c, S.red32);
+  if (tot <= (uint32_t)kSortCap) {
+    for (int j = threadIdx.x; j < n; j += blockDim.x) {
+      float s = row[j];
+      if (bucket_of(s, smax) == b) {
+        uint32_t slot = atomicAdd(&S.lcount, 1u);
+        S.list[slot] = ((unsigned long long)f2key(s) << 32) | (uint32_t)(~(uint32_t)j);
+      }
+    }
+    __syncthreads();
+    sort_desc(S.list, (int)tot);
+    uint32_t key = (uint32_t)(S.list[pos] >> 32);
+    // ties of that key at positions <= pos
+    uint32_t t = 0;
+    for (int i = threadIdx.x; i <= pos; i += blockDim.x)
+      if ((uint32_t)(S.list[i] >> 32) == key) t++;
+    uint32_t ties = block_sum<uint32_t>(t, S.red32);
+    *out_key = key;
+    *out_ties = ties;
+  } else {
+    // bitwise search for the largest key K with count(bucket b, key >= K) > pos
+    uint32_t K = 0;
+    for (int bit = 31; bit >= 0; bit--) {
+      uint32_t cand = K | (1u << bit);
+      uint32_t cc = 0;
+      for (int j = threadIdx.x; j < n; j += blockDim.x) {
+        float s = row[j];
+        if (bucket_of(s, smax) == b && f2key(s) >= cand) cc++;
+      }
+      uint32_t tc = block_sum<uint32_t>(cc, S.red32);
+      if ((int64_t)tc > pos) K = cand;
+    }
+    uint32_t gt = 0;
+    for (int j = threadIdx.x; j < n; j += blockDim.x) {
+      float s = row[j];
+      if (bucket_of(s, smax) == b && f2key(s) > K) gt++;
+    }
+    uint32_t tg = block_sum<uint32_t>(gt, S.red32);
+    *out_key = K;
+    *out_ties = pos - (int64_t)tg + 1;
+  }
+  __syncthreads();
+}
+
+// Per query block row: count of selected key blocks, the threshold key and
+// the number of threshold-key ties to take.  S_i = first max(k, L*) keys in
+// the order (score desc, index asc), L* = shortest prefix whose integer
+// softmax weights reach ceil(p 2^32) Z / 2^32 (Z = row total).
+__global__ __launch_bounds__(kSelThreads) void k_select_count(
+    const float* __restrict__ scores, int n, int64_t g0, int k_count, float k_frac, float p,
+    int32_t* __restrict__ row_cnt, uint32_t* __restrict__ row_key,
+    int32_t* __restrict__ row_tie) {
+  __shared__ SelShared S;
+  const int i = blockIdx.x;
+  const float* row = scores + (int64_t)i * n;
+  const int64_t g = g0 + i;
+  int64_t kk = k_count;
+  if (k_frac > 0.0f) kk = (int64_t)ceil((double)k_frac * (double)n);
+  if (kk > n) kk = n;
+  if (kk < 0) kk = 0;
+  if (p >= 1.0f) {  // every block
+    if (threadIdx.x == 0) {
+      row_cnt[g] = n;
+      row_key[g] = 0u;
+      row_tie[g] = 0;
+    }
+    return;
+  }
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) mx = fmaxf(mx, row[j]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if ((threadIdx.x & 63) == 0) S.redf[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  float smax = S.redf[0];
+  for (int w = 1; w < kSelThreads / 64; w++) smax = fmaxf(smax, S.redf[w]);
+  __syncthreads();
+
+  // bucket histograms (count, weight) in order of descending score
+  const int wv = threadIdx.x >> 6;
+  for (int b = threadIdx.x; b < 4 * 256; b += blockDim.x) {
+    (&S.cnt[0][0])[b] = 0;
+    (&S.wt[0][0])[b] = 0ull;
+  }
+  __syncthreads();
+  const bool need_w = p > 0.0f;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    float s = row[j];
+    int b = bucket_of(s, smax);
+    atomicAdd(&S.cnt[wv][b], 1u);
+    if (need_w) atomicAdd(&S.wt[wv][b], (unsigned long long)weight_of(s, smax));
+  }
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    int b = threadIdx.x;
+    S.cnt[0][b] = S.cnt[0][b] + S.cnt[1][b] + S.cnt[2][b] + S.cnt[3][b];
+    S.wt[0][b] = S.wt[0][b] + S.wt[1][b] + S.wt[2][b] + S.wt[3][b];
+  }
+  __syncthreads();
+
+  int64_t L = 0;
+  uint32_t keyL = 0;
+  int64_t tieL = 0;
+  if (need_w) {
+    if (threadIdx.x == 0) {
+      unsigned long long Zt = 0;
+      for (int b = 0; b < 256; b++) Zt += S.wt[0][b];
+      unsigned long long P32 = (unsigned long long)ceil((double)p * 4294967296.0);
+      // Wstar = ceil(P32 * Z / 2^32) without overflow: P32 <= 2^32
+      unsigned long long zh = Zt >> 32, zl = Zt & 0xffffffffull;
+      unsigned long long Wstar = P32 * zh + ((P32 * zl + 0xffffffffull) >> 32);
+      unsigned long long wa = 0;
+      uint32_t ca = 0;
+      int bs = 255;
+      for (int b = 0; b < 256; b++) {
+        if (wa + S.wt[0][b] >= Wstar) {
+          bs = b;
+          break;
+        }
+        wa += S.wt[0][b];
+        ca += S.cnt[0][b];
+      }
+      S.bsel[0] = bs;
+      S.above_w[0] = Wstar - wa;  // weight still needed inside bucket bs
+      S.above_c[0] = ca;
+    }
+    __syncthreads();
+    const int bs = S.bsel[0];
+    const unsigned long long need = S.above_w[0];
+    const uint32_t ca = S.above_c[0];
+    // exact crossing inside bucket bs: collect, sort, prefix weights
+    if (threadIdx.x == 0) S.lcount = 0;
+    __syncthreads();
+    uint32_t c = 0;
+    for (int j = threadIdx.x; j < n; j += blockDim.x)
+      if (bucket_of(row[j], smax) == bs) c++;
+    uint32_t tot = block_sum<uint32_t>(c, S.red32);
+    if (tot <= (uint32_t)kSortCap) {
+      for (int j = threadIdx.x; j < n; j += blockDim.x) {
+        float s = row[j];
+        if (bucket_of(s, smax) == bs) {
+          uint32_t slot = atomicAdd(&S.lcount, 1u);
+          S.list[slot] = ((unsigned long long)f2key(s) << 32) | (uint32_t)(~(uint32_t)j);
+        }
+      }
+      __syncthreads();
+      sort_desc(S.list, (int)tot);
+      L = (int64_t)ca + first_crossing(S.list, (int)tot, need, smax, S) + 1;
+    } else {
+      // bucket too large for the list: bitwise search for the crossing key
+      uint32_t K = 0;
+      for (int bit = 31; bit >= 0; bit--) {
+        uint32_t cand = K | (1u << bit);
+        unsigned long long wsum = 0;
+        for (int j = threadIdx.x; j < n; j += blockDim.x) {
+          float s = row[j];
+          if (bucket_of(s, smax) == bs && f2key(s) >= cand) wsum += weight_of(s, smax);
+        }
+        unsigned long long tw = block_sum<unsigned long long>(wsum, S.red64);
+        if (tw >= need) K = cand;
+      }
+      unsigned long long wg = 0;
+      uint32_t cg = 0;
+      for (int j = threadIdx.x; j < n; j += blockDim.x) {
+        float s = row[j];
+        if (bucket_of(s, smax) == bs && f2key(s) > K) {
+          wg += weight_of(s, smax);
+          cg++;
+        }
+      }
+      unsigned long long twg = block_sum<unsigned long long>(wg, S.red64);
+      uint32_t tcg = block_sum<uint32_t>(cg, S.red32);
+      unsigned long long wk = weight_of(key2f(K), smax);
+      unsigned long long rest = need - twg;
+      L = (int64_t)ca + tcg + (int64_t)((rest + wk - 1) / wk);
+    }
+  }
+  int64_t nsel = kk > L ? kk : L;
+  if (nsel > n) nsel = n;
+  if (nsel == 0) {
+    keyL = 0xffffffffu;
+    tieL = 0;
+  } else {
+    // key of the nsel-th element in order and ties to take
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t ca = 0;
+      int bs = 255;
+      for (int b = 0; b < 256; b++) {
+        if ((int64_t)ca + S.cnt[0][b] >= nsel) {
+          bs = b;
+          break;
+        }
+        ca += S.cnt[0][b];
+      }
+      S.bsel[2] = bs;
+      S.above_c[1] = ca;
+    }
+    __syncthreads();
+    bucket_position(row, n, smax, S.bsel[2], nsel - 1 - (int64_t)S.above_c[1], S, &keyL,
+                    &tieL);
+  }
+  if (threadIdx.x == 0) {
+    row_cnt[g] = (int32_t)nsel;
+    row_key[g] = keyL;
+    row_tie[g] = (int32_t)tieL;
+  }
+}
+
+// Exclusive scan of a head's row counts into row_ptr (base = running total in
+// counters[0]); one block of 1024 threads.
+__global__ __launch_bounds__(1024) void k_scan_rows(const int32_t* __restrict__ cnt, int n,
+                                                    int64_t g0, int64_t* __restrict__ ptr,
+                                                    int64_t* __restrict__ counters,
+                                                    int last) {
+  __shared__ int64_t sh[1024];
+  int64_t carry = counters[0];
+  for (int i0 = 0; i0 < n; i0 += 1024) {
+    int i = i0 + threadIdx.x;
+    int64_t v = i < n ? cnt[g0 + i] : 0;
+    sh[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      int64_t a = threadIdx.x >= off ? sh[threadIdx.x - off] : 0;
+      __syncthreads();
+      sh[threadIdx.x] += a;
+      __syncthreads();
+    }
+    if (i < n) ptr[g0 + i] = carry + sh[threadIdx.x] - v;
+    carry += sh[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    counters[0] = carry;
+    if (last) ptr[g0 + n] = carry;
+  }
+}
+
+// Emit each row's selected key blocks in ascending index order; also the
+// row's attention cost B_i * sum_j B_j.
+__global__ __launch_bounds__(256) void k_select_fill(
+    const float* __restrict__ scores, int n, int64_t g0, const int32_t* __restrict__ row_cnt,
+    const uint32_t* __restrict__ row_key, const int32_t* __restrict__ row_tie,
+    const int64_t* __restrict__ row_ptr, int64_t cap, const uint8_t* __restrict__ blk_shape,
+    int32_t* __restrict__ col_idx, int64_t* __restrict__ row_cost) {
+  __shared__ int sh_a[256], sh_b[256];
+  __shared__ int64_t sh_cost[4];
+  const int i = blockIdx.x;
+  const int64_t g = g0 + i;
+  const float* row = scores + (int64_t)i * n;
+  const uint32_t K = row_key[g];
+  const int tie = row_tie[g];
+  const int64_t base = row_ptr[g];
+  const bool fits = base + row_cnt[g] <= cap;
+  int tie_carry = 0, out_carry = 0;
+  int64_t cost = 0;
+  for (int j0 = 0; j0 < n; j0 += 256) {
+    int j = j0 + threadIdx.x;
+    uint32_t key = j < n ? f2key(row[j]) : 0u;
+    int is_tie = (j < n && key == K) ? 1 : 0;
+    sh_a[threadIdx.x] = is_tie;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      int a = threadIdx.x >= off ? sh_a[threadIdx.x - off] : 0;
+      __syncthreads();
+      sh_a[threadIdx.x] += a;
+      __syncthreads();
+    }
+    int tie_rank = tie_carry + sh_a[threadIdx.x] - is_tie;
+    int sel = (j < n) && (key > K || (is_tie && tie_rank < tie));
+    tie_carry += sh_a[255];
+    sh_b[threadIdx.x] = sel;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      int a = threadIdx.x >= off ? sh_b[threadIdx.x - off] : 0;
+      __syncthreads();
+      sh_b[threadIdx.x] += a;
+      __syncthreads();
+    }
+    if (sel) {
+      int pos = out_carry + sh_b[threadIdx.x] - 1;
+      if (fits) col_idx[base + pos] = j;
+      cost += d_shapes[blk_shape[g0 + j]].volume;
+    }
+    out_carry += sh_b[255];
+    __syncthreads();
+  }
+  int64_t c = block_sum<int64_t>(cost, sh_cost);
+  if (threadIdx.x == 0) row_cost[g] = c * (int64_t)d_shapes[blk_shape[g]].volume;
+}
+
+// ============================================================ K7: key-major lists
+// For each key block, the query blocks whose S_i contains it, ascending.
+__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// per chunk of 64 query rows: column histograms (integer atomics)
+__global__ __launch_bounds__(256) void k_colt_count(const int64_t* __restrict__ row_ptr,
+                                                    const int32_t* __restrict__ col_idx, int n,
+                                                    int64_t g0, int32_t* __restrict__ chunk_cnt,
+                                                    int32_t* __restrict__ colt_cnt) {
+  const int c = blockIdx.x;
+  const int i0 = c * 64, i1 = min(n, i0 + 64);
+  for (int i = i0; i < i1; i++) {
+    int64_t a = row_ptr[g0 + i], b = row_ptr[g0 + i + 1];
+    for (int64_t e = a + threadIdx.x; e < b; e += blockDim.x) {
+      int j = col_idx[e];
+      atomicAdd(&chunk_cnt[(int64_t)c * n + j], 1);
+      atomicAdd(&colt_cnt[j], 1);
+    }
+  }
+}
+
+// per column: turn the chunk counts into absolute output positions
+__global__ void k_colt_offsets(const int64_t* __restrict__ colt_ptr, int n, int64_t g0,
+                               int nch, int32_t* __restrict__ chunk_cnt) {
+  int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  int64_t run = colt_ptr[g0 + j];
+  for (int c = 0; c < nch; c++) {
+    int32_t t = chunk_cnt[(int64_t)c * n + j];
+    chunk_cnt[(int64_t)c * n + j] = (int32_t)(run);
+    run += t;
+  }
+}
+
+// per chunk: rows in ascending order, each row's entries in parallel
+__global__ __launch_bounds__(256) void k_colt_fill(const int64_t* __restrict__ row_ptr,
+                                                   const int32_t* __restrict__ col_idx, int n,
+                                                   int64_t g0, int32_t* __restrict__ chunk_cnt,
+                                                   int32_t* __restrict__ colt_idx) {
+  const int c = blockIdx.x;
+  const int i0 = c * 64, i1 = min(n, i0 + 64);
+  for (int i = i0; i < i1; i++) {
+    int64_t a = row_ptr[g0 + i], b = row_ptr[g0 + i + 1];
+    for (int64_t e = a + threadIdx.x; e < b; e += blockDim.x) {
+      int j = col_idx[e];
+      int pos = atomicAdd(&chunk_cnt[(int64_t)c * n + j], 1);
+      colt_idx[pos] = i;
+    }
+    __syncthreads();
+  }
+}
+
+// key-major scan: counts per column -> pointers (reuses k_scan_rows on colt_cnt)
+
+// first global block id of each head (prefix over heads of N_blk)
+__global__ void k_blk_off(const int32_t* __restrict__ nblk, int heads, int64_t* __restrict__ off) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    int64_t a = 0;
+    for (int h = 0; h < heads; h++) {
+      off[h] = a;
+      a += nblk[h];
+    }
+    off[heads] = a;
+  }
+}
+
+// original token of every permuted row, [heads][N]
+__global__ void k_perm_map(const uint8_t* __restrict__ shape_id, int H, int W, int Z,
+                           int64_t N, int heads, int32_t* __restrict__ out) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)heads * N) return;
+  int h = (int)(i / N);
+  int64_t p = i - (int64_t)h * N;
+  int m = (int)(p >> 9), r = (int)(p & 511);
+  out[i] = (int32_t)token_of(d_shapes[shape_id[(int64_t)h * Z + m]], m, r, H, W);
+}
+
+__global__ __launch_bounds__(256) void k_sum_i64(const int64_t* __restrict__ in, int64_t n,
+                                                 int64_t* __restrict__ out) {
+  __shared__ int64_t sh[4];
+  int64_t s = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) s += in[i];
+  s = block_sum<int64_t>(s, sh);
+  if (threadIdx.x == 0) *out = s;
+}
+
+// ============================================================ launchers
+bool launch_blk_off(const PlanDev& P, hipStream_t st) {
+  hipLaunchKernelGGL(k_blk_off, dim3(1), dim3(64), 0, st, P.nblk, P.heads, P.blk_off);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_perm_map(const PlanDev& P, int32_t* out, hipStream_t st) {
+  int64_t tot = (int64_t)P.heads * P.N;
+  hipLaunchKernelGGL(k_perm_map, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
+                     P.shape_id, P.H, P.W, P.Z, P.N, P.heads, out);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_sum_i64(const int64_t* in, int64_t n, int64_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_sum_i64, dim3(1), dim3(256), 0, st, in, n, out);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_zone_stats(const void* v, int dtype, int D, int H, int W, int Z, int heads,
+                       int64_t N, float* out, hipStream_t st) {
+  dim3 grid(heads * Z), block(64);
+  if (dtype == PRISM_BF16 && D == 128)
+    hipLaunchKernelGGL((k_zone_stats<1, 2>), grid, block, 0, st, v, H, W, Z, N, out);
+  else if (dtype == PRISM_BF16 && D == 64)
+    hipLaunchKernelGGL((k_zone_stats<1, 1>), grid, block, 0, st, v, H, W, Z, N, out);
+  else if (dtype == PRISM_F32 && D == 64)
+    hipLaunchKernelGGL((k_zone_stats<0, 1>), grid, block, 0, st, v, H, W, Z, N, out);
+  else if (dtype == PRISM_F32 && D == 128)
+    hipLaunchKernelGGL((k_zone_stats<0, 2>), grid, block, 0, st, v, H, W, Z, N, out);
+  else
+    return false;
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_audio_stats(const float* a, int H, int W, int Z, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_audio_stats, dim3((Z + 63) / 64), dim3(64), 0, st, a, H, W, Z, out);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_shapes(const PlanDev& P, int have_audio, const prism_config& c, int fixed_id,
+                   hipStream_t st) {
+  hipLaunchKernelGGL(k_shapes, dim3(P.heads), dim3(256), 0, st, P.vstats, P.astats, have_audio,
+                     P.Z, c.eps, c.tau128, c.tau256, c.volume_mask, fixed_id, P.shape_id,
+                     P.zone_base, P.nblk);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_permute_pool(const PlanDev& P, const void* q, const void* k, const void* v,
+                         hipStream_t st) {
+  dim3 grid(P.heads * P.Z), block(512);
+#define PP_ARGS                                                                           \
+  q, k, v, P.H, P.W, P.Z, P.N, P.shape_id, P.zone_base, P.blk_off, P.kp, P.vp, P.blk_start, \
+      P.blk_shape, P.blk_head, P.qbar, P.kbar, P.qgrid, P.kgrid, P.qexp, P.kexp
+  if (P.dtype == PRISM_BF16 && P.D == 128)
+    hipLaunchKernelGGL((k_permute_pool<1, 2, true>), grid, block, 0, st, PP_ARGS);
+  else if (P.dtype == PRISM_BF16 && P.D == 64)
+    hipLaunchKernelGGL((k_permute_pool<1, 1, false>), grid, block, 0, st, PP_ARGS);
+  else if (P.dtype == PRISM_F32 && P.D == 64)
+    hipLaunchKernelGGL((k_permute_pool<0, 1, false>), grid, block, 0, st, PP_ARGS);
+  else if (P.dtype == PRISM_F32 && P.D == 128)
+    hipLaunchKernelGGL((k_permute_pool<0, 2, false>), grid, block, 0, st, PP_ARGS);
+  else
+    return false;
+#undef PP_ARGS
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_block_scores(const PlanDev& P, int64_t g0, int n, float* out, hipStream_t st) {
+  if (n <= 0) return true;
+  float cD = (float)(1.0 / sqrt((double)P.D));
+  dim3 grid((n + 127) / 128, (n + 127) / 128), block(256);
+  if (P.D == 128)
+    hipLaunchKernelGGL((k_block_scores<128>), grid, block, 0, st, P.qgrid, P.kgrid, P.qexp,
+                       P.kexp, g0, n, cD, out);
+  else
+    hipLaunchKernelGGL((k_block_scores<64>), grid, block, 0, st, P.qgrid, P.kgrid, P.qexp,
+                       P.kexp, g0, n, cD, out);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_select(const PlanDev& P, int64_t g0, int n, const prism_config& c, int last,
+                   hipStream_t st) {
+  if (n > 0)
+    hipLaunchKernelGGL(k_select_count, dim3(n), dim3(kSelThreads), 0, st, P.scores, n, g0,
+                       c.top_k, c.top_k_frac, c.top_p, P.row_cnt, P.row_key, P.row_tie);
+  hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, st, P.row_cnt, n, g0, P.row_ptr,
+                     P.counters, last);
+  if (n > 0)
+    hipLaunchKernelGGL(k_select_fill, dim3(n), dim3(256), 0, st, P.scores, n, g0, P.row_cnt,
+                       P.row_key, P.row_tie, P.row_ptr, P.cap, P.blk_shape, P.col_idx,
+                       P.row_cost);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_transpose(const PlanDev& P, int64_t g0, int n, int last, hipStream_t st) {
+  if (n <= 0) return true;
+  int nch = (n + 63) / 64;
+  int64_t cells = (int64_t)nch * n;
+  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((cells + 255) / 256)), dim3(256), 0, st,
+                     P.chunk_cnt, cells, 0);
+  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, st, P.colt_cnt + g0,
+                     (int64_t)n, 0);
+  hipLaunchKernelGGL(k_colt_count, dim3(nch), dim3(256), 0, st, P.row_ptr, P.col_idx, n, g0,
+                     P.chunk_cnt, P.colt_cnt + g0);
+  hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, st, P.colt_cnt, n, g0, P.colt_ptr,
+                     P.counters + 1, last);
+  hipLaunchKernelGGL(k_colt_offsets, dim3((n + 255) / 256), dim3(256), 0, st, P.colt_ptr, n,
+                     g0, nch, P.chunk_cnt);
+  hipLaunchKernelGGL(k_colt_fill, dim3(nch), dim3(256), 0, st, P.row_ptr, P.col_idx, n, g0,
+                     P.chunk_cnt, P.colt_idx);
+  return hipGetLastError() == hipSuccess;
+}
+
+}  // namespace prism

@@ -1,0 +1,197 @@
+/*
+ * prism.h -- C ABI of an MI355X (gfx950) implementation of Prism's dynamic
+ * block-sparse video self-attention ("Prism: Dynamic Sparse Attention for
+ * Native 2K Joint Video-Audio Generation Model Training", arXiv 2610.05416).
+ *
+ * The method (paper.rainbus.top, section "方法步骤详情", five stages; formulas
+ * on xyznot.com/id, "Metode" 1-3):
+ *   1. per 8x8x8 macro-zone and head: directional variance ratio r_{v,d} of
+ *      the axis-mean-pooled V, audio coupling abar and directional variance
+ *      vhat_{a,d} of the cached A->V cross-attention norm map, indicator
+ *      g_d = r_{v,d} + abar vhat_{a,d} + eps, density rho -> block volume
+ *      B in {64,128,256}, block shape nearest (in log2 space) to the
+ *      continuous optimum b_d ~ g_d^(-1/2) among 16 candidates;
+ *   2. zone-aware re-layout of the tokens into block-contiguous order;
+ *   3. mean-pooled block representatives, block scores
+ *      P_i = softmax(Qbar_i Kbar^T / sqrt(D)), S_i = TopK(P_i,k) U TopP(P_i,p);
+ *   4. attention of every query block over the tokens of S_i only;
+ *   5. results back in the original token order.
+ * The plan (stages 1-3) is a constant for the backward pass: gradients flow
+ * only through attention on the selected blocks (same page, "技术新颖性").
+ *
+ * Conventions for every entry point:
+ *   - tensors are contiguous [heads][T*H*W][head_dim], token n =
+ *     (t*H + h)*W + w (row-major t, h, w), element type cfg->dtype;
+ *   - every tensor pointer is DEVICE memory unless stated otherwise;
+ *   - `stream` is a hipStream_t (NULL = the default stream); all device work
+ *     is enqueued on it, and a call returns once its work is enqueued except
+ *     where a host read-back is stated;
+ *   - the library allocates no device memory: the caller provides every
+ *     buffer and the plan workspace, and keeps them alive while a plan that
+ *     points into them is in use;
+ *   - no call aborts or prints; failures are returned as prism_status.
+ *     Asynchronous device faults surface as PRISM_EDEVICE from a later call.
+ *   - plans may be used from any host thread, but two calls that use one
+ *     plan must not run concurrently on different streams.
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PRISM_OK = 0,
+  PRISM_EINVAL = 1,             /* bad argument: NULL pointer, size, hyper-parameter */
+  PRISM_EUNSUPPORTED = 2,       /* valid, but not provided (dtype / head_dim combination) */
+  PRISM_ENOMEM_WORKSPACE = 3,   /* caller's workspace too small; see *_needed outputs */
+  PRISM_EDEVICE = 4,            /* HIP runtime reported an error */
+  PRISM_ESTATE = 5              /* arguments do not match the plan they are used with */
+} prism_status;
+
+typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
+
+/* Hyper-parameters and problem size.  Defaults (prism_config_default) are
+ * the pages' constants: eps = 1e-4, tau_128 = 0.5, tau_256 = 0.25
+ * (paper.rainbus.top "方法步骤详情" and "复现评估"). */
+typedef struct {
+  int32_t T, H, W;        /* token grid; each a positive multiple of 8 (zones are 8x8x8) */
+  int32_t heads;          /* >= 1 */
+  int32_t head_dim;       /* 64 or 128; the bf16 attention kernels take 128 */
+  int32_t dtype;          /* prism_dtype of Q, K, V, O, dO, dQ, dK, dV */
+  int32_t top_k;          /* Top-k size in key blocks (>= 0, clamped to the head's block count) */
+  float top_k_frac;       /* > 0: Top-k size = ceil(top_k_frac * N_blk) instead of top_k */
+  float top_p;            /* Top-p mass in [0, inf); >= 1 selects every block, 0 = Top-k only */
+  uint32_t volume_mask;   /* allowed volumes: bit0 = 64, bit1 = 128, bit2 = 256 (nonzero) */
+  int32_t fixed_shape[3]; /* {0,0,0}: dynamic shapes; else one (bT,bH,bW) candidate for all zones */
+  float eps;              /* indicator floor, added to every g_d */
+  float tau128;           /* rho < tau128 -> volume >= 128 */
+  float tau256;           /* rho < tau256 -> volume 256 */
+  int32_t need_backward;  /* nonzero: also build the key-major lists prism_attn_bwd needs */
+} prism_config;
+
+/* Opaque plan: block shapes, block table and selected key-block lists of
+ * one layer call.  Host object; its device arrays live in the caller's
+ * workspace. */
+typedef struct prism_plan_s prism_plan_t;
+
+/* Fill *cfg with the defaults above (T=H=W=8, heads=1, head_dim=128, bf16,
+ * top_k=16, top_p=0.9, all volumes, dynamic shapes, need_backward=1). */
+void prism_config_default(prism_config* cfg);
+
+/* Host-only validation of a configuration; no device work. */
+prism_status prism_config_check(const prism_config* cfg);
+
+/* Bytes of device workspace prism_plan needs for `cfg` when up to
+ * nnz_capacity (query block, key block) pairs may be selected over all
+ * heads.  nnz_capacity < 0 asks for the worst case (every block selected).
+ * Host-only. */
+prism_status prism_plan_workspace_size(const prism_config* cfg, int64_t nnz_capacity,
+                                       size_t* bytes);
+
+/* Stages 1-3 plus the re-layout of K and V (stage 2): builds a plan.
+ *   q, k, v       device [heads][N][head_dim] of cfg->dtype
+ *   av_norm       device [N] float32 A->V norm map cached from the previous
+ *                 layer, or NULL for the first layer (g = r + eps)
+ *   workspace     device buffer of workspace_bytes; at least
+ *                 prism_plan_workspace_size(cfg, nnz_capacity) where
+ *                 nnz_capacity is derived from workspace_bytes
+ *   plan_out      receives a new plan (free with prism_plan_destroy)
+ *   nnz_out       receives the number of selected (query block, key block)
+ *                 pairs over all heads (may be NULL)
+ * Reads back two small arrays to the host (per-head block counts and the
+ * pair count), so it synchronises `stream` twice.  If the selection does not
+ * fit the workspace it returns PRISM_ENOMEM_WORKSPACE with *nnz_out set to
+ * the pair count needed and no plan.  The permuted K/V kept in the
+ * workspace are read by prism_attn_fwd/bwd: k and v must not change while
+ * the plan is used. */
+prism_status prism_plan_create(const prism_config* cfg, const void* q, const void* k,
+                               const void* v, const float* av_norm, void* workspace,
+                               size_t workspace_bytes, void* stream, prism_plan_t** plan_out,
+                               int64_t* nnz_out);
+
+void prism_plan_destroy(prism_plan_t* plan);
+
+/* Stage 4-5 forward: O = softmax over the selected key tokens of
+ * (q k^T / sqrt(head_dim)) times v, for every query token, written in the
+ * original token order; lse [heads][N] float32 (natural log of the softmax
+ * normaliser), needed by the backward pass.
+ * q, k, v must be the tensors the plan was built from (k and v are checked
+ * by address: PRISM_ESTATE otherwise).  o: device [heads][N][head_dim]. */
+prism_status prism_attn_fwd(const prism_plan_t* plan, const void* q, const void* k,
+                            const void* v, void* o, float* lse, void* stream);
+
+/* Bytes of device workspace prism_attn_bwd needs.  Host-only. */
+prism_status prism_attn_bwd_workspace_size(const prism_config* cfg, size_t* bytes);
+
+/* Backward with the plan held constant: given dO = dL/dO, writes
+ * dq, dk, dv (device [heads][N][head_dim], original token order).
+ * o and lse are those prism_attn_fwd produced for the same plan and inputs.
+ * Needs a plan built with need_backward; key blocks that no query block
+ * selected receive zero gradient.  Deterministic (no floating-point
+ * atomics). */
+prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void* k,
+                            const void* v, const void* o, const float* lse, const void* d_o,
+                            void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Block scores of one head (stage 3): out_scores device float32
+ * [N_blk(head)][N_blk(head)], s_ij = Qbar_i . Kbar_j / sqrt(head_dim) with
+ * both means on the integer grid of prism_plan_export's QGRID/KGRID. */
+prism_status prism_block_scores(const prism_plan_t* plan, int32_t head, float* out_scores,
+                                void* stream);
+
+/* Plan arrays that can be copied out for inspection. */
+typedef enum {
+  PRISM_ARR_ZONE_STATS = 0,   /* float32 [heads][Z][5]: sigma2_T, sigma2_H, sigma2_W, SV, TV */
+  PRISM_ARR_AUDIO_STATS = 1,  /* float32 [Z][4]: audio sigma2_T, _H, _W, zone mean (zeros if no map) */
+  PRISM_ARR_SHAPE_ID = 2,     /* uint8 [heads][Z]: candidate id (see prism_candidate) */
+  PRISM_ARR_BLK_OFF = 3,      /* int64 [heads+1]: first global block id of each head */
+  PRISM_ARR_BLK_START = 4,    /* int32 [G]: first permuted row of each block within its head */
+  PRISM_ARR_QBAR = 5,         /* float32 [G][head_dim]: block-mean of Q */
+  PRISM_ARR_KBAR = 6,         /* float32 [G][head_dim]: block-mean of K */
+  PRISM_ARR_QEXP = 7,         /* int32 [G]: E with Qbar ~ 2^E * QGRID */
+  PRISM_ARR_KEXP = 8,         /* int32 [G] */
+  PRISM_ARR_ROW_PTR = 9,      /* int64 [G+1]: CSR row pointer over global query blocks */
+  PRISM_ARR_COL_IDX = 10,     /* int32 [nnz]: selected key blocks (local ids, ascending) */
+  PRISM_ARR_COLT_PTR = 11,    /* int64 [G+1]: key-major pointer (need_backward) */
+  PRISM_ARR_COLT_IDX = 12,    /* int32 [nnz]: query blocks selecting each key block, ascending */
+  PRISM_ARR_PERM = 13,        /* int32 [heads][N]: original token of each permuted row */
+  PRISM_ARR_QGRID = 14,       /* uint16 (bf16 bits) [G][head_dim]: integer grid of Qbar */
+  PRISM_ARR_KGRID = 15        /* uint16 (bf16 bits) [G][head_dim] */
+} prism_array;
+
+/* Size in bytes of a plan array. Host-only. */
+prism_status prism_plan_array_bytes(const prism_plan_t* plan, int32_t which, size_t* bytes);
+
+/* Copy a plan array into HOST memory dst (dst_bytes >= its size);
+ * synchronises `stream`. */
+prism_status prism_plan_export(const prism_plan_t* plan, int32_t which, void* dst,
+                               size_t dst_bytes, void* stream);
+
+/* Host-side plan summary. */
+typedef struct {
+  int64_t total_blocks;       /* G = sum over heads of N_blk */
+  int64_t nnz;                /* selected (query block, key block) pairs */
+  int64_t max_blocks_per_head;
+  double pair_tokens;         /* sum over selected pairs of B_i * B_j */
+  int64_t shape_hist[16];     /* zones per candidate shape, over all heads */
+} prism_plan_info_t;
+
+/* Fills *info; pair_tokens needs one device read-back (synchronises). */
+prism_status prism_plan_info(const prism_plan_t* plan, prism_plan_info_t* info, void* stream);
+
+/* Candidate shape table, id order: by volume, then lexicographic (bT,bH,bW).
+ * Writes bT, bH, bW, B of candidate `id` (0..15). Host-only. */
+prism_status prism_candidate(int32_t id, int32_t* out4);
+
+const char* prism_status_str(prism_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PRISM_H */

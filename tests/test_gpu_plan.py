@@ -1,0 +1,148 @@
+"""Parity of the plan stages on the GPU with the CPU oracle: zone statistics,
+shapes, block table, permutation, pooled means and their integer grid, block
+scores and the selected key-block lists must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from dynamic_block_sparse_zone_amd import synth
+from tests.helpers import csr_rows, gpu_plan, host_bits, oracle_config, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def prism():
+    import dynamic_block_sparse_zone_amd as p
+    return p
+
+
+def _case(prism, orc, name, use_audio=True, **over):
+    wl = synth.WORKLOADS[name]
+    x = synth.make_inputs(wl, device="cpu", with_grad=False)
+    print(f"[plan parity] workload={name} over={over} audio={use_audio}", flush=True)
+    dx = to_dev(x, DEV)
+    pl = gpu_plan(prism, wl, dx, use_audio=use_audio, **over)
+    torch.cuda.synchronize()
+    hb = host_bits(x)
+    cfg = oracle_config(orc, wl, **over)
+    opl = orc.plan(hb["q"], hb["k"], hb["v"], x["av"].numpy() if use_audio else None, cfg)
+    return wl, pl, opl
+
+
+def _check_plan_arrays(pl, opl, cfg):
+    H, Z = cfg.heads, cfg.Z
+    np.testing.assert_array_equal(pl.export("zone_stats").reshape(H, Z, 5), opl.vstats)
+    if opl.astats is not None:
+        np.testing.assert_array_equal(pl.export("audio_stats").reshape(Z, 4), opl.astats)
+    np.testing.assert_array_equal(pl.export("shape_id").reshape(H, Z), opl.shape_id)
+    np.testing.assert_array_equal(pl.export("blk_off"), opl.blk_off)
+    G = int(opl.blk_off[-1])
+    start = pl.export("blk_start")
+    np.testing.assert_array_equal(start[:G], opl.blk_start)
+    np.testing.assert_array_equal(pl.export("perm").reshape(H, -1), opl.perm)
+    D = cfg.head_dim
+    np.testing.assert_array_equal(pl.export("qbar").reshape(G, D), opl.qbar)
+    np.testing.assert_array_equal(pl.export("kbar").reshape(G, D), opl.kbar)
+    np.testing.assert_array_equal(pl.export("qexp"), opl.qexp)
+    np.testing.assert_array_equal(pl.export("kexp"), opl.kexp)
+    qg = pl.export("qgrid").reshape(G, D)
+    kg = pl.export("kgrid").reshape(G, D)
+    to_f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    np.testing.assert_array_equal(to_f(qg), opl.qgrid)
+    np.testing.assert_array_equal(to_f(kg), opl.kgrid)
+
+
+def _check_csr(pl, opl, orc, rows_per_head=None, seed=0):
+    cfg = opl.cfg
+    row_ptr = pl.export("row_ptr")
+    col = pl.export("col_idx")
+    assert row_ptr[-1] == pl.nnz == len(col)
+    rng = np.random.default_rng(seed)
+    checked = 0
+    for h in range(cfg.heads):
+        n = opl.nblk(h)
+        rows = range(n) if rows_per_head is None else rng.choice(n, min(n, rows_per_head),
+                                                                replace=False)
+        for i in rows:
+            g = int(opl.blk_off[h]) + int(i)
+            got = csr_rows(row_ptr, col, g)
+            want = orc.select_row(opl, h, int(i))
+            assert np.array_equal(got, want), (h, i, got[:10], want[:10])
+            checked += 1
+        # every row, any size: ascending, in range, at least k long
+        k = cfg.k_for(n)
+        for i in range(n):
+            r = csr_rows(row_ptr, col, int(opl.blk_off[h]) + i)
+            assert len(r) >= k and (len(r) == 0 or (r[0] >= 0 and r[-1] < n))
+            assert np.all(np.diff(r) > 0)
+    return checked
+
+
+def _check_transpose(pl, opl):
+    cfg = opl.cfg
+    row_ptr, col = pl.export("row_ptr"), pl.export("col_idx")
+    tp, tc = pl.export("colt_ptr"), pl.export("colt_idx")
+    assert tp[-1] == len(col) == len(tc)
+    for h in range(cfg.heads):
+        o, n = int(opl.blk_off[h]), opl.nblk(h)
+        lists = [[] for _ in range(n)]
+        for i in range(n):
+            for j in csr_rows(row_ptr, col, o + i):
+                lists[j].append(i)
+        for j in range(n):
+            assert np.array_equal(csr_rows(tp, tc, o + j), np.array(lists[j], np.int32)), (h, j)
+
+
+@pytest.mark.parametrize("name", ["tiny", "check", "small"])
+def test_plan_bit_exact(prism, orc, name):
+    wl, pl, opl = _case(prism, orc, name)
+    _check_plan_arrays(pl, opl, opl.cfg)
+    _check_csr(pl, opl, orc)
+    _check_transpose(pl, opl)
+    info = pl.info()
+    assert info["nnz"] == pl.nnz and info["total_blocks"] == int(opl.blk_off[-1])
+    hist = np.bincount(opl.shape_id.reshape(-1), minlength=16)
+    assert info["shape_hist"] == hist.tolist()
+
+
+def test_plan_first_layer_without_audio(prism, orc):
+    wl, pl, opl = _case(prism, orc, "check", use_audio=False)
+    _check_plan_arrays(pl, opl, opl.cfg)
+    _check_csr(pl, opl, orc)
+
+
+@pytest.mark.parametrize("over", [
+    {"top_p": 1.0},                    # every block
+    {"top_p": 0.0, "top_k": 5},        # Top-k only
+    {"top_p": 0.0, "top_k": 0},        # empty selection
+    {"top_k": 1000, "top_p": 0.5},     # k larger than the block count
+    {"top_k_frac": 0.05, "top_p": 0.2},  # the pages' operating point
+    {"fixed_shape": (4, 4, 8)},
+    {"volume_mask": 5},
+    {"tau128": 0.9, "tau256": 0.6},
+])
+def test_plan_variants(prism, orc, over):
+    wl, pl, opl = _case(prism, orc, "check", **over)
+    _check_plan_arrays(pl, opl, opl.cfg)
+    _check_csr(pl, opl, orc)
+
+
+def test_block_scores_bit_exact(prism, orc):
+    wl, pl, opl = _case(prism, orc, "small")
+    rng = np.random.default_rng(3)
+    for h in (0, wl.heads - 1):
+        s = prism.block_scores(pl, h).cpu().numpy()
+        for i in rng.choice(opl.nblk(h), 12, replace=False):
+            np.testing.assert_array_equal(s[i], orc.score_row(opl, h, int(i)))
+
+
+def test_plan_deterministic(prism):
+    wl = synth.WORKLOADS["small"]
+    dx = to_dev(synth.make_inputs(wl, device="cpu", with_grad=False), DEV)
+    a = gpu_plan(prism, wl, dx)
+    b = gpu_plan(prism, wl, dx)
+    for name in ("shape_id", "row_ptr", "col_idx", "colt_idx", "qbar", "zone_stats"):
+        assert np.array_equal(a.export(name), b.export(name)), name
