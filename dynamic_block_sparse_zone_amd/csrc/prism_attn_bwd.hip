@@ -1,10 +1,486 @@
-// Sparse attention backward (placeholder until the gfx950 kernels land).
+// Sparse attention backward with the plan held constant (paper.rainbus.top,
+// "技术新颖性": shapes and selections are detached, gradients flow only
+// through attention on the selected blocks).  With P = softmax over the
+// selected keys, dP = dO V^T, Delta = rowsum(dO * O), dS = P (dP - Delta):
+//   dV = P^T dO,  dK = dS^T Q / sqrt(D),  dQ = dS K / sqrt(D).
+//
+// gfx950 design (bf16, head_dim 128), deterministic (no atomics):
+//  * prep: Q and dO gathered into the permuted, swizzled tile layout of K/V;
+//    Delta and log2(e) * LSE per permuted row;
+//  * dK/dV: a work-group owns 128 permuted key rows (4 waves x 32 keys, K and
+//    V of its keys in registers) and walks the query blocks whose S_i holds
+//    its key blocks (key-major lists); Q and dO tiles are staged into LDS by
+//    direct global->LDS loads, double-buffered; per 32-query slice it forms
+//    S = Q K^T and dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS with
+//    the transposed operands read by ds_read_b64_tr_b16;
+//  * dQ: a work-group owns 128 permuted query rows and walks its key blocks
+//    as the forward does: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
 #include "prism_common.h"
 #include "prism_kernels.h"
 
 namespace prism {
-bool launch_attn_bwd(const PlanDev&, const BwdDev&, const void*, const void*, const float*,
-                     const void*, void*, void*, void*, hipStream_t) {
-  return false;
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4b;
+
+namespace {
+
+struct UIter {
+  const int32_t* col;
+  int64_t a, ae, b, be;
+  bool same;
+  __device__ bool next(int& j, int& fa, int& fb) {
+    if (same) {
+      if (a >= ae) return false;
+      j = col[a++];
+      fa = fb = 1;
+      return true;
+    }
+    int ja = a < ae ? col[a] : 0x7fffffff;
+    int jb = b < be ? col[b] : 0x7fffffff;
+    if (ja == 0x7fffffff && jb == 0x7fffffff) return false;
+    j = ja < jb ? ja : jb;
+    fa = ja == j;
+    fb = jb == j;
+    if (fa) a++;
+    if (fb) b++;
+    return true;
+  }
+};
+
+struct TIter {
+  UIter U;
+  const int32_t* blk_start;
+  const uint8_t* blk_shape;
+  int64_t hoff;
+  int64_t row;
+  int t, nt, fa, fb;
+  bool valid;
+  __device__ void init(const int32_t* col, int64_t a, int64_t ae, int64_t b, int64_t be,
+                       bool same, const int32_t* bs, const uint8_t* bsh, int64_t off) {
+    U.col = col;
+    U.a = a;
+    U.ae = ae;
+    U.b = b;
+    U.be = be;
+    U.same = same;
+    blk_start = bs;
+    blk_shape = bsh;
+    hoff = off;
+    valid = true;
+    t = 0;
+    nt = 0;
+    advance();
+  }
+  __device__ void advance() {
+    if (valid && t + 1 < nt) {
+      t++;
+      row += 64;
+      return;
+    }
+    int j;
+    valid = U.next(j, fa, fb);
+    if (valid) {
+      row = blk_start[hoff + j];
+      nt = d_shapes[blk_shape[hoff + j]].volume >> 6;
+      t = 0;
+    }
+  }
+};
+
+__device__ inline bf16x8 lds_chunk(const uint16_t* tile, int row, int chunk) {
+  const uint4* p = (const uint4*)(tile + row * 128 + ((chunk ^ chunk_swizzle(row)) << 3));
+  return __builtin_bit_cast(bf16x8, *p);
 }
+
+// fragment of X^T (rows = channels 32db..32db+31, k = 16 rows of chunk c of
+// the 64-row tile X, in the order {16c+4hl+0..3, 16c+8+4hl+0..3})
+__device__ inline bf16x8 lds_tfrag(const uint16_t* tile, int c, int db, int lane) {
+  const int hl = lane >> 5;
+  const int rowA = 16 * c + 4 * hl + ((lane & 15) >> 2);
+  const int rowB = rowA + 8;
+  const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int off = 4 * (lane & 1);
+  const uint16_t* pa = tile + rowA * 128 + ((chunk ^ chunk_swizzle(rowA)) << 3) + off;
+  const uint16_t* pb = tile + rowB * 128 + ((chunk ^ chunk_swizzle(rowB)) << 3) + off;
+  s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b*)pa);
+  s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b*)pb);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ inline uint32_t pk2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// one row chunk (16 B) of a permuted, swizzled [rows][128] bf16 buffer
+__device__ inline bf16x8 row_chunk(const uint16_t* buf, int64_t row, int chunk) {
+  return __builtin_bit_cast(
+      bf16x8, *(const uint4*)(buf + row * 128 + ((chunk ^ chunk_swizzle((int)(row & 63))) << 3)));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- prep
+// One block of 256 threads per 64-row tile; wave w handles rows w, w+4, ...
+__global__ __launch_bounds__(256) void k_bwd_prep(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
+    const uint8_t* __restrict__ shape_id, int H, int W, int Z, int64_t N,
+    uint16_t* __restrict__ qp, uint16_t* __restrict__ dop, float* __restrict__ delta,
+    float* __restrict__ lse2) {
+  const int64_t tpH = N >> 6;
+  const int h = (int)(blockIdx.x / tpH);
+  const int64_t r0 = (blockIdx.x - (int64_t)h * tpH) << 6;
+  const int m = (int)(r0 >> 9);
+  const Shape sh = d_shapes[shape_id[(int64_t)h * Z + m]];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = wv; i < 64; i += 4) {
+    const int64_t p = r0 + i;
+    const int64_t tok = token_of(sh, m, (int)(p & 511), H, W);
+    const int64_t src = ((int64_t)h * N + tok) * 128 + lane * 2;
+    const uint32_t qv = *(const uint32_t*)(q + src);
+    const uint32_t dv = *(const uint32_t*)(d_o + src);
+    const uint32_t ov = *(const uint32_t*)(o + src);
+    const int64_t dst = ((int64_t)h * N + p) * 128 +
+                        (((lane >> 2) ^ chunk_swizzle(i)) << 3) + (lane & 3) * 2;
+    *(uint32_t*)(qp + dst) = qv;
+    *(uint32_t*)(dop + dst) = dv;
+    float s = __uint_as_float(dv << 16) * __uint_as_float(ov << 16);
+    s = __builtin_fmaf(__uint_as_float(dv & 0xffff0000u), __uint_as_float(ov & 0xffff0000u), s);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) {
+      delta[(int64_t)h * N + p] = s;
+      lse2[(int64_t)h * N + p] = lse[(int64_t)h * N + tok] * 1.44269504088896340736f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+__global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
+    const uint16_t* __restrict__ qp, const uint16_t* __restrict__ dop,
+    const float* __restrict__ lse2, const float* __restrict__ delta,
+    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+    const uint8_t* __restrict__ shape_id, const int32_t* __restrict__ zone_base,
+    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_start,
+    const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ colt_ptr,
+    const int32_t* __restrict__ colt_idx, int H, int W, int Z, int64_t N, float c_log2,
+    float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][64 * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t sD[2][64 * 128];
+  __shared__ __attribute__((aligned(16))) float sL[2][64];
+  __shared__ __attribute__((aligned(16))) float sDel[2][64];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int64_t upH = N >> 7;
+  const int h = (int)(blockIdx.x / upH);
+  const int64_t r0 = (blockIdx.x - (int64_t)h * upH) << 7;
+  const int m = (int)(r0 >> 9);
+  const Shape sh = d_shapes[shape_id[(int64_t)h * Z + m]];
+  const int B = sh.volume;
+  const int rz = (int)(r0 & 511);
+  const int64_t hoff = blk_off[h];
+  const int64_t gbase = hoff + zone_base[(int64_t)h * Z + m];
+  const int64_t gA = gbase + rz / B, gB = gbase + (rz + 64) / B;
+  const int half = wv >> 1;
+
+  // this wave's 32 keys: K and V rows as MFMA B operands (k = channel)
+  const int64_t hrow = (int64_t)h * N;
+  const int64_t krow = hrow + r0 + wv * 32 + l32;
+  bf16x8 kr[8], vr[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; kk++) {
+    kr[kk] = row_chunk(kp, krow, 2 * kk + hl);
+    vr[kk] = row_chunk(vp, krow, 2 * kk + hl);
+  }
+  f32x16 dkt[4], dvt[4];
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      dkt[db][r] = 0.0f;
+      dvt[db][r] = 0.0f;
+    }
+
+  TIter it;
+  it.init(colt_idx, colt_ptr[gA], colt_ptr[gA + 1], colt_ptr[gB], colt_ptr[gB + 1], gA == gB,
+          blk_start, blk_shape, hoff);
+  const uint4* qbase = (const uint4*)(qp + hrow * 128);
+  const uint4* dbase = (const uint4*)(dop + hrow * 128);
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  auto stage = [&](int bi, int64_t row) {
+    const uint4* qs = qbase + row * 16;
+    const uint4* ds = dbase + row * 16;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int piece = i * 256 + wvu * 64;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(qs + piece + lane),
+          (__attribute__((address_space(3))) void*)((uint4*)sQ[bi] + piece), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(ds + piece + lane),
+          (__attribute__((address_space(3))) void*)((uint4*)sD[bi] + piece), 16, 0, 0);
+    }
+    if (wvu == 0)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(lse2 + hrow + row + lane),
+          (__attribute__((address_space(3))) void*)(sL[bi]), 4, 0, 0);
+    if (wvu == 1)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(delta + hrow + row + lane),
+          (__attribute__((address_space(3))) void*)(sDel[bi]), 4, 0, 0);
+  };
+
+  int buf = 0, cur_fa = 0, cur_fb = 0;
+  if (it.valid) {
+    stage(0, it.row);
+    cur_fa = it.fa;
+    cur_fb = it.fb;
+    it.advance();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    while (true) {
+      const bool has_next = it.valid;
+      const int nfa = it.fa, nfb = it.fb;
+      if (has_next) stage(buf ^ 1, it.row);
+      const bool active = half == 0 ? cur_fa : cur_fb;
+      if (active) {
+        const uint16_t* Qs = sQ[buf];
+        const uint16_t* Ds = sD[buf];
+#pragma unroll
+        for (int qb = 0; qb < 2; qb++) {
+          f32x16 s, dp;
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            s[r] = 0.0f;
+            dp[r] = 0.0f;
+          }
+#pragma unroll
+          for (int kk = 0; kk < 8; kk++) {
+            bf16x8 aq = lds_chunk(Qs, 32 * qb + l32, 2 * kk + hl);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kr[kk], s, 0, 0, 0);
+            bf16x8 ad = lds_chunk(Ds, 32 * qb + l32, 2 * kk + hl);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vr[kk], dp, 0, 0, 0);
+          }
+          // rows of s/dp held by this lane: q = 32qb + 8j + 4hl + i (r = 4j + i)
+          uint32_t pp[8], ps[8];
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const float4 L4 = *(const float4*)(&sL[buf][32 * qb + 8 * j + 4 * hl]);
+            const float4 D4 = *(const float4*)(&sDel[buf][32 * qb + 8 * j + 4 * hl]);
+            const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+            const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+            float pv[4], sv[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * j + i], c_log2, -Lv[i]));
+              sv[i] = pv[i] * (dp[4 * j + i] - Dv[i]);
+            }
+            pp[2 * j] = pk2(pv[0], pv[1]);
+            pp[2 * j + 1] = pk2(pv[2], pv[3]);
+            ps[2 * j] = pk2(sv[0], sv[1]);
+            ps[2 * j + 1] = pk2(sv[2], sv[3]);
+          }
+#pragma unroll
+          for (int c = 0; c < 2; c++) {
+            const bf16x8 bp = __builtin_bit_cast(
+                bf16x8, make_uint4(pp[4 * c], pp[4 * c + 1], pp[4 * c + 2], pp[4 * c + 3]));
+            const bf16x8 bs = __builtin_bit_cast(
+                bf16x8, make_uint4(ps[4 * c], ps[4 * c + 1], ps[4 * c + 2], ps[4 * c + 3]));
+#pragma unroll
+            for (int db = 0; db < 4; db++) {
+              bf16x8 ado = lds_tfrag(Ds, 2 * qb + c, db, lane);
+              dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, bp, dvt[db], 0, 0, 0);
+              bf16x8 aqq = lds_tfrag(Qs, 2 * qb + c, db, lane);
+              dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqq, bs, dkt[db], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if (!has_next) break;
+      cur_fa = nfa;
+      cur_fb = nfb;
+      it.advance();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+  // lane holds key r0 + 32wv + l32, channels 32db + 8j + 4hl + 0..3
+  const int64_t p = r0 + wv * 32 + l32;
+  const int64_t tok = token_of(sh, m, (int)(p & 511), H, W);
+  uint16_t* dkr = dk + (hrow + tok) * 128;
+  uint16_t* dvr = dv + (hrow + tok) * 128;
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      uint2 a, b;
+      a.x = pk2(dkt[db][4 * j] * scale, dkt[db][4 * j + 1] * scale);
+      a.y = pk2(dkt[db][4 * j + 2] * scale, dkt[db][4 * j + 3] * scale);
+      b.x = pk2(dvt[db][4 * j], dvt[db][4 * j + 1]);
+      b.y = pk2(dvt[db][4 * j + 2], dvt[db][4 * j + 3]);
+      *(uint2*)(dkr + 32 * db + 8 * j + 4 * hl) = a;
+      *(uint2*)(dvr + 32 * db + 8 * j + 4 * hl) = b;
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+__global__ __launch_bounds__(256, 2) void k_bwd_dq(
+    const uint16_t* __restrict__ qp, const uint16_t* __restrict__ dop,
+    const float* __restrict__ lse2, const float* __restrict__ delta,
+    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+    const uint8_t* __restrict__ shape_id, const int32_t* __restrict__ zone_base,
+    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_start,
+    const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, int H, int W, int Z, int64_t N, float c_log2,
+    float scale, uint16_t* __restrict__ dq) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][64 * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][64 * 128];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int64_t upH = N >> 7;
+  const int h = (int)(blockIdx.x / upH);
+  const int64_t r0 = (blockIdx.x - (int64_t)h * upH) << 7;
+  const int m = (int)(r0 >> 9);
+  const Shape sh = d_shapes[shape_id[(int64_t)h * Z + m]];
+  const int B = sh.volume;
+  const int rz = (int)(r0 & 511);
+  const int64_t hoff = blk_off[h];
+  const int64_t gbase = hoff + zone_base[(int64_t)h * Z + m];
+  const int64_t gA = gbase + rz / B, gB = gbase + (rz + 64) / B;
+  const int half = wv >> 1;
+  const int64_t hrow = (int64_t)h * N;
+  const int64_t qrow = hrow + r0 + wv * 32 + l32;
+  bf16x8 qf[8], df[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; kk++) {
+    qf[kk] = row_chunk(qp, qrow, 2 * kk + hl);
+    df[kk] = row_chunk(dop, qrow, 2 * kk + hl);
+  }
+  const float L = lse2[qrow];
+  const float Dl = delta[qrow];
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[db][r] = 0.0f;
+
+  TIter it;
+  it.init(col_idx, row_ptr[gA], row_ptr[gA + 1], row_ptr[gB], row_ptr[gB + 1], gA == gB,
+          blk_start, blk_shape, hoff);
+  const uint4* kbase = (const uint4*)(kp + hrow * 128);
+  const uint4* vbase = (const uint4*)(vp + hrow * 128);
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  auto stage = [&](int bi, int64_t row) {
+    const uint4* ks = kbase + row * 16;
+    const uint4* vs = vbase + row * 16;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int piece = i * 256 + wvu * 64;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(ks + piece + lane),
+          (__attribute__((address_space(3))) void*)((uint4*)sK[bi] + piece), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(vs + piece + lane),
+          (__attribute__((address_space(3))) void*)((uint4*)sV[bi] + piece), 16, 0, 0);
+    }
+  };
+  int buf = 0, cur_fa = 0, cur_fb = 0;
+  if (it.valid) {
+    stage(0, it.row);
+    cur_fa = it.fa;
+    cur_fb = it.fb;
+    it.advance();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    while (true) {
+      const bool has_next = it.valid;
+      const int nfa = it.fa, nfb = it.fb;
+      if (has_next) stage(buf ^ 1, it.row);
+      const bool active = half == 0 ? cur_fa : cur_fb;
+      if (active) {
+        const uint16_t* Ks = sK[buf];
+        const uint16_t* Vs = sV[buf];
+        f32x16 st[2], dpt[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            st[kb][r] = 0.0f;
+            dpt[kb][r] = 0.0f;
+          }
+#pragma unroll
+        for (int kk = 0; kk < 8; kk++)
+#pragma unroll
+          for (int kb = 0; kb < 2; kb++) {
+            bf16x8 ak = lds_chunk(Ks, 32 * kb + l32, 2 * kk + hl);
+            st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kk], st[kb], 0, 0, 0);
+            bf16x8 av = lds_chunk(Vs, 32 * kb + l32, 2 * kk + hl);
+            dpt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, df[kk], dpt[kb], 0, 0, 0);
+          }
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const int r = 8 * (c & 1) + 2 * e;
+            float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r], c_log2, -L));
+            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r + 1], c_log2, -L));
+            pk[e] = pk2(p0 * (dpt[c >> 1][r] - Dl), p1 * (dpt[c >> 1][r + 1] - Dl));
+          }
+          const bf16x8 bs = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+#pragma unroll
+          for (int db = 0; db < 4; db++) {
+            bf16x8 ak = lds_tfrag(Ks, c, db, lane);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bs, acc[db], 0, 0, 0);
+          }
+        }
+      }
+      if (!has_next) break;
+      cur_fa = nfa;
+      cur_fb = nfb;
+      it.advance();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+  const int64_t p = r0 + wv * 32 + l32;
+  const int64_t tok = token_of(sh, m, (int)(p & 511), H, W);
+  uint16_t* row = dq + (hrow + tok) * 128;
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      uint2 u;
+      u.x = pk2(acc[db][4 * j] * scale, acc[db][4 * j + 1] * scale);
+      u.y = pk2(acc[db][4 * j + 2] * scale, acc[db][4 * j + 3] * scale);
+      *(uint2*)(row + 32 * db + 8 * j + 4 * hl) = u;
+    }
+}
+
+bool launch_attn_bwd(const PlanDev& P, const BwdDev& Bd, const void* q, const void* o,
+                     const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                     hipStream_t st) {
+  if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
+  const float c_log2 = (float)(1.4426950408889634 / sqrt(128.0));
+  const float scale = (float)(1.0 / sqrt(128.0));
+  hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)(P.heads * (P.N >> 6))), dim3(256), 0, st,
+                     (const uint16_t*)q, (const uint16_t*)o, (const uint16_t*)d_o, lse,
+                     P.shape_id, P.H, P.W, P.Z, P.N, (uint16_t*)Bd.qp, (uint16_t*)Bd.dop,
+                     Bd.delta, Bd.lse_p);
+  dim3 grid((unsigned)(P.heads * (P.N >> 7))), block(256);
+  hipLaunchKernelGGL(k_bwd_dkdv, grid, block, 0, st, (const uint16_t*)Bd.qp,
+                     (const uint16_t*)Bd.dop, Bd.lse_p, Bd.delta, (const uint16_t*)P.kp,
+                     (const uint16_t*)P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start,
+                     P.blk_shape, P.colt_ptr, P.colt_idx, P.H, P.W, P.Z, P.N, c_log2, scale,
+                     (uint16_t*)dk, (uint16_t*)dv);
+  hipLaunchKernelGGL(k_bwd_dq, grid, block, 0, st, (const uint16_t*)Bd.qp,
+                     (const uint16_t*)Bd.dop, Bd.lse_p, Bd.delta, (const uint16_t*)P.kp,
+                     (const uint16_t*)P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start,
+                     P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W, P.Z, P.N, c_log2, scale,
+                     (uint16_t*)dq);
+  return hipGetLastError() == hipSuccess;
+}
+
 }  // namespace prism

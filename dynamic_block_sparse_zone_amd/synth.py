@@ -73,6 +73,9 @@ WORKLOADS = {
     # zones of every volume, a ragged number of blocks per head
     "check": Workload("check", 16, 24, 32, 3, 128, "bf16", top_k=3, top_p=0.9, seed=1006,
                       backward=True),
+    # smallest bf16 grid with zones of every volume, for full backward checks
+    "bwdcheck": Workload("bwdcheck", 8, 16, 32, 2, 128, "bf16", top_k=3, top_p=0.9, seed=1007,
+                         backward=True),
 }
 
 

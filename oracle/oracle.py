@@ -356,3 +356,17 @@ def tokens_of_block(pl: Plan, h: int, i: int) -> np.ndarray:
     g = int(pl.blk_off[h]) + i
     s, n = int(pl.blk_start[g]), int(pl.blk_len[g])
     return pl.perm[h, s:s + n]
+
+
+def attn_bwd_head(q, k, v, do, pl: Plan, h: int):
+    """dQ, dK, dV of head h ([N, D] fp64 each, original token order), walking
+    every query row once over the head's full selection."""
+    cfg = pl.cfg
+    row_ptr, col = select_all(pl, [h])
+    dq = np.zeros((cfg.N, cfg.head_dim), np.float64)
+    dk = np.zeros_like(dq)
+    dv = np.zeros_like(dq)
+    lib().orc_attn_bwd_head(_p(q), _p(k), _p(v), _p(do), _dtype_code(q), ctypes.c_int64(cfg.N),
+                            cfg.head_dim, _p(pl.perm), _p(pl.blk_off), _p(pl.blk_start),
+                            _p(pl.blk_len), _p(row_ptr), _p(col), h, _p(dq), _p(dk), _p(dv))
+    return dq, dk, dv

@@ -846,3 +846,69 @@ int orc_attn_bwd_kv(const void* q, const void* k, const void* v, const void* dO,
   }
   return OR_OK;
 }
+
+/* All gradients of one head by walking every query row once: for row n of
+ * query block i, P and dP over the keys of S_i, Delta = sum_m P dP; then
+ * dQ_n = sum_m dS k_m / sqrt D and, for each selected key m,
+ * dK_m += dS q_n / sqrt D, dV_m += P dO_n.  row_ptr/col_idx hold the full
+ * selection (global block ids index row_ptr).  dq, dk, dv: [N][D] in the
+ * original token order. */
+int orc_attn_bwd_head(const void* q, const void* k, const void* v, const void* dO, int dtype,
+                      int64_t N, int D, const int32_t* perm, const int64_t* blk_off,
+                      const int32_t* blk_start, const int32_t* blk_len, const int64_t* row_ptr,
+                      const int32_t* col_idx, int h, double* dq, double* dk, double* dv) {
+  double scale = 1.0 / sqrt((double)D);
+  const int32_t* perm_h = perm + (int64_t)h * N;
+  int64_t goff = blk_off[h];
+  int nblk = (int)(blk_off[h + 1] - blk_off[h]);
+  memset(dq, 0, sizeof(double) * N * D);
+  memset(dk, 0, sizeof(double) * N * D);
+  memset(dv, 0, sizeof(double) * N * D);
+#pragma omp parallel
+  {
+    double* lk = (double*)calloc((size_t)N * D, sizeof(double));
+    double* lv = (double*)calloc((size_t)N * D, sizeof(double));
+#pragma omp for schedule(dynamic)
+    for (int i = 0; i < nblk; i++) {
+      int64_t gi = goff + i;
+      const int32_t* sel = col_idx + row_ptr[gi];
+      int ns = (int)(row_ptr[gi + 1] - row_ptr[gi]);
+      int64_t nk = 0;
+      for (int a = 0; a < ns; a++) nk += blk_len[goff + sel[a]];
+      double* P = (double*)malloc(sizeof(double) * (nk + 1));
+      double* dP = (double*)malloc(sizeof(double) * (nk + 1));
+      for (int u = 0; u < blk_len[gi]; u++) {
+        int64_t nq = perm_h[blk_start[gi] + u];
+        double delta;
+        row_softmax_grad(q, k, v, dO, dtype, N, D, perm_h, h, nq, sel, ns, blk_start, blk_len,
+                         goff, P, dP, &delta);
+        int64_t idx = 0;
+        for (int a = 0; a < ns; a++) {
+          int64_t gk = goff + sel[a];
+          for (int r = 0; r < blk_len[gk]; r++) {
+            int64_t nkt = perm_h[blk_start[gk] + r];
+            double pr = P[idx], ds = P[idx] * (dP[idx] - delta) * scale;
+            for (int c = 0; c < D; c++) {
+              dq[nq * D + c] += ds * ld(k, dtype, ((int64_t)h * N + nkt) * D + c);
+              lk[nkt * D + c] += ds * ld(q, dtype, ((int64_t)h * N + nq) * D + c);
+              lv[nkt * D + c] += pr * ld(dO, dtype, ((int64_t)h * N + nq) * D + c);
+            }
+            idx++;
+          }
+        }
+      }
+      free(P);
+      free(dP);
+    }
+#pragma omp critical
+    {
+      for (int64_t e = 0; e < N * D; e++) {
+        dk[e] += lk[e];
+        dv[e] += lv[e];
+      }
+    }
+    free(lk);
+    free(lv);
+  }
+  return OR_OK;
+}
