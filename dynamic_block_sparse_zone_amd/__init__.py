@@ -2,8 +2,8 @@
 self-attention: zone statistics, content-adaptive block shapes, zone-aware
 re-layout, Top-k U Top-p block selection and sparse attention forward and
 backward, behind the C ABI of include/prism.h."""
-from .api import (Plan, attn_bwd, attn_fwd, block_scores, candidate, make_config, plan,
-                  workspace_bytes)
+from .api import (Plan, attn_bwd, attn_bwd_workspace_bytes, attn_fwd, block_scores, candidate,
+                  make_config, plan, timing_enable, timing_read, workspace_bytes)
 
-__all__ = ["Plan", "plan", "attn_fwd", "attn_bwd", "block_scores", "candidate",
-           "make_config", "workspace_bytes"]
+__all__ = ["Plan", "plan", "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "block_scores",
+           "candidate", "make_config", "workspace_bytes", "timing_enable", "timing_read"]

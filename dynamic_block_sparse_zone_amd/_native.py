@@ -32,7 +32,7 @@ EXPORTED = [
     "prism_plan_create", "prism_plan_destroy", "prism_attn_fwd",
     "prism_attn_bwd_workspace_size", "prism_attn_bwd", "prism_block_scores",
     "prism_plan_array_bytes", "prism_plan_export", "prism_plan_info", "prism_candidate",
-    "prism_status_str",
+    "prism_status_str", "prism_timing_enable", "prism_timing_read",
 ]
 
 
@@ -53,6 +53,11 @@ class PrismPlanInfo(ctypes.Structure):
         ("max_blocks_per_head", ctypes.c_int64), ("pair_tokens", ctypes.c_double),
         ("shape_hist", ctypes.c_int64 * 16),
     ]
+
+
+class PrismStageTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
 
 
 class PrismError(RuntimeError):
@@ -90,6 +95,9 @@ def lib() -> ctypes.CDLL:
         L.prism_plan_export.argtypes = [vp, i32, vp, sz, vp]
         L.prism_plan_info.argtypes = [vp, ctypes.POINTER(PrismPlanInfo), vp]
         L.prism_candidate.argtypes = [i32, ctypes.POINTER(ctypes.c_int32)]
+        L.prism_timing_enable.argtypes = [i32]
+        L.prism_timing_read.argtypes = [ctypes.POINTER(PrismStageTime), i32,
+                                        ctypes.POINTER(ctypes.c_int32)]
         L.prism_status_str.argtypes = [ctypes.c_int]
         L.prism_status_str.restype = ctypes.c_char_p
         _lib = L

@@ -180,3 +180,17 @@ def candidate(i: int) -> tuple:
     a = (ctypes.c_int32 * 4)()
     nat.check(nat.lib().prism_candidate(int(i), a), "prism_candidate")
     return tuple(a)
+
+
+def timing_enable(on: bool = True) -> None:
+    """Record a HIP event pair around every kernel stage (measurement)."""
+    nat.check(nat.lib().prism_timing_enable(1 if on else 0), "prism_timing_enable")
+
+
+def timing_read() -> dict:
+    """{stage: (launches, total_ms)} since the last read; waits for the events."""
+    arr = (nat.PrismStageTime * 64)()
+    n = ctypes.c_int32()
+    nat.check(nat.lib().prism_timing_read(arr, 64, ctypes.byref(n)), "prism_timing_read")
+    return {arr[i].name.decode(): (int(arr[i].launches), float(arr[i].total_ms))
+            for i in range(min(n.value, 64))}

@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+#include <string>
 #include <vector>
 
 #include "prism_common.h"
@@ -21,6 +23,45 @@ struct prism_plan_s {
   const void* v;
   int32_t* perm;  // device [heads][N], written on export
 };
+
+// ---------------------------------------------------------------- stage timing
+namespace prism {
+namespace {
+struct StageRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<StageRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+hipEvent_t pool_get() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+void stage_begin(const char* name, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_timing) return;
+  StageRec r{name, pool_get(), pool_get()};
+  if (!r.a || !r.b) return;
+  (void)hipEventRecord(r.a, st);
+  g_recs.push_back(r);
+}
+
+void stage_end(hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_timing || g_recs.empty()) return;
+  (void)hipEventRecord(g_recs.back().b, st);
+}
+}  // namespace prism
 
 namespace {
 
@@ -186,14 +227,18 @@ prism_status prism_plan_create(const prism_config* c, const void* q, const void*
   const int fixed_id = fixed_id_of(*c);
 
   PRISM_HIP(hipGetLastError());
+  stage_begin("plan.stats", st);
   bool ok = launch_zone_stats(v, c->dtype, c->head_dim, c->H, c->W, P.Z, c->heads, P.N,
                               P.vstats, st);
   if (av_norm)
     ok = ok && launch_audio_stats(av_norm, c->H, c->W, P.Z, P.astats, st);
   else
     PRISM_HIP(hipMemsetAsync(P.astats, 0, sizeof(float) * 4 * P.Z, st));
+  stage_end(st);
+  stage_begin("plan.shapes", st);
   ok = ok && launch_shapes(P, av_norm != nullptr, *c, fixed_id, st);
   ok = ok && launch_blk_off(P, st);
+  stage_end(st);
   if (!ok) return PRISM_EDEVICE;
   std::vector<int64_t> off(c->heads + 1);
   PRISM_HIP(hipMemcpyAsync(off.data(), P.blk_off, sizeof(int64_t) * (c->heads + 1),
@@ -202,12 +247,18 @@ prism_status prism_plan_create(const prism_config* c, const void* q, const void*
   int64_t maxb = 0;
   for (int h = 0; h < c->heads; h++) maxb = std::max(maxb, off[h + 1] - off[h]);
 
+  stage_begin("plan.permute", st);
   ok = launch_permute_pool(P, q, k, v, st);
+  stage_end(st);
   PRISM_HIP(hipMemsetAsync(P.counters, 0, sizeof(int64_t) * 8, st));
   for (int h = 0; h < c->heads && ok; h++) {
     int n = (int)(off[h + 1] - off[h]);
+    stage_begin("plan.scores", st);
     ok = launch_block_scores(P, off[h], n, P.scores, st);
+    stage_end(st);
+    stage_begin("plan.select", st);
     ok = ok && launch_select(P, off[h], n, *c, h == c->heads - 1, st);
+    stage_end(st);
   }
   if (!ok) return PRISM_EDEVICE;
   int64_t nnz = 0;
@@ -216,10 +267,12 @@ prism_status prism_plan_create(const prism_config* c, const void* q, const void*
   if (nnz_out) *nnz_out = nnz;
   if (nnz > cap) return PRISM_ENOMEM_WORKSPACE;
   if (c->need_backward) {
+    stage_begin("plan.transpose", st);
     for (int h = 0; h < c->heads && ok; h++) {
       int n = (int)(off[h + 1] - off[h]);
       ok = launch_transpose(P, off[h], n, h == c->heads - 1, st);
     }
+    stage_end(st);
     if (!ok) return PRISM_EDEVICE;
   }
   PRISM_HIP(hipGetLastError());
@@ -246,8 +299,10 @@ prism_status prism_attn_fwd(const prism_plan_t* plan, const void* q, const void*
   if (!((c.dtype == PRISM_BF16 && c.head_dim == 128) || c.dtype == PRISM_F32))
     return PRISM_EUNSUPPORTED;
   PRISM_HIP(hipGetLastError());
-  if (!launch_attn_fwd(plan->P, q, o, lse, (hipStream_t)stream)) return PRISM_EDEVICE;
-  return PRISM_OK;
+  stage_begin("attn.fwd", (hipStream_t)stream);
+  bool ok = launch_attn_fwd(plan->P, q, o, lse, (hipStream_t)stream);
+  stage_end((hipStream_t)stream);
+  return ok ? PRISM_OK : PRISM_EDEVICE;
 }
 
 prism_status prism_attn_bwd_workspace_size(const prism_config* c, size_t* bytes) {
@@ -285,9 +340,17 @@ prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void*
   B.qp = A.take<uint16_t>((int64_t)c.heads * N * c.head_dim);
   B.dop = A.take<uint16_t>((int64_t)c.heads * N * c.head_dim);
   PRISM_HIP(hipGetLastError());
-  if (!launch_attn_bwd(plan->P, B, q, o, lse, d_o, dq, dk, dv, (hipStream_t)stream))
-    return PRISM_EDEVICE;
-  return PRISM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  stage_begin("bwd.prep", st);
+  bool ok = launch_bwd_prep(plan->P, B, q, o, lse, d_o, st);
+  stage_end(st);
+  stage_begin("bwd.dkdv", st);
+  ok = ok && launch_bwd_dkdv(plan->P, B, dk, dv, st);
+  stage_end(st);
+  stage_begin("bwd.dq", st);
+  ok = ok && launch_bwd_dq(plan->P, B, dq, st);
+  stage_end(st);
+  return ok ? PRISM_OK : PRISM_EDEVICE;
 }
 
 prism_status prism_block_scores(const prism_plan_t* plan, int32_t head, float* out,
@@ -382,6 +445,41 @@ prism_status prism_candidate(int32_t id, int32_t* out4) {
   out4[2] = h_shapes[id].bw;
   out4[3] = h_shapes[id].volume;
   return PRISM_OK;
+}
+
+prism_status prism_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(prism::g_tmu);
+  prism::g_timing = enable != 0;
+  return PRISM_OK;
+}
+
+prism_status prism_timing_read(prism_stage_time* out, int32_t max, int32_t* count) {
+  if (!count || max < 0 || (max > 0 && !out)) return PRISM_EINVAL;
+  std::lock_guard<std::mutex> lk(prism::g_tmu);
+  std::vector<prism_stage_time> agg;
+  prism_status status = PRISM_OK;
+  for (auto& r : prism::g_recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      status = PRISM_EDEVICE;
+    size_t i = 0;
+    for (; i < agg.size(); i++)
+      if (r.name == agg[i].name) break;
+    if (i == agg.size()) {
+      prism_stage_time t;
+      memset(&t, 0, sizeof(t));
+      strncpy(t.name, r.name.c_str(), sizeof(t.name) - 1);
+      agg.push_back(t);
+    }
+    agg[i].launches++;
+    agg[i].total_ms += ms;
+    prism::g_pool.push_back(r.a);
+    prism::g_pool.push_back(r.b);
+  }
+  prism::g_recs.clear();
+  *count = (int32_t)agg.size();
+  for (int32_t i = 0; i < (int32_t)agg.size() && i < max; i++) out[i] = agg[i];
+  return status;
 }
 
 const char* prism_status_str(prism_status s) {

@@ -459,26 +459,37 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     }
 }
 
-bool launch_attn_bwd(const PlanDev& P, const BwdDev& Bd, const void* q, const void* o,
-                     const float* lse, const void* d_o, void* dq, void* dk, void* dv,
-                     hipStream_t st) {
+static const float kCLog2 = (float)(1.4426950408889634 / 11.313708498984761);
+static const float kScale = (float)(1.0 / 11.313708498984761);
+
+bool launch_bwd_prep(const PlanDev& P, const BwdDev& Bd, const void* q, const void* o,
+                     const float* lse, const void* d_o, hipStream_t st) {
   if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
-  const float c_log2 = (float)(1.4426950408889634 / sqrt(128.0));
-  const float scale = (float)(1.0 / sqrt(128.0));
   hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)(P.heads * (P.N >> 6))), dim3(256), 0, st,
                      (const uint16_t*)q, (const uint16_t*)o, (const uint16_t*)d_o, lse,
                      P.shape_id, P.H, P.W, P.Z, P.N, (uint16_t*)Bd.qp, (uint16_t*)Bd.dop,
                      Bd.delta, Bd.lse_p);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& Bd, void* dk, void* dv, hipStream_t st) {
+  if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
   dim3 grid((unsigned)(P.heads * (P.N >> 7))), block(256);
   hipLaunchKernelGGL(k_bwd_dkdv, grid, block, 0, st, (const uint16_t*)Bd.qp,
                      (const uint16_t*)Bd.dop, Bd.lse_p, Bd.delta, (const uint16_t*)P.kp,
                      (const uint16_t*)P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start,
-                     P.blk_shape, P.colt_ptr, P.colt_idx, P.H, P.W, P.Z, P.N, c_log2, scale,
+                     P.blk_shape, P.colt_ptr, P.colt_idx, P.H, P.W, P.Z, P.N, kCLog2, kScale,
                      (uint16_t*)dk, (uint16_t*)dv);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_bwd_dq(const PlanDev& P, const BwdDev& Bd, void* dq, hipStream_t st) {
+  if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
+  dim3 grid((unsigned)(P.heads * (P.N >> 7))), block(256);
   hipLaunchKernelGGL(k_bwd_dq, grid, block, 0, st, (const uint16_t*)Bd.qp,
                      (const uint16_t*)Bd.dop, Bd.lse_p, Bd.delta, (const uint16_t*)P.kp,
                      (const uint16_t*)P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start,
-                     P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W, P.Z, P.N, c_log2, scale,
+                     P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W, P.Z, P.N, kCLog2, kScale,
                      (uint16_t*)dq);
   return hipGetLastError() == hipSuccess;
 }

@@ -27,8 +27,13 @@ struct BwdDev {
   void* qp;        // [heads][N][D] permuted Q (swizzled like K/V)
   void* dop;       // [heads][N][D] permuted dO
 };
-bool launch_attn_bwd(const PlanDev& P, const BwdDev& B, const void* q, const void* o,
-                     const float* lse, const void* d_o, void* dq, void* dk, void* dv,
-                     hipStream_t st);
+bool launch_bwd_prep(const PlanDev& P, const BwdDev& B, const void* q, const void* o,
+                     const float* lse, const void* d_o, hipStream_t st);
+bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& B, void* dk, void* dv, hipStream_t st);
+bool launch_bwd_dq(const PlanDev& P, const BwdDev& B, void* dq, hipStream_t st);
+
+// stage timing (measurement support)
+void stage_begin(const char* name, hipStream_t st);
+void stage_end(hipStream_t st);
 
 }  // namespace prism

@@ -189,6 +189,24 @@ prism_status prism_plan_info(const prism_plan_t* plan, prism_plan_info_t* info, 
  * Writes bT, bH, bW, B of candidate `id` (0..15). Host-only. */
 prism_status prism_candidate(int32_t id, int32_t* out4);
 
+/* Measurement support.  While enabled, every kernel stage the library
+ * enqueues is bracketed by a pair of HIP events recorded on the stage's own
+ * stream (stage names: plan.stats, plan.shapes, plan.permute, plan.scores,
+ * plan.select, plan.transpose, attn.fwd, bwd.prep, bwd.dkdv, bwd.dq).
+ * Host-only; off by default. */
+prism_status prism_timing_enable(int32_t enable);
+
+typedef struct {
+  char name[32];
+  int64_t launches;   /* recorded launches of this stage */
+  double total_ms;    /* sum of their event-to-event durations */
+} prism_stage_time;
+
+/* Aggregates and clears the recorded stages: writes up to max entries to
+ * out (host memory) and the number of distinct stages to *count.  Waits for
+ * the recorded events to complete. */
+prism_status prism_timing_read(prism_stage_time* out, int32_t max, int32_t* count);
+
 const char* prism_status_str(prism_status s);
 
 #ifdef __cplusplus
