@@ -21,6 +21,7 @@
 namespace prism {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4b;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -81,7 +82,7 @@ struct TIter {
     valid = U.next(j, fa, fb);
     if (valid) {
       row = blk_start[hoff + j];
-      nt = d_shapes[blk_shape[hoff + j]].volume >> 6;
+      nt = d_shapes[block_shape_at(blk_shape, hoff + j)].volume >> 6;
       t = 0;
     }
   }
@@ -110,13 +111,80 @@ __device__ inline bf16x8 lds_tfrag(const uint16_t* tile, int c, int db, int lane
 }
 
 __device__ inline uint32_t pk2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  // one v_cvt_pk_bf16_f32 (round to nearest even)
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // one row chunk (16 B) of a permuted, swizzled [rows][128] bf16 buffer
 __device__ inline bf16x8 row_chunk(const uint16_t* buf, int64_t row, int chunk) {
   return __builtin_bit_cast(
       bf16x8, *(const uint4*)(buf + row * 128 + ((chunk ^ chunk_swizzle((int)(row & 63))) << 3)));
+}
+
+// Query-tile ring depth of dK/dV; s_waitcnt immediates (vmcnt in bits 3:0
+// and 15:14, expcnt and lgkmcnt at their maxima) for the loads of two tiles
+// (nine per wave each) and for none.
+constexpr int kBwdRing = 4;
+// one ring slot: a 64-row Q (or K) tile and the dO (or V) tile
+constexpr int kTile = 64 * 128 * 2;
+constexpr int kQSlot = 2 * kTile;
+constexpr int kWaitVm18 = 0x0F72 | (1 << 14);
+constexpr int kWaitVm0 = 0x0F70;
+
+// LDS byte offset of a shared-memory object, opaque to alias analysis: loads
+// aimed at it carry no object identity, so the compiler adds no wait of its
+// own between them and reads of other ring slots (the ring's explicit waits
+// and barriers order them).
+__device__ inline uint32_t lds_offset(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+// direct global->LDS load: 64 lanes x 16 B (or 4 B) to LDS offset `o`
+__device__ inline void dma16(const uint4* g, uint32_t o) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)(uintptr_t)o, 16, 0,
+                                   0);
+}
+__device__ inline void dma4(const float* g, uint32_t o) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)(uintptr_t)o, 4, 0,
+                                   0);
+}
+
+// Per-lane byte offsets inside a swizzled 64-row tile (row stride 256 B).
+// ro[kk]: the 16-byte chunk 2kk + hl of row l32 (the MFMA row operand; row
+// l32 + 32 adds 8192).  to[db][0/1]: the two 8-byte transposed reads of
+// channels 32db.. for rows 4hl + (lane&15)/4 and 8 below (rows 16c.. add
+// 4096 c).  The swizzle depends on the row's low four bits only, so these
+// constants cover every read and the rest folds into instruction offsets.
+__device__ inline void row_offsets(int lane, uint32_t (&ro)[8]) {
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int sw = chunk_swizzle(l32);
+#pragma unroll
+  for (int kk = 0; kk < 8; kk++) ro[kk] = l32 * 256 + (((2 * kk + hl) ^ sw) << 4);
+}
+__device__ inline void tr_offsets(int lane, uint32_t (&to)[4][2]) {
+  const int rA = 4 * (lane >> 5) + ((lane & 15) >> 2), rB = rA + 8;
+  const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int off = 8 * (lane & 1);
+#pragma unroll
+  for (int db = 0; db < 4; db++) {
+    to[db][0] = rA * 256 + (((4 * db + cl) ^ chunk_swizzle(rA)) << 4) + off;
+    to[db][1] = rB * 256 + (((4 * db + cl) ^ chunk_swizzle(rB)) << 4) + off;
+  }
+}
+__device__ inline bf16x8 ld_frag(const char* p) {
+  return __builtin_bit_cast(bf16x8, *(const uint4*)p);
+}
+__device__ inline bf16x8 ld_tfrag(const char* pa, const char* pb) {
+  s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b*)pa);
+  s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b*)pb);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 }  // namespace
@@ -167,14 +235,16 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ colt_ptr,
     const int32_t* __restrict__ colt_idx, int H, int W, int Z, int64_t N, float c_log2,
     float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][64 * 128];
-  __shared__ __attribute__((aligned(16))) uint16_t sD[2][64 * 128];
-  __shared__ __attribute__((aligned(16))) float sL[2][64];
-  __shared__ __attribute__((aligned(16))) float sDel[2][64];
+  // ring of kBwdRing query-tile slots, kBwdRing - 1 of them in flight: Q and
+  // dO tiles, and the LSE and Delta columns (two objects, so that the reads of
+  // each carry their own alias scope)
+  __shared__ __attribute__((aligned(16))) char ring[kBwdRing * kQSlot];
+  __shared__ __attribute__((aligned(16))) float ringc[kBwdRing * 128];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int64_t upH = N >> 7;
-  const int h = (int)(blockIdx.x / upH);
-  const int64_t r0 = (blockIdx.x - (int64_t)h * upH) << 7;
+  const int64_t unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int h = (int)(unit / upH);
+  const int64_t r0 = (unit - (int64_t)h * upH) << 7;
   const int m = (int)(r0 >> 9);
   const Shape sh = d_shapes[shape_id[(int64_t)h * Z + m]];
   const int B = sh.volume;
@@ -182,7 +252,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
   const int64_t hoff = blk_off[h];
   const int64_t gbase = hoff + zone_base[(int64_t)h * Z + m];
   const int64_t gA = gbase + rz / B, gB = gbase + (rz + 64) / B;
-  const int half = wv >> 1;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const int half = wvu >> 1;  // waves 0-1 hold keys of block gA, waves 2-3 of gB
 
   // this wave's 32 keys: K and V rows as MFMA B operands (k = channel)
   const int64_t hrow = (int64_t)h * N;
@@ -193,6 +264,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     kr[kk] = row_chunk(kp, krow, 2 * kk + hl);
     vr[kk] = row_chunk(vp, krow, 2 * kk + hl);
   }
+  // the key fragments land before any tile load is issued, so the ring's
+  // waits only ever concern tiles (the empty asm consumes them here)
+#pragma unroll
+  for (int kk = 0; kk < 8; kk++) asm volatile("" : "+v"(kr[kk]), "+v"(vr[kk]));
   f32x16 dkt[4], dvt[4];
 #pragma unroll
   for (int db = 0; db < 4; db++)
@@ -201,111 +276,132 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
       dkt[db][r] = 0.0f;
       dvt[db][r] = 0.0f;
     }
+#pragma unroll
+  for (int db = 0; db < 4; db++) asm volatile("" : "+a"(dkt[db]), "+a"(dvt[db]));
+  uint32_t ro[8], to[4][2];
+  row_offsets(lane, ro);
+  tr_offsets(lane, to);
 
   TIter it;
   it.init(colt_idx, colt_ptr[gA], colt_ptr[gA + 1], colt_ptr[gB], colt_ptr[gB + 1], gA == gB,
           blk_start, blk_shape, hoff);
   const uint4* qbase = (const uint4*)(qp + hrow * 128);
   const uint4* dbase = (const uint4*)(dop + hrow * 128);
-  const int wvu = __builtin_amdgcn_readfirstlane(wv);
-  auto stage = [&](int bi, int64_t row) {
+  // waves 0 and 2 bring the LSE column, waves 1 and 3 Delta (both pairs write
+  // the same values), so that every wave issues the same nine loads per tile
+  const float* colsrc = (wvu & 1) ? delta + hrow : lse2 + hrow;
+  const uint32_t lring = lds_offset(ring);
+  const uint32_t lcol = lds_offset(ringc) + (wvu & 1) * 256;
+  auto stage = [&](int b, int64_t row) {
     const uint4* qs = qbase + row * 16;
     const uint4* ds = dbase + row * 16;
+    const uint32_t o = lring + b * kQSlot;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int piece = i * 256 + wvu * 64;
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(qs + piece + lane),
-          (__attribute__((address_space(3))) void*)((uint4*)sQ[bi] + piece), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(ds + piece + lane),
-          (__attribute__((address_space(3))) void*)((uint4*)sD[bi] + piece), 16, 0, 0);
+      const uint32_t piece = i * 256 + wvu * 64;
+      dma16(qs + piece + lane, o + piece * 16);
+      dma16(ds + piece + lane, o + kTile + piece * 16);
     }
-    if (wvu == 0)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(lse2 + hrow + row + lane),
-          (__attribute__((address_space(3))) void*)(sL[bi]), 4, 0, 0);
-    if (wvu == 1)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(delta + hrow + row + lane),
-          (__attribute__((address_space(3))) void*)(sDel[bi]), 4, 0, 0);
+    dma4(colsrc + row + lane, lcol + b * 512);
   };
 
-  int buf = 0, cur_fa = 0, cur_fb = 0;
-  if (it.valid) {
-    stage(0, it.row);
-    cur_fa = it.fa;
-    cur_fb = it.fb;
-    it.advance();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    while (true) {
-      const bool has_next = it.valid;
-      const int nfa = it.fa, nfb = it.fb;
-      if (has_next) stage(buf ^ 1, it.row);
-      const bool active = half == 0 ? cur_fa : cur_fb;
-      if (active) {
-        const uint16_t* Qs = sQ[buf];
-        const uint16_t* Ds = sD[buf];
+  uint32_t ring_f = 0;  // per slot: bit 0 = block gA listed, bit 1 = block gB listed
+  int nreal = 0;        // real tiles issued; later slots re-read the last one
+  int64_t last_row = 0;
+  auto issue = [&](int b) {
+    int64_t row = last_row;
+    uint32_t f = 0;
+    if (it.valid) {
+      row = it.row;
+      f = (uint32_t)(it.fa | (it.fb << 1));
+      last_row = row;
+      nreal++;
+      it.advance();
+    }
+    ring_f = (ring_f & ~(3u << (2 * b))) | (f << (2 * b));
+    stage(b, row);
+  };
+  issue(0);
+  issue(1);
+  issue(2);
+  // One ring step per tile, in every wave: tile j and every older load are
+  // done once at most the 18 loads of tiles j+1 and j+2 are pending; after
+  // the barrier every wave is done with tile j-1, whose slot takes tile j+3.
+  auto ring_step = [&](int j) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm18);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue((j + kBwdRing - 1) & (kBwdRing - 1));
+  };
+  auto listed = [&](int j) { return ((ring_f >> (2 * (j & (kBwdRing - 1)) + half)) & 1u) != 0; };
+  int j = 0;
+  while (true) {
+    // tiles whose query block does not list this wave's key block only move
+    // the ring along (a loop of its own, so the accumulators stay in place)
+    while (j < nreal && !listed(j)) ring_step(j++);
+    if (j >= nreal) break;
+    ring_step(j);
+    const char* sq = ring + (j & (kBwdRing - 1)) * kQSlot;  // Q tile
+    const char* sd = sq + kTile;                            // dO tile
+    const float* sl = ringc + (j & (kBwdRing - 1)) * 128;   // log2(e) LSE
+    const float* sdl = sl + 64;                             // Delta
 #pragma unroll
-        for (int qb = 0; qb < 2; qb++) {
-          f32x16 s, dp;
+    for (int qb = 0; qb < 2; qb++) {
+      f32x16 s, dp;
 #pragma unroll
-          for (int r = 0; r < 16; r++) {
-            s[r] = 0.0f;
-            dp[r] = 0.0f;
-          }
+      for (int r = 0; r < 16; r++) {
+        s[r] = 0.0f;
+        dp[r] = 0.0f;
+      }
 #pragma unroll
-          for (int kk = 0; kk < 8; kk++) {
-            bf16x8 aq = lds_chunk(Qs, 32 * qb + l32, 2 * kk + hl);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kr[kk], s, 0, 0, 0);
-            bf16x8 ad = lds_chunk(Ds, 32 * qb + l32, 2 * kk + hl);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vr[kk], dp, 0, 0, 0);
-          }
-          // rows of s/dp held by this lane: q = 32qb + 8j + 4hl + i (r = 4j + i)
-          uint32_t pp[8], ps[8];
+      for (int kk = 0; kk < 8; kk++) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sq + qb * 8192 + ro[kk]), kr[kk], s,
+                                                    0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sd + qb * 8192 + ro[kk]), vr[kk],
+                                                     dp, 0, 0, 0);
+      }
+      // rows of s/dp held by this lane: q = 32qb + 8jj + 4hl + i (r = 4jj + i)
+      uint32_t pp[8], ps[8];
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const float4 L4 = *(const float4*)(&sL[buf][32 * qb + 8 * j + 4 * hl]);
-            const float4 D4 = *(const float4*)(&sDel[buf][32 * qb + 8 * j + 4 * hl]);
-            const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-            const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
-            float pv[4], sv[4];
+      for (int jj = 0; jj < 4; jj++) {
+        const f32x4 Lv = *(const f32x4*)(sl + 32 * qb + 8 * jj + 4 * hl);
+        const f32x4 Dv = *(const f32x4*)(sdl + 32 * qb + 8 * jj + 4 * hl);
+        float pv[4], sv[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-              pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * j + i], c_log2, -Lv[i]));
-              sv[i] = pv[i] * (dp[4 * j + i] - Dv[i]);
-            }
-            pp[2 * j] = pk2(pv[0], pv[1]);
-            pp[2 * j + 1] = pk2(pv[2], pv[3]);
-            ps[2 * j] = pk2(sv[0], sv[1]);
-            ps[2 * j + 1] = pk2(sv[2], sv[3]);
-          }
+        for (int i = 0; i < 4; i++) {
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * jj + i], c_log2, -Lv[i]));
+          sv[i] = pv[i] * (dp[4 * jj + i] - Dv[i]);
+        }
+        pp[2 * jj] = pk2(pv[0], pv[1]);
+        pp[2 * jj + 1] = pk2(pv[2], pv[3]);
+        ps[2 * jj] = pk2(sv[0], sv[1]);
+        ps[2 * jj + 1] = pk2(sv[2], sv[3]);
+      }
 #pragma unroll
-          for (int c = 0; c < 2; c++) {
-            const bf16x8 bp = __builtin_bit_cast(
-                bf16x8, make_uint4(pp[4 * c], pp[4 * c + 1], pp[4 * c + 2], pp[4 * c + 3]));
-            const bf16x8 bs = __builtin_bit_cast(
-                bf16x8, make_uint4(ps[4 * c], ps[4 * c + 1], ps[4 * c + 2], ps[4 * c + 3]));
+      for (int c = 0; c < 2; c++) {
+        const bf16x8 bp = __builtin_bit_cast(
+            bf16x8, make_uint4(pp[4 * c], pp[4 * c + 1], pp[4 * c + 2], pp[4 * c + 3]));
+        const bf16x8 bs = __builtin_bit_cast(
+            bf16x8, make_uint4(ps[4 * c], ps[4 * c + 1], ps[4 * c + 2], ps[4 * c + 3]));
+        const int cc = (2 * qb + c) * 4096;  // rows 16 (2qb + c) ..
 #pragma unroll
-            for (int db = 0; db < 4; db++) {
-              bf16x8 ado = lds_tfrag(Ds, 2 * qb + c, db, lane);
-              dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, bp, dvt[db], 0, 0, 0);
-              bf16x8 aqq = lds_tfrag(Qs, 2 * qb + c, db, lane);
-              dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqq, bs, dkt[db], 0, 0, 0);
-            }
-          }
+        for (int db = 0; db < 4; db++) {
+          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              ld_tfrag(sd + cc + to[db][0], sd + cc + to[db][1]), bp, dvt[db], 0, 0, 0);
+          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              ld_tfrag(sq + cc + to[db][0], sq + cc + to[db][1]), bs, dkt[db], 0, 0, 0);
         }
       }
-      if (!has_next) break;
-      cur_fa = nfa;
-      cur_fb = nfb;
-      it.advance();
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      buf ^= 1;
     }
+    // pin the accumulators to the accumulation registers across the loop
+    // (otherwise they are parked in ordinary registers and copied both ways
+    // on every tile)
+#pragma unroll
+    for (int db = 0; db < 4; db++) asm volatile("" : "+a"(dkt[db]), "+a"(dvt[db]));
+    j++;
   }
+  // no tile load may still be writing LDS when the work-group ends
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   // lane holds key r0 + 32wv + l32, channels 32db + 8j + 4hl + 0..3
   const int64_t p = r0 + wv * 32 + l32;
   const int64_t tok = token_of(sh, m, (int)(p & 511), H, W);
@@ -339,8 +435,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][64 * 128];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int64_t upH = N >> 7;
-  const int h = (int)(blockIdx.x / upH);
-  const int64_t r0 = (blockIdx.x - (int64_t)h * upH) << 7;
+  const int64_t unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int h = (int)(unit / upH);
+  const int64_t r0 = (unit - (int64_t)h * upH) << 7;
   const int m = (int)(r0 >> 9);
   const Shape sh = d_shapes[shape_id[(int64_t)h * Z + m]];
   const int B = sh.volume;

@@ -69,6 +69,25 @@ __host__ __device__ inline int chunk_swizzle(int rho) {
   return ((rho & 3) << 2) | ((rho >> 2) & 3);
 }
 
+// Work-groups are dispatched to the 8 XCDs round-robin by block id, and each
+// XCD has its own L2.  This maps the block id to a logical work unit so that
+// XCD x runs the contiguous unit range [x*G/8, (x+1)*G/8): neighbouring units
+// (same head, nearby zones, near-identical key lists) then share one L2 and
+// walk the same K/V tiles at the same time.
+__device__ inline int64_t xcd_unit(int64_t b, int64_t G) {
+  const int64_t x = b & 7, i = b >> 3;
+  const int64_t per = G >> 3, rem = G & 7;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+// Shape id of global block g from the byte array blk_shape, read through its
+// aligned 32-bit word so that a uniform index becomes a scalar load (a vector
+// byte load would be counted with, and waited for behind, in-flight tile loads).
+__device__ inline int block_shape_at(const uint8_t* blk_shape, int64_t g) {
+  const uint32_t w = ((const uint32_t*)blk_shape)[g >> 2];
+  return (int)((w >> (8 * (g & 3))) & 0xffu);
+}
+
 // ---------------------------------------------------------------- numbers
 __device__ inline float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
