@@ -8,186 +8,32 @@
 //  * prep: Q and dO gathered into the permuted, swizzled tile layout of K/V;
 //    Delta and log2(e) * LSE per permuted row;
 //  * dK/dV: a work-group owns 128 permuted key rows (4 waves x 32 keys, K and
-//    V of its keys in registers) and walks the query blocks whose S_i holds
-//    its key blocks (key-major lists); Q and dO tiles are staged into LDS by
-//    direct global->LDS loads, double-buffered; per 32-query slice it forms
-//    S = Q K^T and dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS with
-//    the transposed operands read by ds_read_b64_tr_b16;
-//  * dQ: a work-group owns 128 permuted query rows and walks its key blocks
-//    as the forward does: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
-#include "prism_common.h"
+//    V of its keys in registers, dK/dV accumulators pinned to AGPRs) and
+//    walks the query blocks whose S_i holds its key blocks (key-major lists);
+//    Q and dO tiles with their LSE and Delta columns stream through a 4-slot
+//    LDS ring; per 32-query slice it forms S = Q K^T and dP = dO V^T, then
+//    dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by
+//    ds_read_b64_tr_b16;
+//  * dQ: a work-group owns 256 permuted query rows (8 waves) and walks its
+//    key blocks as the forward does: S^T = K Q^T, dP^T = V dO^T,
+//    dQ^T += K^T dS^T.
+#include "prism_attn_common.h"
 #include "prism_kernels.h"
 
 namespace prism {
 
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4b;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-namespace {
-
-struct UIter {
-  const int32_t* col;
-  int64_t a, ae, b, be;
-  bool same;
-  __device__ bool next(int& j, int& fa, int& fb) {
-    if (same) {
-      if (a >= ae) return false;
-      j = col[a++];
-      fa = fb = 1;
-      return true;
-    }
-    int ja = a < ae ? col[a] : 0x7fffffff;
-    int jb = b < be ? col[b] : 0x7fffffff;
-    if (ja == 0x7fffffff && jb == 0x7fffffff) return false;
-    j = ja < jb ? ja : jb;
-    fa = ja == j;
-    fb = jb == j;
-    if (fa) a++;
-    if (fb) b++;
-    return true;
-  }
-};
-
-struct TIter {
-  UIter U;
-  const int32_t* blk_start;
-  const uint8_t* blk_shape;
-  int64_t hoff;
-  int64_t row;
-  int t, nt, fa, fb;
-  bool valid;
-  __device__ void init(const int32_t* col, int64_t a, int64_t ae, int64_t b, int64_t be,
-                       bool same, const int32_t* bs, const uint8_t* bsh, int64_t off) {
-    U.col = col;
-    U.a = a;
-    U.ae = ae;
-    U.b = b;
-    U.be = be;
-    U.same = same;
-    blk_start = bs;
-    blk_shape = bsh;
-    hoff = off;
-    valid = true;
-    t = 0;
-    nt = 0;
-    advance();
-  }
-  __device__ void advance() {
-    if (valid && t + 1 < nt) {
-      t++;
-      row += 64;
-      return;
-    }
-    int j;
-    valid = U.next(j, fa, fb);
-    if (valid) {
-      row = blk_start[hoff + j];
-      nt = d_shapes[block_shape_at(blk_shape, hoff + j)].volume >> 6;
-      t = 0;
-    }
-  }
-};
-
-__device__ inline bf16x8 lds_chunk(const uint16_t* tile, int row, int chunk) {
-  const uint4* p = (const uint4*)(tile + row * 128 + ((chunk ^ chunk_swizzle(row)) << 3));
-  return __builtin_bit_cast(bf16x8, *p);
-}
-
-// fragment of X^T (rows = channels 32db..32db+31, k = 16 rows of chunk c of
-// the 64-row tile X, in the order {16c+4hl+0..3, 16c+8+4hl+0..3})
-__device__ inline bf16x8 lds_tfrag(const uint16_t* tile, int c, int db, int lane) {
-  const int hl = lane >> 5;
-  const int rowA = 16 * c + 4 * hl + ((lane & 15) >> 2);
-  const int rowB = rowA + 8;
-  const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int off = 4 * (lane & 1);
-  const uint16_t* pa = tile + rowA * 128 + ((chunk ^ chunk_swizzle(rowA)) << 3) + off;
-  const uint16_t* pb = tile + rowB * 128 + ((chunk ^ chunk_swizzle(rowB)) << 3) + off;
-  s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b*)pa);
-  s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b*)pb);
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  s16x8 r = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-__device__ inline uint32_t pk2(float a, float b) {
-  // one v_cvt_pk_bf16_f32 (round to nearest even)
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
-// one row chunk (16 B) of a permuted, swizzled [rows][128] bf16 buffer
-__device__ inline bf16x8 row_chunk(const uint16_t* buf, int64_t row, int chunk) {
-  return __builtin_bit_cast(
-      bf16x8, *(const uint4*)(buf + row * 128 + ((chunk ^ chunk_swizzle((int)(row & 63))) << 3)));
-}
-
-// Query-tile ring depth of dK/dV; s_waitcnt immediates (vmcnt in bits 3:0
-// and 15:14, expcnt and lgkmcnt at their maxima) for the loads of two tiles
-// (nine per wave each) and for none.
-constexpr int kBwdRing = 4;
-// one ring slot: a 64-row Q (or K) tile and the dO (or V) tile
-constexpr int kTile = 64 * 128 * 2;
-constexpr int kQSlot = 2 * kTile;
-constexpr int kWaitVm18 = 0x0F72 | (1 << 14);
-constexpr int kWaitVm0 = 0x0F70;
-
-// LDS byte offset of a shared-memory object, opaque to alias analysis: loads
-// aimed at it carry no object identity, so the compiler adds no wait of its
-// own between them and reads of other ring slots (the ring's explicit waits
-// and barriers order them).
-__device__ inline uint32_t lds_offset(const void* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
-}
-// direct global->LDS load: 64 lanes x 16 B (or 4 B) to LDS offset `o`
-__device__ inline void dma16(const uint4* g, uint32_t o) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)(uintptr_t)o, 16, 0,
-                                   0);
-}
-__device__ inline void dma4(const float* g, uint32_t o) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)(uintptr_t)o, 4, 0,
-                                   0);
-}
-
-// Per-lane byte offsets inside a swizzled 64-row tile (row stride 256 B).
-// ro[kk]: the 16-byte chunk 2kk + hl of row l32 (the MFMA row operand; row
-// l32 + 32 adds 8192).  to[db][0/1]: the two 8-byte transposed reads of
-// channels 32db.. for rows 4hl + (lane&15)/4 and 8 below (rows 16c.. add
-// 4096 c).  The swizzle depends on the row's low four bits only, so these
-// constants cover every read and the rest folds into instruction offsets.
-__device__ inline void row_offsets(int lane, uint32_t (&ro)[8]) {
-  const int l32 = lane & 31, hl = lane >> 5;
-  const int sw = chunk_swizzle(l32);
-#pragma unroll
-  for (int kk = 0; kk < 8; kk++) ro[kk] = l32 * 256 + (((2 * kk + hl) ^ sw) << 4);
-}
-__device__ inline void tr_offsets(int lane, uint32_t (&to)[4][2]) {
-  const int rA = 4 * (lane >> 5) + ((lane & 15) >> 2), rB = rA + 8;
-  const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int off = 8 * (lane & 1);
-#pragma unroll
-  for (int db = 0; db < 4; db++) {
-    to[db][0] = rA * 256 + (((4 * db + cl) ^ chunk_swizzle(rA)) << 4) + off;
-    to[db][1] = rB * 256 + (((4 * db + cl) ^ chunk_swizzle(rB)) << 4) + off;
-  }
-}
-__device__ inline bf16x8 ld_frag(const char* p) {
-  return __builtin_bit_cast(bf16x8, *(const uint4*)p);
-}
-__device__ inline bf16x8 ld_tfrag(const char* pa, const char* pb) {
-  s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b*)pa);
-  s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4b*)pb);
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  s16x8 r = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-}  // namespace
+// dK/dV work units: 128 key rows, 4 waves x 32 keys; each query tile of the
+// ring carries its Q and dO tiles and its LSE and Delta columns.
+constexpr int kKvRows = 128;
+constexpr int kKvWaves = kKvRows / 32;
+// loads per wave per query tile: 2 x 16 KB in 1 KB pieces over 4 waves, plus
+// one 256-byte column load
+constexpr int kKvLoads = 2 * kTile / (kKvWaves * 1024) + 1;
+// dQ work units: 256 query rows, 8 waves x 32 rows; K/V tile pairs as in the
+// forward
+constexpr int kDqRows = 256;
+constexpr int kDqWaves = kDqRows / 32;
+constexpr int kDqLoads = 2 * kTile / (kDqWaves * 1024);
 
 // ---------------------------------------------------------------- prep
 // One block of 256 threads per 64-row tile; wave w handles rows w, w+4, ...
@@ -226,7 +72,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(
 }
 
 // ---------------------------------------------------------------- dK, dV
-__global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
+__global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
     const uint16_t* __restrict__ qp, const uint16_t* __restrict__ dop,
     const float* __restrict__ lse2, const float* __restrict__ delta,
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
@@ -235,25 +81,23 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ colt_ptr,
     const int32_t* __restrict__ colt_idx, int H, int W, int Z, int64_t N, float c_log2,
     float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-  // ring of kBwdRing query-tile slots, kBwdRing - 1 of them in flight: Q and
-  // dO tiles, and the LSE and Delta columns (two objects, so that the reads of
-  // each carry their own alias scope)
-  __shared__ __attribute__((aligned(16))) char ring[kBwdRing * kQSlot];
-  __shared__ __attribute__((aligned(16))) float ringc[kBwdRing * 128];
+  // ring of query-tile slots: Q and dO tiles, and the LSE and Delta columns
+  // (two objects, so that the reads of each carry their own alias scope)
+  __shared__ __attribute__((aligned(16))) char ring[kRing * 2 * kTile];
+  __shared__ __attribute__((aligned(16))) float ringc[kRing * 128];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  const int64_t upH = N >> 7;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const int64_t upH = N / kKvRows;
   const int64_t unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit / upH);
-  const int64_t r0 = (unit - (int64_t)h * upH) << 7;
+  const int64_t r0 = (unit - (int64_t)h * upH) * kKvRows;
   const int m = (int)(r0 >> 9);
   const Shape sh = d_shapes[shape_id[(int64_t)h * Z + m]];
   const int B = sh.volume;
   const int rz = (int)(r0 & 511);
   const int64_t hoff = blk_off[h];
-  const int64_t gbase = hoff + zone_base[(int64_t)h * Z + m];
-  const int64_t gA = gbase + rz / B, gB = gbase + (rz + 64) / B;
-  const int wvu = __builtin_amdgcn_readfirstlane(wv);
-  const int half = wvu >> 1;  // waves 0-1 hold keys of block gA, waves 2-3 of gB
+  const int nlists = B >= kKvRows ? 1 : kKvRows / B;  // key blocks in the unit
+  const int mylist = (32 * wvu) / B < nlists ? (32 * wvu) / B : 0;
 
   // this wave's 32 keys: K and V rows as MFMA B operands (k = channel)
   const int64_t hrow = (int64_t)h * N;
@@ -282,9 +126,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
   row_offsets(lane, ro);
   tr_offsets(lane, to);
 
-  TIter it;
-  it.init(colt_idx, colt_ptr[gA], colt_ptr[gA + 1], colt_ptr[gB], colt_ptr[gB + 1], gA == gB,
-          blk_start, blk_shape, hoff);
+  TileIter it;
+  it.init(colt_ptr, colt_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_start,
+          blk_shape, hoff);
   const uint4* qbase = (const uint4*)(qp + hrow * 128);
   const uint4* dbase = (const uint4*)(dop + hrow * 128);
   // waves 0 and 2 bring the LSE column, waves 1 and 3 Delta (both pairs write
@@ -295,7 +139,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
   auto stage = [&](int b, int64_t row) {
     const uint4* qs = qbase + row * 16;
     const uint4* ds = dbase + row * 16;
-    const uint32_t o = lring + b * kQSlot;
+    const uint32_t o = lring + b * 2 * kTile;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const uint32_t piece = i * 256 + wvu * 64;
@@ -305,7 +149,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     dma4(colsrc + row + lane, lcol + b * 512);
   };
 
-  uint32_t ring_f = 0;  // per slot: bit 0 = block gA listed, bit 1 = block gB listed
+  uint32_t ring_f = 0;  // list masks of the tiles in the ring, a byte per slot
   int nreal = 0;        // real tiles issued; later slots re-read the last one
   int64_t last_row = 0;
   auto issue = [&](int b) {
@@ -313,27 +157,25 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     uint32_t f = 0;
     if (it.valid) {
       row = it.row;
-      f = (uint32_t)(it.fa | (it.fb << 1));
+      f = (uint32_t)it.mask;
       last_row = row;
       nreal++;
       it.advance();
     }
-    ring_f = (ring_f & ~(3u << (2 * b))) | (f << (2 * b));
+    ring_f = (ring_f & ~(0xffu << (8 * b))) | (f << (8 * b));
     stage(b, row);
   };
   issue(0);
   issue(1);
   issue(2);
-  // One ring step per tile, in every wave: tile j and every older load are
-  // done once at most the 18 loads of tiles j+1 and j+2 are pending; after
-  // the barrier every wave is done with tile j-1, whose slot takes tile j+3.
+  // one ring step per tile, in every wave
   auto ring_step = [&](int j) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm18);
+    __builtin_amdgcn_s_waitcnt(wait_vm(2 * kKvLoads));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue((j + kBwdRing - 1) & (kBwdRing - 1));
+    issue((j + kRing - 1) & (kRing - 1));
   };
-  auto listed = [&](int j) { return ((ring_f >> (2 * (j & (kBwdRing - 1)) + half)) & 1u) != 0; };
+  auto listed = [&](int j) { return ((ring_f >> (8 * (j & (kRing - 1)) + mylist)) & 1u) != 0; };
   int j = 0;
   while (true) {
     // tiles whose query block does not list this wave's key block only move
@@ -341,9 +183,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     while (j < nreal && !listed(j)) ring_step(j++);
     if (j >= nreal) break;
     ring_step(j);
-    const char* sq = ring + (j & (kBwdRing - 1)) * kQSlot;  // Q tile
+    const char* sq = ring + (j & (kRing - 1)) * 2 * kTile;  // Q tile
     const char* sd = sq + kTile;                            // dO tile
-    const float* sl = ringc + (j & (kBwdRing - 1)) * 128;   // log2(e) LSE
+    const float* sl = ringc + (j & (kRing - 1)) * 128;      // log2(e) LSE
     const float* sdl = sl + 64;                             // Delta
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
@@ -401,7 +243,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     j++;
   }
   // no tile load may still be writing LDS when the work-group ends
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
   // lane holds key r0 + 32wv + l32, channels 32db + 8j + 4hl + 0..3
   const int64_t p = r0 + wv * 32 + l32;
   const int64_t tok = token_of(sh, m, (int)(p & 511), H, W);
@@ -422,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
 }
 
 // ---------------------------------------------------------------- dQ
-__global__ __launch_bounds__(256, 2) void k_bwd_dq(
+__global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
     const uint16_t* __restrict__ qp, const uint16_t* __restrict__ dop,
     const float* __restrict__ lse2, const float* __restrict__ delta,
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
@@ -431,21 +273,28 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, int H, int W, int Z, int64_t N, float c_log2,
     float scale, uint16_t* __restrict__ dq) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][64 * 128];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][64 * 128];
+  __shared__ __attribute__((aligned(16))) char ringK[kRing * kTile];
+  __shared__ __attribute__((aligned(16))) char ringV[kRing * kTile];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  const int64_t upH = N >> 7;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const int64_t upH = N / kDqRows;
   const int64_t unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit / upH);
-  const int64_t r0 = (unit - (int64_t)h * upH) << 7;
+  const int64_t r0 = (unit - (int64_t)h * upH) * kDqRows;
   const int m = (int)(r0 >> 9);
   const Shape sh = d_shapes[shape_id[(int64_t)h * Z + m]];
   const int B = sh.volume;
   const int rz = (int)(r0 & 511);
   const int64_t hoff = blk_off[h];
-  const int64_t gbase = hoff + zone_base[(int64_t)h * Z + m];
-  const int64_t gA = gbase + rz / B, gB = gbase + (rz + 64) / B;
-  const int half = wv >> 1;
+  const int nlists = B >= kDqRows ? 1 : kDqRows / B;  // query blocks in the unit
+  const int mylist = (32 * wvu) / B < nlists ? (32 * wvu) / B : 0;
+
+  TileIter it;
+  it.init(row_ptr, col_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_start,
+          blk_shape, hoff);
+
+  // this wave's 32 query rows: Q and dO as MFMA B operands, LSE and Delta of
+  // the lane's row
   const int64_t hrow = (int64_t)h * N;
   const int64_t qrow = hrow + r0 + wv * 32 + l32;
   bf16x8 qf[8], df[8];
@@ -454,105 +303,121 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     qf[kk] = row_chunk(qp, qrow, 2 * kk + hl);
     df[kk] = row_chunk(dop, qrow, 2 * kk + hl);
   }
-  const float L = lse2[qrow];
-  const float Dl = delta[qrow];
+  float L = lse2[qrow];
+  float Dl = delta[qrow];
+  // all of it lands before any tile load is issued (the empty asm consumes
+  // it), so the ring's waits only ever concern tiles
+#pragma unroll
+  for (int kk = 0; kk < 8; kk++) asm volatile("" : "+v"(qf[kk]), "+v"(df[kk]));
+  asm volatile("" : "+v"(L), "+v"(Dl));
+  uint32_t ro[8], to[4][2];
+  row_offsets(lane, ro);
+  tr_offsets(lane, to);
   f32x16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; db++)
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[db][r] = 0.0f;
 
-  TIter it;
-  it.init(col_idx, row_ptr[gA], row_ptr[gA + 1], row_ptr[gB], row_ptr[gB + 1], gA == gB,
-          blk_start, blk_shape, hoff);
   const uint4* kbase = (const uint4*)(kp + hrow * 128);
   const uint4* vbase = (const uint4*)(vp + hrow * 128);
-  const int wvu = __builtin_amdgcn_readfirstlane(wv);
-  auto stage = [&](int bi, int64_t row) {
+  const uint32_t lK = lds_offset(ringK), lV = lds_offset(ringV);
+  auto stage = [&](int b, int64_t row) {
     const uint4* ks = kbase + row * 16;
     const uint4* vs = vbase + row * 16;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int piece = i * 256 + wvu * 64;
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(ks + piece + lane),
-          (__attribute__((address_space(3))) void*)((uint4*)sK[bi] + piece), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(vs + piece + lane),
-          (__attribute__((address_space(3))) void*)((uint4*)sV[bi] + piece), 16, 0, 0);
+    for (int i = 0; i < 2; i++) {
+      const uint32_t piece = i * 512 + wvu * 64;
+      dma16(ks + piece + lane, lK + b * kTile + piece * 16);
+      dma16(vs + piece + lane, lV + b * kTile + piece * 16);
     }
   };
-  int buf = 0, cur_fa = 0, cur_fb = 0;
-  if (it.valid) {
-    stage(0, it.row);
-    cur_fa = it.fa;
-    cur_fb = it.fb;
-    it.advance();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    while (true) {
-      const bool has_next = it.valid;
-      const int nfa = it.fa, nfb = it.fb;
-      if (has_next) stage(buf ^ 1, it.row);
-      const bool active = half == 0 ? cur_fa : cur_fb;
-      if (active) {
-        const uint16_t* Ks = sK[buf];
-        const uint16_t* Vs = sV[buf];
-        f32x16 st[2], dpt[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            st[kb][r] = 0.0f;
-            dpt[kb][r] = 0.0f;
-          }
-#pragma unroll
-        for (int kk = 0; kk < 8; kk++)
-#pragma unroll
-          for (int kb = 0; kb < 2; kb++) {
-            bf16x8 ak = lds_chunk(Ks, 32 * kb + l32, 2 * kk + hl);
-            st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kk], st[kb], 0, 0, 0);
-            bf16x8 av = lds_chunk(Vs, 32 * kb + l32, 2 * kk + hl);
-            dpt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, df[kk], dpt[kb], 0, 0, 0);
-          }
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-          uint32_t pk[4];
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const int r = 8 * (c & 1) + 2 * e;
-            float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r], c_log2, -L));
-            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r + 1], c_log2, -L));
-            pk[e] = pk2(p0 * (dpt[c >> 1][r] - Dl), p1 * (dpt[c >> 1][r + 1] - Dl));
-          }
-          const bf16x8 bs = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-#pragma unroll
-          for (int db = 0; db < 4; db++) {
-            bf16x8 ak = lds_tfrag(Ks, c, db, lane);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bs, acc[db], 0, 0, 0);
-          }
-        }
-      }
-      if (!has_next) break;
-      cur_fa = nfa;
-      cur_fb = nfb;
+  uint32_t ring_mask = 0;  // list masks of the tiles in the ring, a byte per slot
+  int nreal = 0;           // real tiles issued
+  int64_t last_row = 0;
+  auto issue = [&](int b) {
+    int64_t row = last_row;
+    uint32_t mask = 0;
+    if (it.valid) {
+      row = it.row;
+      mask = (uint32_t)it.mask;
+      last_row = row;
+      nreal++;
       it.advance();
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      buf ^= 1;
     }
+    ring_mask = (ring_mask & ~(0xffu << (8 * b))) | (mask << (8 * b));
+    stage(b, row);
+  };
+  auto ring_step = [&](int j) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDqLoads));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue((j + kRing - 1) & (kRing - 1));
+  };
+  auto listed = [&](int j) {
+    return ((ring_mask >> (8 * (j & (kRing - 1)) + mylist)) & 1u) != 0;
+  };
+  issue(0);
+  issue(1);
+  issue(2);
+  int j = 0;
+  while (true) {
+    while (j < nreal && !listed(j)) ring_step(j++);
+    if (j >= nreal) break;
+    ring_step(j);
+    const char* sk = ringK + (j & (kRing - 1)) * kTile;
+    const char* sv = ringV + (j & (kRing - 1)) * kTile;
+    // S^T = K Q^T and dP^T = V dO^T: lane holds query l32, keys 8r' + 4hl + i
+    f32x16 st[2], dpt[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        st[kb][r] = 0.0f;
+        dpt[kb][r] = 0.0f;
+      }
+#pragma unroll
+    for (int kk = 0; kk < 8; kk++)
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++) {
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sk + kb * 8192 + ro[kk]),
+                                                         qf[kk], st[kb], 0, 0, 0);
+        dpt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sv + kb * 8192 + ro[kk]),
+                                                          df[kk], dpt[kb], 0, 0, 0);
+      }
+    // dS = P (dP - Delta) as the B operand of dQ^T += K^T dS^T
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int r = 8 * (c & 1) + 2 * e;
+        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r], c_log2, -L));
+        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r + 1], c_log2, -L));
+        pk[e] = pk2(p0 * (dpt[c >> 1][r] - Dl), p1 * (dpt[c >> 1][r + 1] - Dl));
+      }
+      const bf16x8 bs = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ld_tfrag(sk + c * 4096 + to[db][0], sk + c * 4096 + to[db][1]), bs, acc[db], 0, 0,
+            0);
+    }
+    j++;
   }
+  // no tile load may still be writing LDS when the work-group ends
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
   const int64_t p = r0 + wv * 32 + l32;
   const int64_t tok = token_of(sh, m, (int)(p & 511), H, W);
   uint16_t* row = dq + (hrow + tok) * 128;
 #pragma unroll
   for (int db = 0; db < 4; db++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int jj = 0; jj < 4; jj++) {
       uint2 u;
-      u.x = pk2(acc[db][4 * j] * scale, acc[db][4 * j + 1] * scale);
-      u.y = pk2(acc[db][4 * j + 2] * scale, acc[db][4 * j + 3] * scale);
-      *(uint2*)(row + 32 * db + 8 * j + 4 * hl) = u;
+      u.x = pk2(acc[db][4 * jj] * scale, acc[db][4 * jj + 1] * scale);
+      u.y = pk2(acc[db][4 * jj + 2] * scale, acc[db][4 * jj + 3] * scale);
+      *(uint2*)(row + 32 * db + 8 * jj + 4 * hl) = u;
     }
 }
 
@@ -571,7 +436,7 @@ bool launch_bwd_prep(const PlanDev& P, const BwdDev& Bd, const void* q, const vo
 
 bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& Bd, void* dk, void* dv, hipStream_t st) {
   if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
-  dim3 grid((unsigned)(P.heads * (P.N >> 7))), block(256);
+  dim3 grid((unsigned)(P.heads * (P.N / kKvRows))), block(kKvWaves * 64);
   hipLaunchKernelGGL(k_bwd_dkdv, grid, block, 0, st, (const uint16_t*)Bd.qp,
                      (const uint16_t*)Bd.dop, Bd.lse_p, Bd.delta, (const uint16_t*)P.kp,
                      (const uint16_t*)P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start,
@@ -582,7 +447,7 @@ bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& Bd, void* dk, void* dv, hip
 
 bool launch_bwd_dq(const PlanDev& P, const BwdDev& Bd, void* dq, hipStream_t st) {
   if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
-  dim3 grid((unsigned)(P.heads * (P.N >> 7))), block(256);
+  dim3 grid((unsigned)(P.heads * (P.N / kDqRows))), block(kDqWaves * 64);
   hipLaunchKernelGGL(k_bwd_dq, grid, block, 0, st, (const uint16_t*)Bd.qp,
                      (const uint16_t*)Bd.dop, Bd.lse_p, Bd.delta, (const uint16_t*)P.kp,
                      (const uint16_t*)P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start,

@@ -1,0 +1,175 @@
+// Device pieces shared by the sparse-attention kernels (forward, dK/dV, dQ):
+// the walk over selected key blocks, the LDS tile ring and its fragment reads.
+//
+// Tiles.  Permuted K, V (and, in the backward, Q, dO) rows are stored
+// [heads][N][128] bf16 with the 16-byte chunks of every row swizzled
+// (chunk c of row rho at c ^ chunk_swizzle(rho)), so one 64-row tile is a
+// contiguous 16 KB block that is copied verbatim into LDS.
+//
+// Ring.  A work-group keeps kRing tile slots in LDS with kRing - 1 tiles in
+// flight.  Every step issues exactly one tile (past the end of the lists it
+// re-reads the last real tile into a slot that is never computed on), so
+// the number of loads issued after tile j is fixed and a single
+// s_waitcnt vmcnt(n) says tile j has landed; a bare s_barrier then says
+// every wave has its share and is done with tile j - 1, whose slot is
+// refilled.  The tile loads go straight from HBM to LDS and their LDS
+// addresses are passed as opaque offsets: they carry no object identity, so
+// the compiler adds no conservative full drain of its own before LDS reads.
+#pragma once
+#include "prism_common.h"
+
+namespace prism {
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 64 * 128 * 2;  // bytes of one 64-row bf16 tile
+constexpr int kRing = 4;             // tile slots per ring
+
+// s_waitcnt immediates: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at
+// their maxima (no wait on them)
+__host__ __device__ constexpr int wait_vm(int n) {
+  return 0x0F70 | (n & 15) | ((n >> 4) << 14);
+}
+
+// LDS byte offset of a shared-memory object, opaque to alias analysis
+__device__ inline uint32_t lds_offset(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+// direct global -> LDS load: 64 lanes x 16 B (or x 4 B) to LDS offset `o`
+__device__ inline void dma16(const uint4* g, uint32_t o) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)(uintptr_t)o, 16, 0,
+                                   0);
+}
+__device__ inline void dma4(const float* g, uint32_t o) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)(uintptr_t)o, 4, 0,
+                                   0);
+}
+
+// Per-lane byte offsets inside a swizzled 64-row tile (row stride 256 B).
+// ro[kk]: the 16-byte chunk 2kk + hl of row l32 -- the MFMA operand whose
+// rows are the tile's rows (row l32 + 32 adds 8192).  to[db][0/1]: the two
+// 8-byte transposed reads that give the operand whose rows are the channels
+// 32db.., with k = 16 tile rows in the order {16c+4hl+0..3, 16c+8+4hl+0..3}
+// (rows 16c.. add 4096 c).  The swizzle depends on a row's low four bits
+// only, so these constants cover every read and the rest folds into
+// instruction offsets.
+__device__ inline void row_offsets(int lane, uint32_t (&ro)[8]) {
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int sw = chunk_swizzle(l32);
+#pragma unroll
+  for (int kk = 0; kk < 8; kk++) ro[kk] = l32 * 256 + (((2 * kk + hl) ^ sw) << 4);
+}
+__device__ inline void tr_offsets(int lane, uint32_t (&to)[4][2]) {
+  const int rA = 4 * (lane >> 5) + ((lane & 15) >> 2), rB = rA + 8;
+  const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int off = 8 * (lane & 1);
+#pragma unroll
+  for (int db = 0; db < 4; db++) {
+    to[db][0] = rA * 256 + (((4 * db + cl) ^ chunk_swizzle(rA)) << 4) + off;
+    to[db][1] = rB * 256 + (((4 * db + cl) ^ chunk_swizzle(rB)) << 4) + off;
+  }
+}
+__device__ inline bf16x8 ld_frag(const char* p) {
+  return __builtin_bit_cast(bf16x8, *(const uint4*)p);
+}
+__device__ inline bf16x8 ld_tfrag(const char* pa, const char* pb) {
+  s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
+  s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pb);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// two floats to packed bf16, one v_cvt_pk_bf16_f32 (round to nearest even)
+__device__ inline uint32_t pk2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// one row chunk (16 B) of a permuted, swizzled [rows][128] bf16 buffer
+__device__ inline bf16x8 row_chunk(const uint16_t* buf, int64_t row, int chunk) {
+  return __builtin_bit_cast(
+      bf16x8, *(const uint4*)(buf + row * 128 + ((chunk ^ chunk_swizzle((int)(row & 63))) << 3)));
+}
+
+// Merged walk over up to four ascending block lists (the lists of the
+// query blocks of one work unit, or of its key blocks in the key-major
+// transpose): yields each block once, with a bit mask of the lists that
+// hold it.
+struct UnionIter {
+  const int32_t* col;
+  int64_t a[4], e[4];
+  int head[4];
+  __device__ void init(const int32_t* c, int nl) {
+    col = c;
+#pragma unroll
+    for (int i = 0; i < 4; i++) head[i] = (i < nl && a[i] < e[i]) ? col[a[i]] : 0x7fffffff;
+  }
+  __device__ bool next(int& j, int& mask) {
+    int best = head[0];
+#pragma unroll
+    for (int i = 1; i < 4; i++) best = head[i] < best ? head[i] : best;
+    if (best == 0x7fffffff) return false;
+    mask = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      if (head[i] == best) {
+        mask |= 1 << i;
+        a[i]++;
+        head[i] = a[i] < e[i] ? col[a[i]] : 0x7fffffff;
+      }
+    j = best;
+    return true;
+  }
+};
+
+// The 64-row tiles of the blocks of a merged walk, in order.
+struct TileIter {
+  UnionIter U;
+  const int32_t* blk_start;
+  const uint8_t* blk_shape;
+  int64_t hoff;
+  int64_t row;  // first permuted row of the current tile
+  int t, nt, mask;
+  bool valid;
+  // lists ptr[g0 + i] .. ptr[g0 + i + 1] for i < nl
+  __device__ void init(const int64_t* ptr, const int32_t* col, int64_t g0, int nl,
+                       const int32_t* bs, const uint8_t* bsh, int64_t off) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t g = g0 + (i < nl ? i : 0);
+      U.a[i] = ptr[g];
+      U.e[i] = ptr[g + 1];
+    }
+    U.init(col, nl);
+    blk_start = bs;
+    blk_shape = bsh;
+    hoff = off;
+    valid = true;
+    t = 0;
+    nt = 0;
+    advance();
+  }
+  __device__ void advance() {
+    if (valid && t + 1 < nt) {
+      t++;
+      row += 64;
+      return;
+    }
+    int j;
+    valid = U.next(j, mask);
+    if (valid) {
+      row = blk_start[hoff + j];
+      nt = d_shapes[block_shape_at(blk_shape, hoff + j)].volume >> 6;
+      t = 0;
+    }
+  }
+};
+
+}  // namespace prism
