@@ -129,24 +129,24 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
   TileIter it;
   it.init(colt_ptr, colt_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_start,
           blk_shape, hoff);
-  const uint4* qbase = (const uint4*)(qp + hrow * 128);
-  const uint4* dbase = (const uint4*)(dop + hrow * 128);
+  const __amdgpu_buffer_rsrc_t rsQ = buffer_of(qp + hrow * 128, (uint32_t)(N * 256));
+  const __amdgpu_buffer_rsrc_t rsD = buffer_of(dop + hrow * 128, (uint32_t)(N * 256));
   // waves 0 and 2 bring the LSE column, waves 1 and 3 Delta (both pairs write
   // the same values), so that every wave issues the same nine loads per tile
-  const float* colsrc = (wvu & 1) ? delta + hrow : lse2 + hrow;
+  const __amdgpu_buffer_rsrc_t rsC =
+      buffer_of((wvu & 1) ? delta + hrow : lse2 + hrow, (uint32_t)(N * 4));
   const uint32_t lring = lds_offset(ring);
   const uint32_t lcol = lds_offset(ringc) + (wvu & 1) * 256;
   auto stage = [&](int b, int64_t row) {
-    const uint4* qs = qbase + row * 16;
-    const uint4* ds = dbase + row * 16;
     const uint32_t o = lring + b * 2 * kTile;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const uint32_t piece = i * 256 + wvu * 64;
-      dma16(qs + piece + lane, o + piece * 16);
-      dma16(ds + piece + lane, o + kTile + piece * 16);
+      const uint32_t src = (uint32_t)row * 256 + (piece + lane) * 16;
+      dma16(rsQ, src, o + piece * 16);
+      dma16(rsD, src, o + kTile + piece * 16);
     }
-    dma4(colsrc + row + lane, lcol + b * 512);
+    dma4(rsC, ((uint32_t)row + lane) * 4, lcol + b * 512);
   };
 
   uint32_t ring_f = 0;  // list masks of the tiles in the ring, a byte per slot
@@ -195,12 +195,17 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
         s[r] = 0.0f;
         dp[r] = 0.0f;
       }
+      // all sixteen fragments first, so that their reads overlap
+      bf16x8 fa[8], fb[8];
 #pragma unroll
       for (int kk = 0; kk < 8; kk++) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sq + qb * 8192 + ro[kk]), kr[kk], s,
-                                                    0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sd + qb * 8192 + ro[kk]), vr[kk],
-                                                     dp, 0, 0, 0);
+        fa[kk] = ld_frag(sq + qb * 8192 + ro[kk]);
+        fb[kk] = ld_frag(sd + qb * 8192 + ro[kk]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 8; kk++) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk], kr[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk], vr[kk], dp, 0, 0, 0);
       }
       // rows of s/dp held by this lane: q = 32qb + 8jj + 4hl + i (r = 4jj + i)
       uint32_t pp[8], ps[8];
@@ -226,12 +231,16 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
         const bf16x8 bs = __builtin_bit_cast(
             bf16x8, make_uint4(ps[4 * c], ps[4 * c + 1], ps[4 * c + 2], ps[4 * c + 3]));
         const int cc = (2 * qb + c) * 4096;  // rows 16 (2qb + c) ..
+        bf16x8 ta[4], tb[4];
 #pragma unroll
         for (int db = 0; db < 4; db++) {
-          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              ld_tfrag(sd + cc + to[db][0], sd + cc + to[db][1]), bp, dvt[db], 0, 0, 0);
-          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              ld_tfrag(sq + cc + to[db][0], sq + cc + to[db][1]), bs, dkt[db], 0, 0, 0);
+          ta[db] = ld_tfrag(sd + cc + to[db][0], sd + cc + to[db][1]);
+          tb[db] = ld_tfrag(sq + cc + to[db][0], sq + cc + to[db][1]);
+        }
+#pragma unroll
+        for (int db = 0; db < 4; db++) {
+          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[db], bp, dvt[db], 0, 0, 0);
+          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[db], bs, dkt[db], 0, 0, 0);
         }
       }
     }
@@ -319,17 +328,16 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[db][r] = 0.0f;
 
-  const uint4* kbase = (const uint4*)(kp + hrow * 128);
-  const uint4* vbase = (const uint4*)(vp + hrow * 128);
+  const __amdgpu_buffer_rsrc_t rsK = buffer_of(kp + hrow * 128, (uint32_t)(N * 256));
+  const __amdgpu_buffer_rsrc_t rsV = buffer_of(vp + hrow * 128, (uint32_t)(N * 256));
   const uint32_t lK = lds_offset(ringK), lV = lds_offset(ringV);
   auto stage = [&](int b, int64_t row) {
-    const uint4* ks = kbase + row * 16;
-    const uint4* vs = vbase + row * 16;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const uint32_t piece = i * 512 + wvu * 64;
-      dma16(ks + piece + lane, lK + b * kTile + piece * 16);
-      dma16(vs + piece + lane, lV + b * kTile + piece * 16);
+      const uint32_t src = (uint32_t)row * 256 + (piece + lane) * 16;
+      dma16(rsK, src, lK + b * kTile + piece * 16);
+      dma16(rsV, src, lV + b * kTile + piece * 16);
     }
   };
   uint32_t ring_mask = 0;  // list masks of the tiles in the ring, a byte per slot

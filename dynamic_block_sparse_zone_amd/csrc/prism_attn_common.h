@@ -37,16 +37,22 @@ __device__ inline uint32_t lds_offset(const void* p) {
   return __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
 }
-// direct global -> LDS load: 64 lanes x 16 B (or x 4 B) to LDS offset `o`
-__device__ inline void dma16(const uint4* g, uint32_t o) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)(uintptr_t)o, 16, 0,
-                                   0);
+// Direct HBM -> LDS loads in the buffer (MUBUF) form: 64 lanes x 16 B (or
+// x 4 B) from byte offset `voff` (per lane) of buffer `rs` to LDS offset `o`.
+// The buffer form is used rather than the global one because the compiler
+// counts a global (FLAT) load to LDS as a possible LDS access too, and then
+// turns every LDS-read wait into a full drain.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  // raw buffer, no stride, range-checked against `bytes`
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
-__device__ inline void dma4(const float* g, uint32_t o) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)(uintptr_t)o, 4, 0,
-                                   0);
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t o) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)(uintptr_t)o, 16, voff, 0, 0, 0);
+}
+__device__ inline void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t o) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)(uintptr_t)o, 4, voff, 0, 0, 0);
 }
 
 // Per-lane byte offsets inside a swizzled 64-row tile (row stride 256 B).

@@ -77,19 +77,19 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
     for (int r = 0; r < 16; r++) acc[db][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const uint4* kbase = (const uint4*)(kp + (int64_t)h * N * 128);
-  const uint4* vbase = (const uint4*)(vp + (int64_t)h * N * 128);
+  // this head's K and V (N rows of 256 B) as buffers
+  const __amdgpu_buffer_rsrc_t rsK = buffer_of(kp + (int64_t)h * N * 128, (uint32_t)(N * 256));
+  const __amdgpu_buffer_rsrc_t rsV = buffer_of(vp + (int64_t)h * N * 128, (uint32_t)(N * 256));
   const uint32_t lK = lds_offset(ringK), lV = lds_offset(ringV);
   // one K tile and one V tile (already in LDS layout) into slot b: wave w
   // moves the 1 KB pieces w, w + 8 of each
   auto stage = [&](int b, int64_t row) {
-    const uint4* ks = kbase + row * 16;
-    const uint4* vs = vbase + row * 16;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const uint32_t piece = i * 512 + wvu * 64;
-      dma16(ks + piece + lane, lK + b * kTile + piece * 16);
-      dma16(vs + piece + lane, lV + b * kTile + piece * 16);
+      const uint32_t src = (uint32_t)row * 256 + (piece + lane) * 16;
+      dma16(rsK, src, lK + b * kTile + piece * 16);
+      dma16(rsV, src, lV + b * kTile + piece * 16);
     }
   };
   uint32_t ring_mask = 0;  // list masks of the tiles in the ring, a byte per slot
