@@ -178,7 +178,9 @@ prism_status prism_config_check(const prism_config* c) {
   if (c->T <= 0 || c->H <= 0 || c->W <= 0 || c->T % 8 || c->H % 8 || c->W % 8)
     return PRISM_EINVAL;
   if (c->heads <= 0) return PRISM_EINVAL;
-  if ((int64_t)c->T * c->H * c->W > (int64_t)0x7fffffff) return PRISM_EUNSUPPORTED;
+  // one head's rows of 128 bf16 channels are addressed with 32-bit byte
+  // offsets by the attention kernels: T*H*W < 2^24
+  if ((int64_t)c->T * c->H * c->W >= ((int64_t)1 << 24)) return PRISM_EUNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PRISM_EUNSUPPORTED;
   if (c->dtype != PRISM_F32 && c->dtype != PRISM_BF16) return PRISM_EINVAL;
   if (c->top_k < 0) return PRISM_EINVAL;

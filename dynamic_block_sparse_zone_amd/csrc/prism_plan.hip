@@ -1031,15 +1031,15 @@ __global__ __launch_bounds__(256) void k_colt_count(const int64_t* __restrict__ 
   }
 }
 
-// per column: turn the chunk counts into absolute output positions
-__global__ void k_colt_offsets(const int64_t* __restrict__ colt_ptr, int n, int64_t g0,
-                               int nch, int32_t* __restrict__ chunk_cnt) {
+// per column: turn the chunk counts into output positions relative to the
+// column's start (at most n, so they fit in 32 bits at any nnz)
+__global__ void k_colt_offsets(int n, int nch, int32_t* __restrict__ chunk_cnt) {
   int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
-  int64_t run = colt_ptr[g0 + j];
+  int32_t run = 0;
   for (int c = 0; c < nch; c++) {
     int32_t t = chunk_cnt[(int64_t)c * n + j];
-    chunk_cnt[(int64_t)c * n + j] = (int32_t)(run);
+    chunk_cnt[(int64_t)c * n + j] = run;
     run += t;
   }
 }
@@ -1047,7 +1047,8 @@ __global__ void k_colt_offsets(const int64_t* __restrict__ colt_ptr, int n, int6
 // per chunk: rows in ascending order, each row's entries in parallel
 __global__ __launch_bounds__(256) void k_colt_fill(const int64_t* __restrict__ row_ptr,
                                                    const int32_t* __restrict__ col_idx, int n,
-                                                   int64_t g0, int32_t* __restrict__ chunk_cnt,
+                                                   int64_t g0, const int64_t* __restrict__ colt_ptr,
+                                                   int32_t* __restrict__ chunk_cnt,
                                                    int32_t* __restrict__ colt_idx) {
   const int c = blockIdx.x;
   const int i0 = c * 64, i1 = min(n, i0 + 64);
@@ -1055,7 +1056,7 @@ __global__ __launch_bounds__(256) void k_colt_fill(const int64_t* __restrict__ r
     int64_t a = row_ptr[g0 + i], b = row_ptr[g0 + i + 1];
     for (int64_t e = a + threadIdx.x; e < b; e += blockDim.x) {
       int j = col_idx[e];
-      int pos = atomicAdd(&chunk_cnt[(int64_t)c * n + j], 1);
+      const int64_t pos = colt_ptr[g0 + j] + atomicAdd(&chunk_cnt[(int64_t)c * n + j], 1);
       colt_idx[pos] = i;
     }
     __syncthreads();
@@ -1202,10 +1203,10 @@ bool launch_transpose(const PlanDev& P, int64_t g0, int n, int last, hipStream_t
                      P.chunk_cnt, P.colt_cnt + g0);
   hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, st, P.colt_cnt, n, g0, P.colt_ptr,
                      P.counters + 1, last);
-  hipLaunchKernelGGL(k_colt_offsets, dim3((n + 255) / 256), dim3(256), 0, st, P.colt_ptr, n,
-                     g0, nch, P.chunk_cnt);
+  hipLaunchKernelGGL(k_colt_offsets, dim3((n + 255) / 256), dim3(256), 0, st, n, nch,
+                     P.chunk_cnt);
   hipLaunchKernelGGL(k_colt_fill, dim3(nch), dim3(256), 0, st, P.row_ptr, P.col_idx, n, g0,
-                     P.chunk_cnt, P.colt_idx);
+                     P.colt_ptr, P.chunk_cnt, P.colt_idx);
   return hipGetLastError() == hipSuccess;
 }
 

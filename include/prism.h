@@ -83,7 +83,10 @@ typedef struct prism_plan_s prism_plan_t;
  * top_k=16, top_p=0.9, all volumes, dynamic shapes, need_backward=1). */
 void prism_config_default(prism_config* cfg);
 
-/* Host-only validation of a configuration; no device work. */
+/* Host-only validation of a configuration; no device work.  PRISM_EINVAL for
+ * a malformed configuration; PRISM_EUNSUPPORTED for T*H*W >= 2^24 tokens per
+ * head (the kernels address one head's rows with 32-bit byte offsets) or a
+ * head_dim other than 64 and 128. */
 prism_status prism_config_check(const prism_config* cfg);
 
 /* Bytes of device workspace prism_plan needs for `cfg` when up to

@@ -55,6 +55,8 @@ def _cfg(nat, **kw):
     ({"volume_mask": 0}, 1), ({"volume_mask": 9}, 1), ({"fixed_shape": (4, 4, 4)}, 0),
     ({"fixed_shape": (4, 4, 3)}, 1), ({"fixed_shape": (8, 8, 8)}, 1), ({"eps": 0.0}, 1),
     ({"tau128": 0.2, "tau256": 0.3}, 1), ({"top_k_frac": -1.0}, 1), ({"top_p": 1.5}, 0),
+    # one head's rows are addressed with 32-bit byte offsets: fewer than 2^24 tokens
+    ({"T": 256, "H": 256, "W": 256}, 2), ({"T": 248, "H": 256, "W": 256}, 0),
 ])
 def test_config_validation(nat, kw, status):
     c = _cfg(nat, **kw)
