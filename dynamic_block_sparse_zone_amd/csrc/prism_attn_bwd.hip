@@ -187,15 +187,18 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
     const char* sd = sq + kTile;                            // dO tile
     const float* sl = ringc + (j & (kRing - 1)) * 128;      // log2(e) LSE
     const float* sdl = sl + 64;                             // Delta
-#pragma unroll
-    for (int qb = 0; qb < 2; qb++) {
-      f32x16 s, dp;
+    // Two 32-query halves per tile, software-pipelined: the S and dP products
+    // of the second half are issued between the softmax of the first half
+    // and its dV/dK products, so one wave has independent MFMA and VALU work
+    // at hand.
+    f32x16 s[2], dp[2];
+    auto sdp = [&](int qb) {  // S = Q K^T, dP = dO V^T of half qb
+      // all sixteen fragments first, so that their reads overlap
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        s[r] = 0.0f;
-        dp[r] = 0.0f;
+        s[qb][r] = 0.0f;
+        dp[qb][r] = 0.0f;
       }
-      // all sixteen fragments first, so that their reads overlap
       bf16x8 fa[8], fb[8];
 #pragma unroll
       for (int kk = 0; kk < 8; kk++) {
@@ -204,9 +207,12 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
       }
 #pragma unroll
       for (int kk = 0; kk < 8; kk++) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk], kr[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk], vr[kk], dp, 0, 0, 0);
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk], kr[kk], s[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk], vr[kk], dp[qb], 0, 0, 0);
       }
+    };
+    // dS = P (dP - Delta); dV^T += dO^T P, dK^T += Q^T dS for half qb
+    auto rest = [&](int qb, bool next) {
       // rows of s/dp held by this lane: q = 32qb + 8jj + 4hl + i (r = 4jj + i)
       uint32_t pp[8], ps[8];
 #pragma unroll
@@ -216,21 +222,22 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
         float pv[4], sv[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * jj + i], c_log2, -Lv[i]));
-          sv[i] = pv[i] * (dp[4 * jj + i] - Dv[i]);
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][4 * jj + i], c_log2, -Lv[i]));
+          sv[i] = pv[i] * (dp[qb][4 * jj + i] - Dv[i]);
         }
         pp[2 * jj] = pk2(pv[0], pv[1]);
         pp[2 * jj + 1] = pk2(pv[2], pv[3]);
         ps[2 * jj] = pk2(sv[0], sv[1]);
         ps[2 * jj + 1] = pk2(sv[2], sv[3]);
       }
+      if (next) sdp(1);
 #pragma unroll
       for (int c = 0; c < 2; c++) {
         const bf16x8 bp = __builtin_bit_cast(
             bf16x8, make_uint4(pp[4 * c], pp[4 * c + 1], pp[4 * c + 2], pp[4 * c + 3]));
         const bf16x8 bs = __builtin_bit_cast(
             bf16x8, make_uint4(ps[4 * c], ps[4 * c + 1], ps[4 * c + 2], ps[4 * c + 3]));
-        const int cc = (2 * qb + c) * 4096;  // rows 16 (2qb + c) ..
+        const int cc = (2 * qb + c) * 4096;
         bf16x8 ta[4], tb[4];
 #pragma unroll
         for (int db = 0; db < 4; db++) {
@@ -243,7 +250,10 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
           dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[db], bs, dkt[db], 0, 0, 0);
         }
       }
-    }
+    };
+    sdp(0);
+    rest(0, true);
+    rest(1, false);
     // pin the accumulators to the accumulation registers across the loop
     // (otherwise they are parked in ordinary registers and copied both ways
     // on every tile)

@@ -22,6 +22,9 @@ namespace prism {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// (1, 1) in bf16: a v_dot2 against it sums a packed pair
+static constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int kTile = 64 * 128 * 2;  // bytes of one 64-row bf16 tile
 constexpr int kRing = 4;             // tile slots per ring
