@@ -6,7 +6,7 @@
 // Every quantity that decides a shape or a selected block is computed in fp32
 // in one fixed order (compiled with -ffp-contract=off; fused multiply-add
 // only where written as fmaf), so the plan is reproducible bit for bit.
-#include "prism_common.h"
+#include "prism_attn_common.h"
 #include "prism_kernels.h"
 
 namespace prism {
@@ -620,157 +620,166 @@ __device__ inline T block_sum(T v, T* sh) {
 }
 
 constexpr int kSelThreads = 256;
-constexpr int kSortCap = 2048;
+// longest score row (key blocks of a head) the selection kernels stage in LDS
+constexpr int kSelLdsMax = 16384;
 
-struct SelShared {
-  uint32_t cnt[4][256];
-  unsigned long long wt[4][256];
-  unsigned long long list[kSortCap];  // (key << 32) | ~index
-  uint32_t lcount;
-  unsigned long long red64[8];
-  uint32_t red32[8];
-  float redf[8];
-  int bsel[4];
-  unsigned long long above_w[2];
-  uint32_t above_c[2];
-};
-
-// Sort the collected (key, index) pairs descending by key, ascending by index.
-__device__ void sort_desc(unsigned long long* a, int n) {
-  int P = 1;
-  while (P < n) P <<= 1;
-  for (int i = n + threadIdx.x; i < P; i += blockDim.x) a[i] = 0ull;  // sorts last
+// One score row (n <= kSelLdsMax floats) into LDS: every wave issues its
+// 256-byte pieces as direct HBM->LDS loads, all in flight at once, then one
+// wait and a barrier.  Lanes past n read zeros (range-checked buffer) into
+// the unused tail of `dst`.
+__device__ inline void stage_row(const float* row, int n, float* dst) {
+  const __amdgpu_buffer_rsrc_t rs = buffer_of(row, (uint32_t)n * 4u);
+  const uint32_t o = lds_offset(dst);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  for (int j0 = wv * 64; j0 < n; j0 += kSelThreads)
+    dma4(rs, (uint32_t)(j0 + lane) * 4u, o + (uint32_t)j0 * 4u);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
   __syncthreads();
-  for (int k = 2; k <= P; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          unsigned long long x = a[i], y = a[ixj];
-          bool desc = (i & k) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            a[i] = y;
-            a[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
 }
 
-// inclusive scan over the block (256 threads) of one u64 per thread
+// Shared state of the row selection: per-wave digit histograms (count and
+// integer weight) of one radix level, and the scan scratch.
+struct SelShared {
+  uint32_t cnt[kSelThreads / 64][256];
+  unsigned long long wt[kSelThreads / 64][256];
+  unsigned long long red64[kSelThreads / 64];
+  unsigned long long wstar;
+  float redf[kSelThreads / 64];
+  int pick;
+};
+
+// inclusive scan over the block (kSelThreads threads) of one u64 per thread
 __device__ inline unsigned long long block_incl_scan(unsigned long long v,
-                                                     unsigned long long* sh,
-                                                     unsigned long long* total) {
+                                                     unsigned long long* sh) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     unsigned long long u = __shfl_up(v, off, 64);
     if (lane >= off) v += u;
   }
-  __syncthreads();
   if (lane == 63) sh[wv] = v;
   __syncthreads();
-  unsigned long long before = 0, tot = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); w++) {
-    if (w < wv) before += sh[w];
-    tot += sh[w];
-  }
-  *total = tot;
+  unsigned long long before = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; w++) before += w < wv ? sh[w] : 0ull;
+  __syncthreads();
   return before + v;
 }
 
-// smallest position of the sorted list whose prefix weight reaches `need`
-__device__ int first_crossing(const unsigned long long* list, int tot, unsigned long long need,
-                              float smax, SelShared& S) {
-  unsigned long long carry = 0;
-  if (threadIdx.x == 0) S.bsel[3] = tot - 1;
+// One level of a radix select over the 32-bit order keys of a row, from the
+// most significant byte down.  Among the keys whose bytes above `shift`
+// equal `prefix`, builds the histogram of the byte at `shift` (counts, and
+// integer weights when `by_weight`), then walks the digits from the largest
+// down and returns the digit at which the running total (weight, else
+// count) first reaches `need`; *above_c / *above_w get the count and weight
+// of the keys of that prefix with a larger digit.  Keys are ordered like
+// the scores they encode, so "larger digit" is "earlier in the selection
+// order".
+__device__ int radix_level(const float* row, int n, float smax, uint32_t prefix, int shift,
+                           bool by_weight, unsigned long long need, SelShared& S,
+                           uint32_t* above_c, unsigned long long* above_w,
+                           unsigned long long p32 = 0) {
+  const int wv = threadIdx.x >> 6;
+  for (int b = threadIdx.x; b < (kSelThreads / 64) * 256; b += blockDim.x) {
+    (&S.cnt[0][0])[b] = 0;
+    (&S.wt[0][0])[b] = 0ull;
+  }
   __syncthreads();
-  for (int c0 = 0; c0 < tot; c0 += blockDim.x) {
-    int i = c0 + threadIdx.x;
-    unsigned long long w = i < tot ? weight_of(key2f((uint32_t)(list[i] >> 32)), smax) : 0ull;
-    unsigned long long chunk_total;
-    unsigned long long incl = block_incl_scan(w, S.red64, &chunk_total);
-    if (i < tot && carry + incl >= need) atomicMin(&S.bsel[3], i);
+  const uint32_t hmask = shift >= 24 ? 0u : (0xffffffffu << (shift + 8));
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    const float s = row[j];
+    const uint32_t key = f2key(s);
+    if ((key & hmask) == prefix) {
+      const int d = (key >> shift) & 0xff;
+      atomicAdd(&S.cnt[wv][d], 1u);
+      if (by_weight) atomicAdd(&S.wt[wv][d], (unsigned long long)weight_of(s, smax));
+    }
+  }
+  __syncthreads();
+  // thread t owns digit 255 - t: an inclusive scan in selection order
+  const int d = 255 - (int)threadIdx.x;
+  uint32_t c = 0;
+  unsigned long long w = 0;
+  if (threadIdx.x < 256) {
+#pragma unroll
+    for (int q = 0; q < kSelThreads / 64; q++) {
+      c += S.cnt[q][d];
+      w += S.wt[q][d];
+    }
+  }
+  const unsigned long long mine = by_weight ? w : (unsigned long long)c;
+  if (threadIdx.x == 0) S.pick = 255;
+  const unsigned long long incl = block_incl_scan(mine, S.red64);
+  if (p32) {
+    // first level of the Top-p select: the histogram total is the row's
+    // weight Z, and the target W* = ceil(p32 Z / 2^32) (no overflow: p32 <= 2^32)
+    if (threadIdx.x == kSelThreads - 1) S.red64[0] = incl;
     __syncthreads();
-    if (S.bsel[3] < c0 + (int)blockDim.x && S.bsel[3] < tot - 1) break;
-    carry += chunk_total;
+    const unsigned long long Z = S.red64[0];
+    const unsigned long long zh = Z >> 32, zl = Z & 0xffffffffull;
+    need = p32 * zh + ((p32 * zl + 0xffffffffull) >> 32);
+    if (threadIdx.x == 0) S.wstar = need;
     __syncthreads();
   }
-  int r = S.bsel[3];
+  if (threadIdx.x < 256 && incl >= need && incl - mine < need) S.pick = threadIdx.x;
   __syncthreads();
-  return r;
+  const int t = S.pick;
+  // count and weight above the chosen digit: a second scan of the counts
+  const unsigned long long incl_c = block_incl_scan(c, S.red64);
+  const unsigned long long incl_w = by_weight ? block_incl_scan(w, S.red64) : 0ull;
+  if ((int)threadIdx.x == t) {
+    S.red64[0] = incl_c - c;
+    S.red64[1] = incl_w - w;
+  }
+  __syncthreads();
+  *above_c = (uint32_t)S.red64[0];
+  *above_w = S.red64[1];
+  __syncthreads();
+  return 255 - t;
 }
 
-// Exact position search inside one bucket: returns in *out_key the key of the
-// element at 0-based order position `pos` among the elements of bucket b
-// (order: key desc, index asc) and in *out_ties the number of elements at
-// positions <= pos holding that same key.  Uses the shared list when the
-// bucket fits, else a bitwise search over keys.
-__device__ void bucket_position(const float* __restrict__ row, int n, float smax, int b,
-                                int64_t pos, SelShared& S, uint32_t* out_key,
-                                int64_t* out_ties) {
-  if (threadIdx.x == 0) S.lcount = 0;
-  __syncthreads();
-  // count first
-  uint32_t c = 0;
-  for (int j = threadIdx.x; j < n; j += blockDim.x)
-    if (bucket_of(row[j], smax) == b) c++;
-  uint32_t tot = block_sum<uint32_t>(c, S.red32);
-  if (tot <= (uint32_t)kSortCap) {
-    for (int j = threadIdx.x; j < n; j += blockDim.x) {
-      float s = row[j];
-      if (bucket_of(s, smax) == b) {
-        uint32_t slot = atomicAdd(&S.lcount, 1u);
-        S.list[slot] = ((unsigned long long)f2key(s) << 32) | (uint32_t)(~(uint32_t)j);
-      }
-    }
-    __syncthreads();
-    sort_desc(S.list, (int)tot);
-    uint32_t key = (uint32_t)(S.list[pos] >> 32);
-    // ties of that key at positions <= pos
-    uint32_t t = 0;
-    for (int i = threadIdx.x; i <= pos; i += blockDim.x)
-      if ((uint32_t)(S.list[i] >> 32) == key) t++;
-    uint32_t ties = block_sum<uint32_t>(t, S.red32);
-    *out_key = key;
-    *out_ties = ties;
-  } else {
-    // bitwise search for the largest key K with count(bucket b, key >= K) > pos
-    uint32_t K = 0;
-    for (int bit = 31; bit >= 0; bit--) {
-      uint32_t cand = K | (1u << bit);
-      uint32_t cc = 0;
-      for (int j = threadIdx.x; j < n; j += blockDim.x) {
-        float s = row[j];
-        if (bucket_of(s, smax) == b && f2key(s) >= cand) cc++;
-      }
-      uint32_t tc = block_sum<uint32_t>(cc, S.red32);
-      if ((int64_t)tc > pos) K = cand;
-    }
-    uint32_t gt = 0;
-    for (int j = threadIdx.x; j < n; j += blockDim.x) {
-      float s = row[j];
-      if (bucket_of(s, smax) == b && f2key(s) > K) gt++;
-    }
-    uint32_t tg = block_sum<uint32_t>(gt, S.red32);
-    *out_key = K;
-    *out_ties = pos - (int64_t)tg + 1;
+// Full radix select: the key K of the element at which the running total in
+// selection order first reaches `need`, with the count and weight of the
+// elements whose key is larger.
+// With p32 != 0 the target is the Top-p weight W* of the row, formed from
+// the first level's total; it is returned in *need_out.
+__device__ uint32_t radix_select(const float* row, int n, float smax, bool by_weight,
+                                 unsigned long long need, SelShared& S, uint32_t* above_c,
+                                 unsigned long long* above_w, unsigned long long p32 = 0,
+                                 unsigned long long* need_out = nullptr) {
+  uint32_t prefix = 0, ac = 0;
+  unsigned long long aw = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    uint32_t c;
+    unsigned long long w;
+    const unsigned long long rest = need - (by_weight ? aw : (unsigned long long)ac);
+    const int d = radix_level(row, n, smax, prefix, shift, by_weight, rest, S, &c, &w,
+                              shift == 24 ? p32 : 0ull);
+    if (shift == 24 && p32) need = S.wstar;
+    prefix |= (uint32_t)d << shift;
+    ac += c;
+    aw += w;
   }
-  __syncthreads();
+  if (need_out) *need_out = need;
+  *above_c = ac;
+  *above_w = aw;
+  return prefix;
 }
 
 // Per query block row: count of selected key blocks, the threshold key and
 // the number of threshold-key ties to take.  S_i = first max(k, L*) keys in
 // the order (score desc, index asc), L* = shortest prefix whose integer
-// softmax weights reach ceil(p 2^32) Z / 2^32 (Z = row total).
+// softmax weights reach ceil(p 2^32) Z / 2^32 (Z = row total).  Both
+// positions are found exactly by radix selects over the order keys (equal
+// keys carry equal weights, so a prefix of the order is "every key above K
+// and the first t copies of K").
+template <bool kLds>
 __global__ __launch_bounds__(kSelThreads) void k_select_count(
     const float* __restrict__ scores, int n, int64_t g0, int k_count, float k_frac, float p,
     int32_t* __restrict__ row_cnt, uint32_t* __restrict__ row_key,
     int32_t* __restrict__ row_tie) {
   __shared__ SelShared S;
   const int i = blockIdx.x;
-  const float* row = scores + (int64_t)i * n;
   const int64_t g = g0 + i;
   int64_t kk = k_count;
   if (k_frac > 0.0f) kk = (int64_t)ceil((double)k_frac * (double)n);
@@ -784,6 +793,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select_count(
     }
     return;
   }
+  // the row is read from HBM once: into LDS (n floats of dynamic shared
+  // memory) when it fits, and every later pass runs over that copy
+  const float* grow = scores + (int64_t)i * n;
+  extern __shared__ __attribute__((aligned(16))) float srow_dyn[];
+  if (kLds) stage_row(grow, n, srow_dyn);
+  const float* row = kLds ? (const float*)srow_dyn : grow;
   float mx = -INFINITY;
   for (int j = threadIdx.x; j < n; j += blockDim.x) mx = fmaxf(mx, row[j]);
 #pragma unroll
@@ -794,129 +809,29 @@ __global__ __launch_bounds__(kSelThreads) void k_select_count(
   for (int w = 1; w < kSelThreads / 64; w++) smax = fmaxf(smax, S.redf[w]);
   __syncthreads();
 
-  // bucket histograms (count, weight) in order of descending score
-  const int wv = threadIdx.x >> 6;
-  for (int b = threadIdx.x; b < 4 * 256; b += blockDim.x) {
-    (&S.cnt[0][0])[b] = 0;
-    (&S.wt[0][0])[b] = 0ull;
-  }
-  __syncthreads();
-  const bool need_w = p > 0.0f;
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
-    float s = row[j];
-    int b = bucket_of(s, smax);
-    atomicAdd(&S.cnt[wv][b], 1u);
-    if (need_w) atomicAdd(&S.wt[wv][b], (unsigned long long)weight_of(s, smax));
-  }
-  __syncthreads();
-  if (threadIdx.x < 256) {
-    int b = threadIdx.x;
-    S.cnt[0][b] = S.cnt[0][b] + S.cnt[1][b] + S.cnt[2][b] + S.cnt[3][b];
-    S.wt[0][b] = S.wt[0][b] + S.wt[1][b] + S.wt[2][b] + S.wt[3][b];
-  }
-  __syncthreads();
-
   int64_t L = 0;
-  uint32_t keyL = 0;
-  int64_t tieL = 0;
-  if (need_w) {
-    if (threadIdx.x == 0) {
-      unsigned long long Zt = 0;
-      for (int b = 0; b < 256; b++) Zt += S.wt[0][b];
-      unsigned long long P32 = (unsigned long long)ceil((double)p * 4294967296.0);
-      // Wstar = ceil(P32 * Z / 2^32) without overflow: P32 <= 2^32
-      unsigned long long zh = Zt >> 32, zl = Zt & 0xffffffffull;
-      unsigned long long Wstar = P32 * zh + ((P32 * zl + 0xffffffffull) >> 32);
-      unsigned long long wa = 0;
-      uint32_t ca = 0;
-      int bs = 255;
-      for (int b = 0; b < 256; b++) {
-        if (wa + S.wt[0][b] >= Wstar) {
-          bs = b;
-          break;
-        }
-        wa += S.wt[0][b];
-        ca += S.cnt[0][b];
-      }
-      S.bsel[0] = bs;
-      S.above_w[0] = Wstar - wa;  // weight still needed inside bucket bs
-      S.above_c[0] = ca;
-    }
-    __syncthreads();
-    const int bs = S.bsel[0];
-    const unsigned long long need = S.above_w[0];
-    const uint32_t ca = S.above_c[0];
-    // exact crossing inside bucket bs: collect, sort, prefix weights
-    if (threadIdx.x == 0) S.lcount = 0;
-    __syncthreads();
-    uint32_t c = 0;
-    for (int j = threadIdx.x; j < n; j += blockDim.x)
-      if (bucket_of(row[j], smax) == bs) c++;
-    uint32_t tot = block_sum<uint32_t>(c, S.red32);
-    if (tot <= (uint32_t)kSortCap) {
-      for (int j = threadIdx.x; j < n; j += blockDim.x) {
-        float s = row[j];
-        if (bucket_of(s, smax) == bs) {
-          uint32_t slot = atomicAdd(&S.lcount, 1u);
-          S.list[slot] = ((unsigned long long)f2key(s) << 32) | (uint32_t)(~(uint32_t)j);
-        }
-      }
-      __syncthreads();
-      sort_desc(S.list, (int)tot);
-      L = (int64_t)ca + first_crossing(S.list, (int)tot, need, smax, S) + 1;
-    } else {
-      // bucket too large for the list: bitwise search for the crossing key
-      uint32_t K = 0;
-      for (int bit = 31; bit >= 0; bit--) {
-        uint32_t cand = K | (1u << bit);
-        unsigned long long wsum = 0;
-        for (int j = threadIdx.x; j < n; j += blockDim.x) {
-          float s = row[j];
-          if (bucket_of(s, smax) == bs && f2key(s) >= cand) wsum += weight_of(s, smax);
-        }
-        unsigned long long tw = block_sum<unsigned long long>(wsum, S.red64);
-        if (tw >= need) K = cand;
-      }
-      unsigned long long wg = 0;
-      uint32_t cg = 0;
-      for (int j = threadIdx.x; j < n; j += blockDim.x) {
-        float s = row[j];
-        if (bucket_of(s, smax) == bs && f2key(s) > K) {
-          wg += weight_of(s, smax);
-          cg++;
-        }
-      }
-      unsigned long long twg = block_sum<unsigned long long>(wg, S.red64);
-      uint32_t tcg = block_sum<uint32_t>(cg, S.red32);
-      unsigned long long wk = weight_of(key2f(K), smax);
-      unsigned long long rest = need - twg;
-      L = (int64_t)ca + tcg + (int64_t)((rest + wk - 1) / wk);
-    }
+  uint32_t keyP = 0, caP = 0;
+  if (p > 0.0f) {
+    // W* = ceil(ceil(p 2^32) Z / 2^32) with Z the row's total weight
+    const unsigned long long P32 = (unsigned long long)ceil((double)p * 4294967296.0);
+    unsigned long long wa, Wstar;
+    keyP = radix_select(row, n, smax, true, 0ull, S, &caP, &wa, P32, &Wstar);
+    const unsigned long long wk = weight_of(key2f(keyP), smax);
+    L = (int64_t)caP + (int64_t)((Wstar - wa + wk - 1) / wk);
   }
   int64_t nsel = kk > L ? kk : L;
   if (nsel > n) nsel = n;
-  if (nsel == 0) {
-    keyL = 0xffffffffu;
-    tieL = 0;
-  } else {
-    // key of the nsel-th element in order and ties to take
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t ca = 0;
-      int bs = 255;
-      for (int b = 0; b < 256; b++) {
-        if ((int64_t)ca + S.cnt[0][b] >= nsel) {
-          bs = b;
-          break;
-        }
-        ca += S.cnt[0][b];
-      }
-      S.bsel[2] = bs;
-      S.above_c[1] = ca;
-    }
-    __syncthreads();
-    bucket_position(row, n, smax, S.bsel[2], nsel - 1 - (int64_t)S.above_c[1], S, &keyL,
-                    &tieL);
+  uint32_t keyL = 0xffffffffu;
+  int64_t tieL = 0;
+  if (nsel > 0 && nsel == L) {
+    // the L*-th element of the order carries the crossing key itself
+    keyL = keyP;
+    tieL = L - (int64_t)caP;
+  } else if (nsel > 0) {
+    uint32_t ca;
+    unsigned long long wa;
+    keyL = radix_select(row, n, smax, false, (unsigned long long)nsel, S, &ca, &wa);
+    tieL = nsel - (int64_t)ca;
   }
   if (threadIdx.x == 0) {
     row_cnt[g] = (int32_t)nsel;
@@ -956,55 +871,116 @@ __global__ __launch_bounds__(1024) void k_scan_rows(const int32_t* __restrict__ 
 
 // Emit each row's selected key blocks in ascending index order; also the
 // row's attention cost B_i * sum_j B_j.
-__global__ __launch_bounds__(256) void k_select_fill(
+// exclusive prefix over the block of one int per thread (kSelThreads threads)
+__device__ inline int block_excl_scan_i32(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(x, off, 64);
+    if (lane >= off) x += u;
+  }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; w++) {
+    before += w < wv ? sh[w] : 0;
+    tot += sh[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+// Writes the selected key blocks of each row in ascending order, given the
+// threshold key K and the number of K-ties to take.  Thread t takes the
+// contiguous segment [tC, tC + C) of the row (C <= 64, in registers): one
+// prefix over the ties and one over the selected counts place every thread's
+// output.  With the row staged in LDS, the output is compacted into that
+// same buffer and stored contiguously.
+template <bool kLds>
+__global__ __launch_bounds__(kSelThreads) void k_select_fill(
     const float* __restrict__ scores, int n, int64_t g0, const int32_t* __restrict__ row_cnt,
     const uint32_t* __restrict__ row_key, const int32_t* __restrict__ row_tie,
     const int64_t* __restrict__ row_ptr, int64_t cap, const uint8_t* __restrict__ blk_shape,
     int32_t* __restrict__ col_idx, int64_t* __restrict__ row_cost) {
-  __shared__ int sh_a[256], sh_b[256];
-  __shared__ int64_t sh_cost[4];
+  extern __shared__ __attribute__((aligned(16))) float srow_dyn[];
+  __shared__ int sh[kSelThreads / 64];
+  __shared__ int64_t sh_cost[kSelThreads / 64];
   const int i = blockIdx.x;
   const int64_t g = g0 + i;
-  const float* row = scores + (int64_t)i * n;
+  const float* grow = scores + (int64_t)i * n;
+  if (kLds) stage_row(grow, n, srow_dyn);
+  const float* row = kLds ? (const float*)srow_dyn : grow;
   const uint32_t K = row_key[g];
   const int tie = row_tie[g];
   const int64_t base = row_ptr[g];
   const bool fits = base + row_cnt[g] <= cap;
-  int tie_carry = 0, out_carry = 0;
+  const int C = (n + kSelThreads - 1) / kSelThreads;  // <= 64 on the LDS path
+  const int j0 = min(n, (int)threadIdx.x * C), j1 = min(n, j0 + C);
+  int total = 0;
   int64_t cost = 0;
-  for (int j0 = 0; j0 < n; j0 += 256) {
-    int j = j0 + threadIdx.x;
-    uint32_t key = j < n ? f2key(row[j]) : 0u;
-    int is_tie = (j < n && key == K) ? 1 : 0;
-    sh_a[threadIdx.x] = is_tie;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      int a = threadIdx.x >= off ? sh_a[threadIdx.x - off] : 0;
-      __syncthreads();
-      sh_a[threadIdx.x] += a;
-      __syncthreads();
+  if (kLds) {
+    uint32_t key[kSelLdsMax / kSelThreads];
+    int ties = 0;
+#pragma unroll
+    for (int e = 0; e < kSelLdsMax / kSelThreads; e++) {
+      key[e] = j0 + e < j1 ? f2key(row[j0 + e]) : 0u;
+      ties += (j0 + e < j1 && key[e] == K) ? 1 : 0;
     }
-    int tie_rank = tie_carry + sh_a[threadIdx.x] - is_tie;
-    int sel = (j < n) && (key > K || (is_tie && tie_rank < tie));
-    tie_carry += sh_a[255];
-    sh_b[threadIdx.x] = sel;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      int a = threadIdx.x >= off ? sh_b[threadIdx.x - off] : 0;
-      __syncthreads();
-      sh_b[threadIdx.x] += a;
-      __syncthreads();
+    int unused;
+    const int tie0 = block_excl_scan_i32(ties, sh, &unused);
+    int nsel = 0;
+    uint64_t selm = 0;  // bit e: element j0 + e selected
+#pragma unroll
+    for (int e = 0, t = tie0; e < kSelLdsMax / kSelThreads; e++) {
+      const bool in = j0 + e < j1;
+      const bool sel = in && (key[e] > K || (key[e] == K && t < tie));
+      t += (in && key[e] == K) ? 1 : 0;
+      if (sel) {
+        nsel++;
+        selm |= 1ull << e;
+        cost += d_shapes[block_shape_at(blk_shape, g0 + j0 + e)].volume;
+      }
     }
-    if (sel) {
-      int pos = out_carry + sh_b[threadIdx.x] - 1;
-      if (fits) col_idx[base + pos] = j;
-      cost += d_shapes[blk_shape[g0 + j]].volume;
+    int pos = block_excl_scan_i32(nsel, sh, &total);
+    // every thread holds its keys in registers: the row buffer takes the output
+    int32_t* sout = (int32_t*)srow_dyn;
+    while (selm) {
+      const int e = __builtin_ctzll(selm);
+      selm &= selm - 1;
+      sout[pos++] = j0 + e;
     }
-    out_carry += sh_b[255];
     __syncthreads();
+    if (fits)
+      for (int e = threadIdx.x; e < total; e += blockDim.x) col_idx[base + e] = sout[e];
+  } else {
+    int ties = 0;
+    for (int j = j0; j < j1; j++) ties += f2key(row[j]) == K;
+    int unused;
+    const int tie0 = block_excl_scan_i32(ties, sh, &unused);
+    int nsel = 0;
+    for (int j = j0, t = tie0; j < j1; j++) {
+      const uint32_t key = f2key(row[j]);
+      const bool sel = key > K || (key == K && t < tie);
+      t += key == K;
+      if (sel) {
+        nsel++;
+        cost += d_shapes[block_shape_at(blk_shape, g0 + j)].volume;
+      }
+    }
+    int pos = block_excl_scan_i32(nsel, sh, &total);
+    for (int j = j0, t = tie0; j < j1; j++) {
+      const uint32_t key = f2key(row[j]);
+      const bool sel = key > K || (key == K && t < tie);
+      t += key == K;
+      if (sel && fits) col_idx[base + pos] = j;
+      pos += sel;
+    }
   }
-  int64_t c = block_sum<int64_t>(cost, sh_cost);
-  if (threadIdx.x == 0) row_cost[g] = c * (int64_t)d_shapes[blk_shape[g]].volume;
+  const int64_t c = block_sum<int64_t>(cost, sh_cost);
+  if (threadIdx.x == 0) row_cost[g] = c * (int64_t)d_shapes[block_shape_at(blk_shape, g)].volume;
 }
 
 // ============================================================ K7: key-major lists
@@ -1177,17 +1153,34 @@ bool launch_block_scores(const PlanDev& P, int64_t g0, int n, float* out, hipStr
   return hipGetLastError() == hipSuccess;
 }
 
+// dynamic LDS of the staged row: n floats, rounded up to whole 64-float
+// pieces of the staging loads
+static unsigned sel_lds_bytes(int n) { return (unsigned)((n + 63) / 64 * 64 * 4); }
+
 bool launch_select(const PlanDev& P, int64_t g0, int n, const prism_config& c, int last,
                    hipStream_t st) {
-  if (n > 0)
-    hipLaunchKernelGGL(k_select_count, dim3(n), dim3(kSelThreads), 0, st, P.scores, n, g0,
-                       c.top_k, c.top_k_frac, c.top_p, P.row_cnt, P.row_key, P.row_tie);
+  const bool lds = n <= kSelLdsMax;
+  if (n > 0) {
+    if (lds)
+      hipLaunchKernelGGL(k_select_count<true>, dim3(n), dim3(kSelThreads), sel_lds_bytes(n), st,
+                         P.scores, n, g0, c.top_k, c.top_k_frac, c.top_p, P.row_cnt, P.row_key,
+                         P.row_tie);
+    else
+      hipLaunchKernelGGL(k_select_count<false>, dim3(n), dim3(kSelThreads), 0, st, P.scores, n,
+                         g0, c.top_k, c.top_k_frac, c.top_p, P.row_cnt, P.row_key, P.row_tie);
+  }
   hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, st, P.row_cnt, n, g0, P.row_ptr,
                      P.counters, last);
-  if (n > 0)
-    hipLaunchKernelGGL(k_select_fill, dim3(n), dim3(256), 0, st, P.scores, n, g0, P.row_cnt,
-                       P.row_key, P.row_tie, P.row_ptr, P.cap, P.blk_shape, P.col_idx,
-                       P.row_cost);
+  if (n > 0) {
+    if (lds)
+      hipLaunchKernelGGL(k_select_fill<true>, dim3(n), dim3(kSelThreads), sel_lds_bytes(n), st,
+                         P.scores, n, g0, P.row_cnt, P.row_key, P.row_tie, P.row_ptr, P.cap,
+                         P.blk_shape, P.col_idx, P.row_cost);
+    else
+      hipLaunchKernelGGL(k_select_fill<false>, dim3(n), dim3(kSelThreads), 0, st, P.scores, n,
+                         g0, P.row_cnt, P.row_key, P.row_tie, P.row_ptr, P.cap, P.blk_shape,
+                         P.col_idx, P.row_cost);
+  }
   return hipGetLastError() == hipSuccess;
 }
 
