@@ -983,33 +983,86 @@ __global__ __launch_bounds__(kSelThreads) void k_select_fill(
   if (threadIdx.x == 0) row_cost[g] = c * (int64_t)d_shapes[block_shape_at(blk_shape, g)].volume;
 }
 
-// ============================================================ K7: key-major lists
-// For each key block, the query blocks whose S_i contains it, ascending.
-__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
-  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
+// Key-major transpose of one head's lists, by tiles of 64 query rows x 256
+// key columns.  A work-group takes 64 rows and a part of kTrPart columns:
+// each row's start in that part is found by one binary search, then every
+// 256-column tile is built as one 64-bit row mask per column (one wave per
+// row walks the row's sorted list with coalesced reads; LDS atomic ORs set
+// the bits).  The counting pass stores popcounts per (row tile, column); the
+// fill pass rebuilds the masks and writes each column's rows in ascending
+// order at its offset.  No global atomics, and the result does not depend on
+// the order of the ORs.
+constexpr int kTrRows = 64;
+constexpr int kTrCols = 256;
+constexpr int kTrPart = 2048;
 
-// per chunk of 64 query rows: column histograms (integer atomics)
-__global__ __launch_bounds__(256) void k_colt_count(const int64_t* __restrict__ row_ptr,
-                                                    const int32_t* __restrict__ col_idx, int n,
-                                                    int64_t g0, int32_t* __restrict__ chunk_cnt,
-                                                    int32_t* __restrict__ colt_cnt) {
-  const int c = blockIdx.x;
-  const int i0 = c * 64, i1 = min(n, i0 + 64);
-  for (int i = i0; i < i1; i++) {
-    int64_t a = row_ptr[g0 + i], b = row_ptr[g0 + i + 1];
-    for (int64_t e = a + threadIdx.x; e < b; e += blockDim.x) {
-      int j = col_idx[e];
-      atomicAdd(&chunk_cnt[(int64_t)c * n + j], 1);
-      atomicAdd(&colt_cnt[j], 1);
+template <bool kFill>
+__global__ __launch_bounds__(kTrCols) void k_colt_tiles(
+    const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int n, int64_t g0,
+    const int64_t* __restrict__ colt_ptr, int32_t* __restrict__ tile_cnt,
+    int32_t* __restrict__ colt_idx) {
+  __shared__ int64_t cur[kTrRows], fin[kTrRows];
+  __shared__ unsigned long long mask[kTrCols];
+  const int rt = blockIdx.x;
+  const int i0 = rt * kTrRows, nrows = min(kTrRows, n - i0);
+  const int c0 = blockIdx.y * kTrPart, c1 = min(n, c0 + kTrPart);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (threadIdx.x < kTrRows && (int)threadIdx.x < nrows) {
+    // first entry of the row at or after column c0
+    const int r = threadIdx.x;
+    int64_t lo = row_ptr[g0 + i0 + r], hi = row_ptr[g0 + i0 + r + 1];
+    fin[r] = hi;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (col_idx[mid] < c0)
+        lo = mid + 1;
+      else
+        hi = mid;
     }
+    cur[r] = lo;
+  }
+  __syncthreads();
+  for (int t0 = c0; t0 < c1; t0 += kTrCols) {
+    const int t1 = min(c1, t0 + kTrCols);
+    mask[threadIdx.x] = 0ull;
+    __syncthreads();
+    for (int r = wv; r < nrows; r += kTrCols / 64) {
+      int64_t c = cur[r];
+      const int64_t e = fin[r];
+      while (true) {
+        const int64_t idx = c + lane;
+        const int col = idx < e ? col_idx[idx] : 0x7fffffff;
+        const bool in = col < t1;  // a prefix of the lanes: the list is sorted
+        if (in) atomicOr(&mask[col - t0], 1ull << r);
+        const int m = __popcll(__ballot(in));
+        c += m;
+        if (m < 64) break;
+      }
+      if (lane == 0) cur[r] = c;
+    }
+    __syncthreads();
+    const int col = t0 + threadIdx.x;
+    if (col < t1) {
+      unsigned long long m = mask[threadIdx.x];
+      if (!kFill) {
+        tile_cnt[(int64_t)rt * n + col] = __popcll(m);
+      } else {
+        int64_t pos = colt_ptr[g0 + col] + tile_cnt[(int64_t)rt * n + col];
+        while (m) {
+          colt_idx[pos++] = i0 + __builtin_ctzll(m);
+          m &= m - 1;
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
-// per column: turn the chunk counts into output positions relative to the
-// column's start (at most n, so they fit in 32 bits at any nnz)
-__global__ void k_colt_offsets(int n, int nch, int32_t* __restrict__ chunk_cnt) {
+// per column: turn the row-tile counts into output positions relative to the
+// column's start (at most n, so they fit in 32 bits at any nnz), and the
+// column's total
+__global__ void k_colt_offsets(int n, int nch, int32_t* __restrict__ chunk_cnt,
+                               int32_t* __restrict__ colt_cnt) {
   int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
   int32_t run = 0;
@@ -1018,25 +1071,7 @@ __global__ void k_colt_offsets(int n, int nch, int32_t* __restrict__ chunk_cnt) 
     chunk_cnt[(int64_t)c * n + j] = run;
     run += t;
   }
-}
-
-// per chunk: rows in ascending order, each row's entries in parallel
-__global__ __launch_bounds__(256) void k_colt_fill(const int64_t* __restrict__ row_ptr,
-                                                   const int32_t* __restrict__ col_idx, int n,
-                                                   int64_t g0, const int64_t* __restrict__ colt_ptr,
-                                                   int32_t* __restrict__ chunk_cnt,
-                                                   int32_t* __restrict__ colt_idx) {
-  const int c = blockIdx.x;
-  const int i0 = c * 64, i1 = min(n, i0 + 64);
-  for (int i = i0; i < i1; i++) {
-    int64_t a = row_ptr[g0 + i], b = row_ptr[g0 + i + 1];
-    for (int64_t e = a + threadIdx.x; e < b; e += blockDim.x) {
-      int j = col_idx[e];
-      const int64_t pos = colt_ptr[g0 + j] + atomicAdd(&chunk_cnt[(int64_t)c * n + j], 1);
-      colt_idx[pos] = i;
-    }
-    __syncthreads();
-  }
+  colt_cnt[j] = run;
 }
 
 // key-major scan: counts per column -> pointers (reuses k_scan_rows on colt_cnt)
@@ -1186,20 +1221,16 @@ bool launch_select(const PlanDev& P, int64_t g0, int n, const prism_config& c, i
 
 bool launch_transpose(const PlanDev& P, int64_t g0, int n, int last, hipStream_t st) {
   if (n <= 0) return true;
-  int nch = (n + 63) / 64;
-  int64_t cells = (int64_t)nch * n;
-  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((cells + 255) / 256)), dim3(256), 0, st,
-                     P.chunk_cnt, cells, 0);
-  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, st, P.colt_cnt + g0,
-                     (int64_t)n, 0);
-  hipLaunchKernelGGL(k_colt_count, dim3(nch), dim3(256), 0, st, P.row_ptr, P.col_idx, n, g0,
+  const int nrt = (n + kTrRows - 1) / kTrRows;
+  const dim3 grid((unsigned)nrt, (unsigned)((n + kTrPart - 1) / kTrPart));
+  hipLaunchKernelGGL(k_colt_tiles<false>, grid, dim3(kTrCols), 0, st, P.row_ptr, P.col_idx, n,
+                     g0, P.colt_ptr, P.chunk_cnt, P.colt_idx);
+  hipLaunchKernelGGL(k_colt_offsets, dim3((n + 255) / 256), dim3(256), 0, st, n, nrt,
                      P.chunk_cnt, P.colt_cnt + g0);
   hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, st, P.colt_cnt, n, g0, P.colt_ptr,
                      P.counters + 1, last);
-  hipLaunchKernelGGL(k_colt_offsets, dim3((n + 255) / 256), dim3(256), 0, st, n, nch,
-                     P.chunk_cnt);
-  hipLaunchKernelGGL(k_colt_fill, dim3(nch), dim3(256), 0, st, P.row_ptr, P.col_idx, n, g0,
-                     P.colt_ptr, P.chunk_cnt, P.colt_idx);
+  hipLaunchKernelGGL(k_colt_tiles<true>, grid, dim3(kTrCols), 0, st, P.row_ptr, P.col_idx, n,
+                     g0, P.colt_ptr, P.chunk_cnt, P.colt_idx);
   return hipGetLastError() == hipSuccess;
 }
 
