@@ -57,6 +57,7 @@ def cpu_baseline(wl, x, nblocks):
     bits = {n: synth.to_numpy_bits(h0[n]) for n in h0}
     av = x["av"].detach().cpu().numpy()
     cfg = O.Config(wl.T, wl.H, wl.W, 1, wl.head_dim, top_k=wl.top_k, top_p=wl.top_p,
+                   top_k_frac=wl.top_k_frac,
                    volume_mask=wl.volume_mask, fixed_shape=tuple(wl.fixed_shape))
     pl = O.plan(bits["q"], bits["k"], bits["v"], av, cfg)
     lens = pl.blk_len[: pl.nblk(0)]
@@ -99,7 +100,7 @@ def main():
     print(f"[bench] inputs {wl.name} drawn in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
     q, k, v, do, av = x["q"], x["k"], x["v"], x["do"], x["av"]
-    kw = dict(T=wl.T, H=wl.H, W=wl.W, top_k=wl.top_k, top_p=wl.top_p,
+    kw = dict(T=wl.T, H=wl.H, W=wl.W, top_k=wl.top_k, top_p=wl.top_p, top_k_frac=wl.top_k_frac,
               volume_mask=wl.volume_mask, fixed_shape=tuple(wl.fixed_shape),
               need_backward=not args.fwd_only)
     o = torch.empty_like(q)
@@ -192,9 +193,12 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: T*H*W={wl.T}x{wl.H}x{wl.W} ({wl.N} tokens), "
-                               f"{wl.heads} heads x {D}, k={wl.top_k}, p={wl.top_p}, "
+                               f"{wl.heads} heads x {D}, "
+                               f"k={f'{wl.top_k_frac:g} of N_blk' if wl.top_k_frac else wl.top_k}, "
+                               f"p={wl.top_p}, "
                                f"{'fwd' if args.fwd_only else 'fwd+bwd'}",
                    "tokens": wl.N, "heads": wl.heads, "head_dim": D, "top_k": wl.top_k,
+                   "top_k_frac": wl.top_k_frac,
                    "top_p": wl.top_p, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

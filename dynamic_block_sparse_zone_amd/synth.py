@@ -37,6 +37,7 @@ class Workload:
     seed: int = 1001
     backward: bool = False
     unit_var: bool = False
+    top_k_frac: float = 0.0    # > 0: k = ceil(frac * N_blk) per head instead of top_k
 
     @property
     def N(self) -> int:
@@ -69,6 +70,12 @@ WORKLOADS = {
     "fixed2k": Workload("fixed2k", 64, 104, 128, 40, 128, "bf16", top_k=16, top_p=0.9,
                         kind="background", active_frac=0.2, seed=1003,
                         fixed_shape=(4, 4, 8)),
+    # the pages' operating point (Top-k at 95 % sparsity, i.e. 5 % of the key
+    # blocks, with Top-p 0.2) on the inference- and training-scale inputs
+    "infer2k_op": Workload("infer2k_op", 64, 104, 128, 40, 128, "bf16", top_k=0, top_p=0.2,
+                           kind="background", active_frac=0.2, seed=1003, top_k_frac=0.05),
+    "train2k_op": Workload("train2k_op", 72, 120, 120, 40, 128, "bf16", top_k=0, top_p=0.2,
+                           seed=1004, backward=True, unit_var=True, top_k_frac=0.05),
     # small bf16 grid for full element-by-element checks (fwd + bwd): several
     # zones of every volume, a ragged number of blocks per head
     "check": Workload("check", 16, 24, 32, 3, 128, "bf16", top_k=3, top_p=0.9, seed=1006,
