@@ -119,56 +119,56 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
   };
   // one tile: S^T = K Q^T, online softmax, O^T += V^T P^T
   auto compute = [&](const char* sk, const char* sv) {
-      f32x16 st[2];
-  #pragma unroll
+    f32x16 st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) st[kb][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 8; kk++)
+#pragma unroll
       for (int kb = 0; kb < 2; kb++)
-  #pragma unroll
-        for (int r = 0; r < 16; r++) st[kb][r] = 0.0f;
-  #pragma unroll
-      for (int kk = 0; kk < 8; kk++)
-  #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sk + kb * 8192 + ro[kk]),
-                                                           qf[kk], st[kb], 0, 0, 0);
-      float mx = st[0][0];
-  #pragma unroll
-      for (int r = 1; r < 16; r++) mx = fmaxf(mx, st[0][r]);
-  #pragma unroll
-      for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[1][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mt = mx * c_log2;
-      const bool need = mt > m_run + 8.0f;
-      if (__any(need)) {
-        const float mnew = need ? mt : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-        l_run *= alpha;
-  #pragma unroll
-        for (int db = 0; db < 4; db++)
-  #pragma unroll
-          for (int r = 0; r < 16; r++) acc[db][r] *= alpha;
-        m_run = mnew;
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sk + kb * 8192 + ro[kk]),
+                                                         qf[kk], st[kb], 0, 0, 0);
+    float mx = st[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; r++) mx = fmaxf(mx, st[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[1][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mt = mx * c_log2;
+    const bool need = mt > m_run + 8.0f;
+    if (__any(need)) {
+      const float mnew = need ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[db][r] *= alpha;
+      m_run = mnew;
+    }
+    const float negm = -m_run;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int r = 8 * (c & 1) + 2 * e;
+        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r], c_log2, negm));
+        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r + 1], c_log2, negm));
+        pk[e] = pk2(p0, p1);
+        // the row sum takes the same bf16 probabilities that weight V
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), kOnes2,
+                                                l_run, false);
       }
-      const float negm = -m_run;
-  #pragma unroll
-      for (int c = 0; c < 4; c++) {
-        uint32_t pk[4];
-  #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int r = 8 * (c & 1) + 2 * e;
-          float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r], c_log2, negm));
-          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r + 1], c_log2, negm));
-          pk[e] = pk2(p0, p1);
-          // the row sum takes the same bf16 probabilities that weight V
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), kOnes2,
-                                                  l_run, false);
-        }
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-  #pragma unroll
-        for (int db = 0; db < 4; db++)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              ld_tfrag(sv + c * 4096 + to[db][0], sv + c * 4096 + to[db][1]), pb, acc[db], 0, 0,
-              0);
-      }
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ld_tfrag(sv + c * 4096 + to[db][0], sv + c * 4096 + to[db][1]), pb, acc[db], 0, 0,
+            0);
+    }
   };
   issue(0);
   issue(1);
