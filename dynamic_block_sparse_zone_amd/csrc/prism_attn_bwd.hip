@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
     int64_t row = last_row;
     uint32_t f = 0;
     if (it.valid) {
-      row = it.row;
+      row = it.row();
       f = (uint32_t)it.mask;
       last_row = row;
       nreal++;
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
   const int nlists = B >= kDqRows ? 1 : kDqRows / B;  // query blocks in the unit
   const int mylist = (32 * wvu) / B < nlists ? (32 * wvu) / B : 0;
 
-  TileIter it;
+  TileIterS it;
   it.init(row_ptr, col_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_start,
           blk_shape, hoff);
 
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
     int64_t row = last_row;
     uint32_t mask = 0;
     if (it.valid) {
-      row = it.row;
+      row = it.row();
       mask = (uint32_t)it.mask;
       last_row = row;
       nreal++;

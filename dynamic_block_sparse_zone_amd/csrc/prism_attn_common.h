@@ -107,11 +107,15 @@ __device__ inline bf16x8 row_chunk(const uint16_t* buf, int64_t row, int chunk) 
       bf16x8, *(const uint4*)(buf + row * 128 + ((chunk ^ chunk_swizzle((int)(row & 63))) << 3)));
 }
 
+// The same walk with plain (scalar) loads, for the dQ kernel, where it runs
+// faster: with the vector-memory walk below, using a list value loaded a
+// step earlier also waits for the tile loads issued before it, which takes
+// one of the two tiles that ring keeps in flight.
 // Merged walk over up to four ascending block lists (the lists of the
 // query blocks of one work unit, or of its key blocks in the key-major
 // transpose): yields each block once, with a bit mask of the lists that
 // hold it.
-struct UnionIter {
+struct UnionIterS {
   const int32_t* col;
   int64_t a[4], e[4];
   int head[4];
@@ -138,13 +142,14 @@ struct UnionIter {
   }
 };
 
-// The 64-row tiles of the blocks of a merged walk, in order.
-struct TileIter {
-  UnionIter U;
+// The 64-row tiles of the blocks of a merged walk, in order (scalar loads).
+struct TileIterS {
+  UnionIterS U;
   const int32_t* blk_start;
   const uint8_t* blk_shape;
   int64_t hoff;
-  int64_t row;  // first permuted row of the current tile
+  int64_t row_;  // first permuted row of the current tile
+  __device__ int64_t row() const { return row_; }
   int t, nt, mask;
   bool valid;
   // lists ptr[g0 + i] .. ptr[g0 + i + 1] for i < nl
@@ -168,16 +173,99 @@ struct TileIter {
   __device__ void advance() {
     if (valid && t + 1 < nt) {
       t++;
-      row += 64;
+      row_ += 64;
       return;
     }
     int j;
     valid = U.next(j, mask);
     if (valid) {
-      row = blk_start[hoff + j];
+      row_ = blk_start[hoff + j];
       nt = d_shapes[block_shape_at(blk_shape, hoff + j)].volume >> 6;
       t = 0;
     }
+  }
+};
+
+// The 64-row tiles of the blocks of a merged walk over up to four ascending
+// block lists (the lists of the query blocks of one work unit, or of its key
+// blocks in the key-major transpose), in block order; each block comes once,
+// with a bit mask of the lists that hold it.
+//
+// The list entries, block starts and shape ids are read with buffer (vector
+// memory) loads whose values are only needed a step later (the next head of
+// a list, the next tile's row and the block's tile count), so their latency
+// hides behind the tile in between; scalar loads would share the counter of
+// the LDS reads, and every LDS wait of the tile would then wait for them too.
+// The loaded values stay in vector registers (the load offsets carry an
+// opaque per-lane zero, so that the compiler does not move them to scalar
+// registers at once, which would wait for the load, and with it for every
+// earlier tile load) and are read out with readfirstlane where they are used.
+struct TileIter {
+  __amdgpu_buffer_rsrc_t rcol, rstart, rshape;
+  int a[4], e[4];  // list positions relative to the first list's start
+  int opq;
+  int head_v[4];         // next entry of each list (0x7fffffff: exhausted)
+  int start_v, sid_v;    // the current block's start row and shape id
+  int t, mask;
+  bool valid;
+  // lists ptr[g0 + i] .. ptr[g0 + i + 1] for i < nl (consecutive, so one
+  // buffer covers them); block j's start and shape id at bs[off + j],
+  // bsh[off + j]
+  __device__ void init(const int64_t* ptr, const int32_t* col, int64_t g0, int nl,
+                       const int32_t* bs, const uint8_t* bsh, int64_t off) {
+    asm volatile("v_mov_b32 %0, 0" : "=v"(opq));
+    const int64_t base = ptr[g0];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      a[i] = i < nl ? (int)(ptr[g0 + i] - base) : 0;
+      e[i] = i < nl ? (int)(ptr[g0 + i + 1] - base) : 0;
+    }
+    rcol = buffer_of(col + base, (uint32_t)(ptr[g0 + nl] - base) * 4u);
+    rstart = buffer_of(bs + off, 0xffffffffu);
+    rshape = buffer_of(bsh + off, 0xffffffffu);
+#pragma unroll
+    for (int i = 0; i < 4; i++) head_v[i] = a[i] < e[i] ? load_col(i) : 0x7fffffff;
+    valid = true;
+    t = 0;
+    sid_v = 0;  // one tile: the first advance moves to the first block
+    advance();
+  }
+  __device__ int load_col(int i) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(rcol, a[i] * 4 + opq, 0, 0);
+  }
+  // shape ids are ordered by volume: 0..6 are 64 rows, 7..12 128, 13..15 256
+  __device__ int tiles() const {
+    const int sid = __builtin_amdgcn_readfirstlane(sid_v);
+    return sid < 7 ? 1 : sid < 13 ? 2 : 4;
+  }
+  // first permuted row of the current tile
+  __device__ int64_t row() const {
+    return (int64_t)__builtin_amdgcn_readfirstlane(start_v) + 64 * t;
+  }
+  __device__ void advance() {
+    if (valid && t + 1 < tiles()) {
+      t++;
+      return;
+    }
+    int head[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) head[i] = __builtin_amdgcn_readfirstlane(head_v[i]);
+    int best = head[0];
+#pragma unroll
+    for (int i = 1; i < 4; i++) best = head[i] < best ? head[i] : best;
+    valid = best != 0x7fffffff;
+    if (!valid) return;
+    mask = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      if (head[i] == best) {
+        mask |= 1 << i;
+        a[i]++;
+        head_v[i] = a[i] < e[i] ? load_col(i) : 0x7fffffff;
+      }
+    start_v = __builtin_amdgcn_raw_buffer_load_b32(rstart, best * 4 + opq, 0, 0);
+    sid_v = __builtin_amdgcn_raw_buffer_load_b8(rshape, best + opq, 0, 0);
+    t = 0;
   }
 };
 

@@ -11,10 +11,18 @@
 //  * every wave owns 32 query rows and computes S^T = K Q^T with
 //    v_mfma_f32_32x32x16_bf16 (K from LDS, Q in registers), so that each lane
 //    holds one query row's scores and the softmax needs one cross-lane step;
-//  * O^T += V^T P^T reuses the score registers as the B operand directly; the
-//    V^T fragments come from the row-major V tile by ds_read_b64_tr_b16;
-//  * K/V tiles of 64 keys stream through a 4-slot LDS ring, three tiles in
-//    flight while one is computed;
+//  * O^T += V^T P^T takes the bf16 probabilities as the B operand directly;
+//    the V^T fragments come from the row-major V tile by ds_read_b64_tr_b16;
+//  * K/V tiles of 64 keys stream through a 4-slot LDS ring: the barrier of
+//    step j publishes tile j + 1 and frees the slot of tile j - 1 for tile
+//    j + 3, so while tile j is computed the next one is already readable;
+//  * the fragment reads that open each matrix stretch are issued one stretch
+//    early (the first K fragments of tile j + 1 during the P V of tile j,
+//    the first V fragments during the softmax), so the two waves of a SIMD,
+//    which run in step, do not both wait for LDS at the start of a stretch;
+//  * the row maximum crosses the two 32-lane halves with v_permlane32_swap
+//    (an LDS-free exchange: a ds_bpermute would make every later LDS wait of
+//    the tile a full drain of the prefetched reads);
 //  * the softmax maximum is only moved when it grows by more than 2^8, so the
 //    accumulator rescale is rare.
 #include "prism_attn_common.h"
@@ -99,7 +107,7 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
     int64_t row = last_row;
     uint32_t mask = 0;
     if (it.valid) {
-      row = it.row;
+      row = it.row();
       mask = (uint32_t)it.mask;
       last_row = row;
       nreal++;
@@ -108,8 +116,11 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
     ring_mask = (ring_mask & ~(0xffu << (8 * b))) | (mask << (8 * b));
     stage(b, row);
   };
+  // step j: tiles j and j + 1 have landed (each wave waits for its own
+  // pieces, the barrier for everybody's), every wave is done with tile
+  // j - 1, and its slot takes tile j + 3
   auto ring_step = [&](int j) {
-    __builtin_amdgcn_s_waitcnt(wait_vm(2 * kFwdLoads));
+    __builtin_amdgcn_s_waitcnt(wait_vm(kFwdLoads));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue((j + kRing - 1) & (kRing - 1));
@@ -117,25 +128,46 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
   auto listed = [&](int j) {
     return ((ring_mask >> (8 * (j & (kRing - 1)) + mylist)) & 1u) != 0;
   };
+  // fragment i (0..15) of S^T = K Q^T: channels 16 (i / 2).., keys 32 (i % 2)..
+  auto kfrag = [&](const char* sk, int i) { return ld_frag(sk + (i & 1) * 8192 + ro[i >> 1]); };
+  // fragment t (0..15) of O^T += V^T P^T: keys 16 (t / 4).., channels 32 (t % 4)..
+  auto vfrag = [&](const char* sv, int t) {
+    return ld_tfrag(sv + (t >> 2) * 4096 + to[t & 3][0], sv + (t >> 2) * 4096 + to[t & 3][1]);
+  };
+  constexpr int kPre = 4;  // fragments read one stretch early
+  bf16x8 kpre[kPre];
+  int kpre_tile = -1;  // the tile whose first K fragments kpre holds
   // one tile: S^T = K Q^T, online softmax, O^T += V^T P^T
-  auto compute = [&](const char* sk, const char* sv) {
+  auto compute = [&](int j) {
+    const char* sk = ringK + (j & (kRing - 1)) * kTile;
+    const char* sv = ringV + (j & (kRing - 1)) * kTile;
+    if (kpre_tile != j) {
+#pragma unroll
+      for (int i = 0; i < kPre; i++) kpre[i] = kfrag(sk, i);
+    }
     f32x16 st[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
+    for (int i = 0; i < 16; i++)
+      st[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(i < kPre ? kpre[i] : kfrag(sk, i),
+                                                          qf[i >> 1], i < 2 ? f32x16{} : st[i & 1],
+                                                          0, 0, 0);
+    // the first V fragments of P V are read while the softmax runs
+    bf16x8 vpre[kPre];
 #pragma unroll
-      for (int r = 0; r < 16; r++) st[kb][r] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 8; kk++)
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++)
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sk + kb * 8192 + ro[kk]),
-                                                         qf[kk], st[kb], 0, 0, 0);
+    for (int t = 0; t < kPre; t++) vpre[t] = vfrag(sv, t);
+    // (the fences keep such early reads where they are written)
+    __builtin_amdgcn_sched_barrier(0);
     float mx = st[0][0];
 #pragma unroll
     for (int r = 1; r < 16; r++) mx = fmaxf(mx, st[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    {
+      const uint32_t mb = __builtin_bit_cast(uint32_t, mx);
+      const auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+      mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
+                 __builtin_bit_cast(float, (uint32_t)sw[1]));
+    }
     const float mt = mx * c_log2;
     const bool need = mt > m_run + 8.0f;
     if (__any(need)) {
@@ -149,6 +181,7 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
       m_run = mnew;
     }
     const float negm = -m_run;
+    bf16x8 pb[4];
 #pragma unroll
     for (int c = 0; c < 4; c++) {
       uint32_t pk[4];
@@ -158,17 +191,22 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
         float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r], c_log2, negm));
         float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r + 1], c_log2, negm));
         pk[e] = pk2(p0, p1);
-        // the row sum takes the same bf16 probabilities that weight V
         l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), kOnes2,
                                                 l_run, false);
       }
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-#pragma unroll
-      for (int db = 0; db < 4; db++)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            ld_tfrag(sv + c * 4096 + to[db][0], sv + c * 4096 + to[db][1]), pb, acc[db], 0, 0,
-            0);
+      pb[c] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
+    // the first K fragments of the next tile (published by this step's
+    // barrier) are read while P V runs
+    const char* skn = ringK + ((j + 1) & (kRing - 1)) * kTile;
+#pragma unroll
+    for (int i = 0; i < kPre; i++) kpre[i] = kfrag(skn, i);
+    kpre_tile = j + 1;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 16; t++)
+      acc[t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t < kPre ? vpre[t] : vfrag(sv, t),
+                                                           pb[t >> 2], acc[t & 3], 0, 0, 0);
   };
   issue(0);
   issue(1);
@@ -179,7 +217,7 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
     while (j < nreal && !listed(j)) ring_step(j++);
     if (j >= nreal) break;
     ring_step(j);
-    compute(ringK + (j & (kRing - 1)) * kTile, ringV + (j & (kRing - 1)) * kTile);
+    compute(j);
     j++;
   }
   // no tile load may still be writing LDS when the work-group ends
