@@ -29,6 +29,99 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # algorithmic FLOP per selected pair (B_i * B_j tokens), per head_dim channel
 FLOP_PER_PAIR = {"attn.fwd": 4, "bwd.dkdv": 8, "bwd.dq": 6}
 
+# timing stage -> (kernel symbol, the sources its code comes from)
+KERNELS = {
+    "attn.fwd": ("k_attn_fwd_bf16", ["prism_attn_fwd.hip"]),
+    "bwd.dkdv": ("k_bwd_dkdv", ["prism_attn_bwd.hip"]),
+    "bwd.dq": ("k_bwd_dq", ["prism_attn_bwd.hip"]),
+}
+COMMON_SOURCES = ["prism_attn_common.h", "prism_common.h", "prism_kernels.h"]
+CALIB_BYTES = 1 << 30       # the calibration copy reads and writes this many bytes
+
+
+def kernel_source_sha(stage):
+    """sha256 over the sources of a stage's kernel (its counters go stale
+    when these change)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNELS[stage][1] + COMMON_SOURCES:
+        with open(os.path.join(ROOT, "dynamic_block_sparse_zone_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_file(stage, workload):
+    return os.path.join(ROOT, "profiles", f"{KERNELS[stage][0]}_{workload}_traffic.md")
+
+
+def read_traffic(stage, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    path = traffic_file(stage, workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != kernel_source_sha(stage):
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def summarize_pmc(fetch_csv, write_csv, stage, workload, cmds, out):
+    """Turns two rocprofv3 counter-collection CSVs (FETCH_SIZE, WRITE_SIZE,
+    in KiB per dispatch) of a profiled step that ends with the calibration
+    copy into per-launch HBM traffic of a stage's kernel, each counter
+    scaled by its reading for the copy of known size."""
+    import csv
+    sym = KERNELS[stage][0]
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        kern = [float(r["Counter_Value"]) * 1024 for r in rows if sym in r["Kernel_Name"]]
+        # the calibration copy is the run's only bitwise-not kernel
+        copies = [float(r["Counter_Value"]) * 1024 for r in rows
+                  if "bitwise_not" in r["Kernel_Name"]]
+        if not kern or len(copies) != 1:
+            raise SystemExit(f"{path}: {len(kern)} {sym} and {len(copies)} copy dispatches "
+                             f"with {counter}")
+        return sum(kern) / len(kern), copies[0]
+
+    fk, fc = per_kernel(fetch_csv, "FETCH_SIZE")
+    wk, wc = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = CALIB_BYTES / fc, CALIB_BYTES / wc
+    fetch, write = fk * f_scale, wk * w_scale
+    lines = [
+        f"# {sym}: HBM traffic per launch, {workload}",
+        "",
+        "Two `rocprofv3 --pmc` passes over one profiled step that ends with a plain",
+        f"copy of {CALIB_BYTES >> 20} MiB (read and write); each counter is scaled by "
+        "the factor that makes it read the copy's known size.",
+        "",
+        "Commands (from /tmp, TMPDIR=/tmp):",
+        "",
+        *[f"    {c}" for c in cmds],
+        "",
+        f"- kernel: `{sym}` (stage `{stage}`)",
+        f"- fetch_raw_bytes_per_launch: {fk:.6g}",
+        f"- write_raw_bytes_per_launch: {wk:.6g}",
+        f"- copy_fetch_raw_bytes: {fc:.6g}",
+        f"- copy_write_raw_bytes: {wc:.6g}",
+        f"- fetch_scale: {f_scale:.4f}",
+        f"- write_scale: {w_scale:.4f}",
+        f"- fetch_bytes_per_launch: {fetch:.6g}",
+        f"- write_bytes_per_launch: {write:.6g}",
+        f"- traffic_bytes_per_launch: {fetch + write:.6g}",
+        f"- source_sha256: `{kernel_source_sha(stage)}`",
+        "",
+    ]
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -40,6 +133,14 @@ def parse():
     ap.add_argument("--cpu-blocks", type=int, default=0,
                     help="query blocks in the CPU-oracle sample (0 = host cores)")
     ap.add_argument("--fwd-only", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="end with a plain copy of known size (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary of the dominant kernel from two "
+                         "rocprofv3 counter-collection CSVs, then exit")
+    ap.add_argument("--stage", default="bwd.dkdv", help="kernel stage for --summarize-pmc")
+    ap.add_argument("--cmd", action="append", default=[],
+                    help="profiling command lines to record in the summary")
     return ap.parse_args()
 
 
@@ -83,6 +184,10 @@ def cpu_baseline(wl, x, nblocks):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.stage, args.workload, args.cmd,
+                      traffic_file(args.stage, args.workload))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
@@ -202,7 +307,8 @@ def main():
                    "top_p": wl.top_p, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": read_traffic(dom, wl.name) if dom in KERNELS else None},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2) if attn_ms else None,
         "stage_ms": {s: round(v, 3) for s, v in sorted(ms.items())},
@@ -218,6 +324,14 @@ def main():
         "shape_hist": info["shape_hist"],
         "wall_s": round(wall, 2),
     }
+    if args.calib_copy:
+        # one elementwise kernel that reads and writes CALIB_BYTES each (an
+        # op that nothing else in the run uses, so its dispatch is found by
+        # name)
+        a = torch.zeros(CALIB_BYTES // 2, dtype=torch.int16, device=dev)
+        b = torch.bitwise_not(a)
+        torch.cuda.synchronize()
+        del a, b
     if not args.no_cpu:
         nb = args.cpu_blocks or max(1, min(16, os.cpu_count() or 1))
         print(f"[bench] cpu baseline: oracle on {nb} query blocks", file=sys.stderr, flush=True)
