@@ -622,6 +622,11 @@ __device__ inline T block_sum(T v, T* sh) {
 constexpr int kSelThreads = 256;
 // longest score row (key blocks of a head) the selection kernels stage in LDS
 constexpr int kSelLdsMax = 16384;
+// floats of LDS a staged row takes (rounded up to whole 64-lane pieces)
+__host__ __device__ inline int sel_row_floats(int n) { return (n + 63) / 64 * 64; }
+// block volume of a shape id (ids are ordered by volume: 0..6 are 64,
+// 7..12 are 128, 13..15 are 256)
+__device__ inline int volume_of_id(int sid) { return sid < 7 ? 64 : sid < 13 ? 128 : 256; }
 
 // One score row (n <= kSelLdsMax floats) into LDS: every wave issues its
 // 256-byte pieces as direct HBM->LDS loads, all in flight at once, then one
@@ -644,7 +649,7 @@ struct SelShared {
   unsigned long long wt[kSelThreads / 64][256];
   unsigned long long red64[kSelThreads / 64];
   unsigned long long wstar;
-  float redf[kSelThreads / 64];
+  float redf[kSelThreads / 64], redn[kSelThreads / 64];
   int pick;
 };
 
@@ -666,104 +671,184 @@ __device__ inline unsigned long long block_incl_scan(unsigned long long v,
   return before + v;
 }
 
-// One level of a radix select over the 32-bit order keys of a row, from the
-// most significant byte down.  Among the keys whose bytes above `shift`
-// equal `prefix`, builds the histogram of the byte at `shift` (counts, and
+// Sources of a row's scores for the selection passes: src.each(f) calls f
+// on every score of this thread's share of the row (elements tid + 256 e).
+// LdsRow reads a row staged in LDS eight elements at a time, all eight reads
+// in flight before any is used (one at a time, every element paid the LDS
+// latency); GlobalRow reads a row of any length from HBM on every pass.
+struct LdsRow {
+  const float* row;
+  int n;
+  template <class F>
+  __device__ void each(F f) const {
+    constexpr int kBatch = 8;
+    for (int j0 = threadIdx.x; j0 < n; j0 += kBatch * kSelThreads) {
+      float v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; k++) {
+        const int j = j0 + k * kSelThreads;
+        v[k] = row[j < n ? j : j0];
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; k++)
+        if (j0 + k * kSelThreads < n) f(v[k]);
+    }
+  }
+};
+struct GlobalRow {
+  const float* row;
+  int n;
+  template <class F>
+  __device__ void each(F f) const {
+    for (int j = threadIdx.x; j < n; j += kSelThreads) f(row[j]);
+  }
+};
+
+// One level of the selection: `cls(s)` gives an element's digit (0..255,
+// larger digits earlier in the selection order) or -1 when the element is
+// not a candidate of this level.  Builds the digit histogram (counts, and
 // integer weights when `by_weight`), then walks the digits from the largest
 // down and returns the digit at which the running total (weight, else
 // count) first reaches `need`; *above_c / *above_w get the count and weight
-// of the keys of that prefix with a larger digit.  Keys are ordered like
-// the scores they encode, so "larger digit" is "earlier in the selection
-// order".
-__device__ int radix_level(const float* row, int n, float smax, uint32_t prefix, int shift,
-                           bool by_weight, unsigned long long need, SelShared& S,
-                           uint32_t* above_c, unsigned long long* above_w,
-                           unsigned long long p32 = 0) {
+// of the candidates with a larger digit.  The row is visited through `src`
+// (LdsRow or GlobalRow).
+template <class Src, class Cls>
+__device__ int select_level(const Src& src, Cls cls, float smax, bool by_weight,
+                            unsigned long long need, SelShared& S, uint32_t* above_c,
+                            unsigned long long* above_w, unsigned long long p32 = 0) {
   const int wv = threadIdx.x >> 6;
   for (int b = threadIdx.x; b < (kSelThreads / 64) * 256; b += blockDim.x) {
     (&S.cnt[0][0])[b] = 0;
     (&S.wt[0][0])[b] = 0ull;
   }
   __syncthreads();
-  const uint32_t hmask = shift >= 24 ? 0u : (0xffffffffu << (shift + 8));
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
-    const float s = row[j];
-    const uint32_t key = f2key(s);
-    if ((key & hmask) == prefix) {
-      const int d = (key >> shift) & 0xff;
+  src.each([&](float s) {
+    const int d = cls(s);
+    if (d >= 0) {
       atomicAdd(&S.cnt[wv][d], 1u);
       if (by_weight) atomicAdd(&S.wt[wv][d], (unsigned long long)weight_of(s, smax));
     }
-  }
+  });
   __syncthreads();
-  // thread t owns digit 255 - t: an inclusive scan in selection order
-  const int d = 255 - (int)threadIdx.x;
-  uint32_t c = 0;
-  unsigned long long w = 0;
-  if (threadIdx.x < 256) {
+  // one wave picks the digit: lane l owns digits 255 - 4l - q (q = 0..3,
+  // selection order), one wave scan of its count and weight totals gives
+  // every digit's running totals
+  if (wv == 0) {
+    const int lane = threadIdx.x & 63;
+    unsigned long long c[4], w[4], sc = 0, sw = 0;
 #pragma unroll
-    for (int q = 0; q < kSelThreads / 64; q++) {
-      c += S.cnt[q][d];
-      w += S.wt[q][d];
+    for (int q = 0; q < 4; q++) {
+      const int d = 255 - 4 * lane - q;
+      c[q] = 0;
+      w[q] = 0;
+#pragma unroll
+      for (int k = 0; k < kSelThreads / 64; k++) {
+        c[q] += S.cnt[k][d];
+        w[q] += S.wt[k][d];
+      }
+      sc += c[q];
+      sw += w[q];
+    }
+    unsigned long long ic = sc, iw = sw;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned long long uc = __shfl_up(ic, off, 64), uw = __shfl_up(iw, off, 64);
+      if (lane >= off) {
+        ic += uc;
+        iw += uw;
+      }
+    }
+    if (p32) {
+      // first level of the Top-p select: the histogram total is the row's
+      // weight Z, and the target W* = ceil(p32 Z / 2^32) (no overflow: p32 <= 2^32)
+      const unsigned long long Z = __shfl(iw, 63, 64);
+      const unsigned long long zh = Z >> 32, zl = Z & 0xffffffffull;
+      need = p32 * zh + ((p32 * zl + 0xffffffffull) >> 32);
+      if (lane == 0) S.wstar = need;
+    }
+    // running totals before this lane's first digit; the crossing digit is
+    // the first whose running total reaches `need` (if none does, digit 0)
+    unsigned long long rc = ic - sc, rw = iw - sw;
+    int pick = -1;
+    unsigned long long pc = 0, pw = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const unsigned long long before = by_weight ? rw : rc;
+      const unsigned long long m = by_weight ? w[q] : c[q];
+      if (pick < 0 && before < need && before + m >= need) {
+        pick = 255 - 4 * lane - q;
+        pc = rc;
+        pw = rw;
+      }
+      rc += c[q];
+      rw += w[q];
+    }
+    const bool found = __ballot(pick >= 0) != 0ull;
+    if (lane == 63 && !found) {
+      pick = 0;
+      pc = rc - c[3];
+      pw = rw - w[3];
+    }
+    if (pick >= 0) {
+      S.pick = pick;
+      S.red64[0] = pc;
+      S.red64[1] = pw;
     }
   }
-  const unsigned long long mine = by_weight ? w : (unsigned long long)c;
-  if (threadIdx.x == 0) S.pick = 255;
-  const unsigned long long incl = block_incl_scan(mine, S.red64);
-  if (p32) {
-    // first level of the Top-p select: the histogram total is the row's
-    // weight Z, and the target W* = ceil(p32 Z / 2^32) (no overflow: p32 <= 2^32)
-    if (threadIdx.x == kSelThreads - 1) S.red64[0] = incl;
-    __syncthreads();
-    const unsigned long long Z = S.red64[0];
-    const unsigned long long zh = Z >> 32, zl = Z & 0xffffffffull;
-    need = p32 * zh + ((p32 * zl + 0xffffffffull) >> 32);
-    if (threadIdx.x == 0) S.wstar = need;
-    __syncthreads();
-  }
-  if (threadIdx.x < 256 && incl >= need && incl - mine < need) S.pick = threadIdx.x;
   __syncthreads();
-  const int t = S.pick;
-  // count and weight above the chosen digit: a second scan of the counts
-  const unsigned long long incl_c = block_incl_scan(c, S.red64);
-  const unsigned long long incl_w = by_weight ? block_incl_scan(w, S.red64) : 0ull;
-  if ((int)threadIdx.x == t) {
-    S.red64[0] = incl_c - c;
-    S.red64[1] = incl_w - w;
-  }
-  __syncthreads();
+  const int d = S.pick;
   *above_c = (uint32_t)S.red64[0];
-  *above_w = S.red64[1];
+  *above_w = by_weight ? S.red64[1] : 0ull;
   __syncthreads();
-  return 255 - t;
+  return d;
 }
 
-// Full radix select: the key K of the element at which the running total in
-// selection order first reaches `need`, with the count and weight of the
-// elements whose key is larger.
-// With p32 != 0 the target is the Top-p weight W* of the row, formed from
-// the first level's total; it is returned in *need_out.
-__device__ uint32_t radix_select(const float* row, int n, float smax, bool by_weight,
+// Exact select: the order key K of the element at which the running total in
+// selection order (score descending) first reaches `need`, with the count
+// and weight of the elements whose key is larger.  The levels take the
+// order keys relative to the row's smallest key, 8 bits at a time from the
+// top of the row's key range (rel = key - kmin orders the elements like the
+// keys; a row's scores lie in a narrow range, so the top bytes of the raw
+// keys would be one or two values, every level's histogram one or two bins,
+// and its LDS atomics would serialise).  With p32 != 0 the target is the
+// Top-p weight W* of the row, formed from the first level's total; it is
+// returned in *need_out.
+template <class Src>
+__device__ uint32_t exact_select(const Src& src, float smax, float smin, bool by_weight,
                                  unsigned long long need, SelShared& S, uint32_t* above_c,
                                  unsigned long long* above_w, unsigned long long p32 = 0,
                                  unsigned long long* need_out = nullptr) {
+  const uint32_t kmin = f2key(smin);
+  const uint32_t span = f2key(smax) - kmin;
   uint32_t prefix = 0, ac = 0;
   unsigned long long aw = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  bool first = true;
+  // (a row of equal keys still takes one level, which forms W*)
+  for (int hi = span ? 32 - __builtin_clz(span) : 1; hi > 0;) {
+    const int lo = hi > 8 ? hi - 8 : 0;
+    const uint64_t pre = (uint64_t)prefix >> hi;
+    const uint32_t dmask = (1u << (hi - lo)) - 1u;
     uint32_t c;
     unsigned long long w;
     const unsigned long long rest = need - (by_weight ? aw : (unsigned long long)ac);
-    const int d = radix_level(row, n, smax, prefix, shift, by_weight, rest, S, &c, &w,
-                              shift == 24 ? p32 : 0ull);
-    if (shift == 24 && p32) need = S.wstar;
-    prefix |= (uint32_t)d << shift;
+    const int d = select_level(
+        src,
+        [&](float s) {
+          const uint32_t rel = f2key(s) - kmin;
+          return ((uint64_t)rel >> hi) == pre ? (int)((rel >> lo) & dmask) : -1;
+        },
+        smax, by_weight, rest, S, &c, &w, first ? p32 : 0ull);
+    if (first && p32) need = S.wstar;
+    first = false;
+    prefix |= (uint32_t)d << lo;
     ac += c;
     aw += w;
+    hi = lo;
   }
   if (need_out) *need_out = need;
   *above_c = ac;
   *above_w = aw;
-  return prefix;
+  return kmin + prefix;
 }
 
 // Per query block row: count of selected key blocks, the threshold key and
@@ -794,20 +879,45 @@ __global__ __launch_bounds__(kSelThreads) void k_select_count(
     return;
   }
   // the row is read from HBM once: into LDS (n floats of dynamic shared
-  // memory) when it fits, and every later pass runs over that copy
+  // memory) when it fits, and every later pass runs over that copy; longer
+  // rows are read from HBM on every pass
   const float* grow = scores + (int64_t)i * n;
   extern __shared__ __attribute__((aligned(16))) float srow_dyn[];
   if (kLds) stage_row(grow, n, srow_dyn);
-  const float* row = kLds ? (const float*)srow_dyn : grow;
-  float mx = -INFINITY;
-  for (int j = threadIdx.x; j < n; j += blockDim.x) mx = fmaxf(mx, row[j]);
+  const LdsRow rr{srow_dyn, n};
+  const GlobalRow gr{grow, n};
+  // the row's maximum and minimum
+  float mx = -INFINITY, mn = INFINITY;
+  auto minmax = [&](float s) {
+    mx = fmaxf(mx, s);
+    mn = fminf(mn, s);
+  };
+  if (kLds)
+    rr.each(minmax);
+  else
+    gr.each(minmax);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if ((threadIdx.x & 63) == 0) S.redf[threadIdx.x >> 6] = mx;
+  for (int off = 32; off >= 1; off >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    mn = fminf(mn, __shfl_xor(mn, off, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    S.redf[threadIdx.x >> 6] = mx;
+    S.redn[threadIdx.x >> 6] = mn;
+  }
   __syncthreads();
-  float smax = S.redf[0];
-  for (int w = 1; w < kSelThreads / 64; w++) smax = fmaxf(smax, S.redf[w]);
+  float smax = S.redf[0], smin = S.redn[0];
+  for (int w = 1; w < kSelThreads / 64; w++) {
+    smax = fmaxf(smax, S.redf[w]);
+    smin = fminf(smin, S.redn[w]);
+  }
   __syncthreads();
+  auto select = [&](bool by_weight, unsigned long long need, uint32_t* ac,
+                    unsigned long long* aw, unsigned long long p32,
+                    unsigned long long* need_out) {
+    return kLds ? exact_select(rr, smax, smin, by_weight, need, S, ac, aw, p32, need_out)
+                : exact_select(gr, smax, smin, by_weight, need, S, ac, aw, p32, need_out);
+  };
 
   int64_t L = 0;
   uint32_t keyP = 0, caP = 0;
@@ -815,7 +925,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_count(
     // W* = ceil(ceil(p 2^32) Z / 2^32) with Z the row's total weight
     const unsigned long long P32 = (unsigned long long)ceil((double)p * 4294967296.0);
     unsigned long long wa, Wstar;
-    keyP = radix_select(row, n, smax, true, 0ull, S, &caP, &wa, P32, &Wstar);
+    keyP = select(true, 0ull, &caP, &wa, P32, &Wstar);
     const unsigned long long wk = weight_of(key2f(keyP), smax);
     L = (int64_t)caP + (int64_t)((Wstar - wa + wk - 1) / wk);
   }
@@ -830,7 +940,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_count(
   } else if (nsel > 0) {
     uint32_t ca;
     unsigned long long wa;
-    keyL = radix_select(row, n, smax, false, (unsigned long long)nsel, S, &ca, &wa);
+    keyL = select(false, (unsigned long long)nsel, &ca, &wa, 0ull, nullptr);
     tieL = nsel - (int64_t)ca;
   }
   if (threadIdx.x == 0) {
@@ -911,7 +1021,21 @@ __global__ __launch_bounds__(kSelThreads) void k_select_fill(
   const int i = blockIdx.x;
   const int64_t g = g0 + i;
   const float* grow = scores + (int64_t)i * n;
-  if (kLds) stage_row(grow, n, srow_dyn);
+  // the head's shape ids (key blocks g0 .. g0 + n - 1) follow the row in
+  // LDS: the aligned words that cover them, moved in the same wait
+  const uint8_t* sshape = nullptr;
+  if (kLds) {
+    const int64_t w0 = g0 >> 2;
+    const int nw = (int)(((g0 + n + 3) >> 2) - w0);
+    uint32_t* dst = (uint32_t*)(srow_dyn + sel_row_floats(n));
+    const __amdgpu_buffer_rsrc_t rs = buffer_of(blk_shape + w0 * 4, (uint32_t)nw * 4u);
+    const uint32_t o = lds_offset(dst);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    for (int j0 = wv * 64; j0 < nw; j0 += kSelThreads)
+      dma4(rs, (uint32_t)(j0 + lane) * 4u, o + (uint32_t)j0 * 4u);
+    sshape = (const uint8_t*)dst + (g0 & 3);
+    stage_row(grow, n, srow_dyn);
+  }
   const float* row = kLds ? (const float*)srow_dyn : grow;
   const uint32_t K = row_key[g];
   const int tie = row_tie[g];
@@ -941,7 +1065,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_fill(
       if (sel) {
         nsel++;
         selm |= 1ull << e;
-        cost += d_shapes[block_shape_at(blk_shape, g0 + j0 + e)].volume;
+        cost += volume_of_id(sshape[j0 + e]);
       }
     }
     int pos = block_excl_scan_i32(nsel, sh, &total);
@@ -967,7 +1091,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_fill(
       t += key == K;
       if (sel) {
         nsel++;
-        cost += d_shapes[block_shape_at(blk_shape, g0 + j)].volume;
+        cost += volume_of_id(block_shape_at(blk_shape, g0 + j));
       }
     }
     int pos = block_excl_scan_i32(nsel, sh, &total);
@@ -990,7 +1114,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_fill(
 // row walks the row's sorted list with coalesced reads; LDS atomic ORs set
 // the bits).  The counting pass stores popcounts per (row tile, column); the
 // fill pass rebuilds the masks and writes each column's rows in ascending
-// order at its offset.  No global atomics, and the result does not depend on
+// order at its offset, one column per store instruction of a wave.  No global atomics, and the result does not depend on
 // the order of the ORs.
 constexpr int kTrRows = 64;
 constexpr int kTrCols = 256;
@@ -1003,6 +1127,7 @@ __global__ __launch_bounds__(kTrCols) void k_colt_tiles(
     int32_t* __restrict__ colt_idx) {
   __shared__ int64_t cur[kTrRows], fin[kTrRows];
   __shared__ unsigned long long mask[kTrCols];
+  __shared__ int64_t cpos[kTrCols];
   const int rt = blockIdx.x;
   const int i0 = rt * kTrRows, nrows = min(kTrRows, n - i0);
   const int c0 = blockIdx.y * kTrPart, c1 = min(n, c0 + kTrPart);
@@ -1042,16 +1167,18 @@ __global__ __launch_bounds__(kTrCols) void k_colt_tiles(
     }
     __syncthreads();
     const int col = t0 + threadIdx.x;
-    if (col < t1) {
-      unsigned long long m = mask[threadIdx.x];
-      if (!kFill) {
-        tile_cnt[(int64_t)rt * n + col] = __popcll(m);
-      } else {
-        int64_t pos = colt_ptr[g0 + col] + tile_cnt[(int64_t)rt * n + col];
-        while (m) {
-          colt_idx[pos++] = i0 + __builtin_ctzll(m);
-          m &= m - 1;
-        }
+    if (!kFill) {
+      if (col < t1) tile_cnt[(int64_t)rt * n + col] = __popcll(mask[threadIdx.x]);
+    } else {
+      // each column's rows go out as one store of a wave: lane r writes row
+      // i0 + r at its rank among the column's rows, so a column's run is
+      // written by consecutive lanes to consecutive addresses
+      if (col < t1) cpos[threadIdx.x] = colt_ptr[g0 + col] + tile_cnt[(int64_t)rt * n + col];
+      __syncthreads();
+      for (int cc = wv; cc < t1 - t0; cc += kTrCols / 64) {
+        const unsigned long long m = mask[cc];
+        if ((m >> lane) & 1ull)
+          colt_idx[cpos[cc] + __popcll(m & ((1ull << lane) - 1ull))] = i0 + lane;
       }
     }
     __syncthreads();
@@ -1190,7 +1317,11 @@ bool launch_block_scores(const PlanDev& P, int64_t g0, int n, float* out, hipStr
 
 // dynamic LDS of the staged row: n floats, rounded up to whole 64-float
 // pieces of the staging loads
-static unsigned sel_lds_bytes(int n) { return (unsigned)((n + 63) / 64 * 64 * 4); }
+static unsigned sel_lds_bytes(int n) { return (unsigned)(sel_row_floats(n) * 4); }
+// the fill kernel also stages the words that cover the head's n shape ids
+static unsigned sel_fill_lds_bytes(int n) {
+  return sel_lds_bytes(n) + (unsigned)(((n + 3) / 4 + 1 + 63) / 64 * 64 * 4);
+}
 
 bool launch_select(const PlanDev& P, int64_t g0, int n, const prism_config& c, int last,
                    hipStream_t st) {
@@ -1208,7 +1339,8 @@ bool launch_select(const PlanDev& P, int64_t g0, int n, const prism_config& c, i
                      P.counters, last);
   if (n > 0) {
     if (lds)
-      hipLaunchKernelGGL(k_select_fill<true>, dim3(n), dim3(kSelThreads), sel_lds_bytes(n), st,
+      hipLaunchKernelGGL(k_select_fill<true>, dim3(n), dim3(kSelThreads), sel_fill_lds_bytes(n),
+                         st,
                          P.scores, n, g0, P.row_cnt, P.row_key, P.row_tie, P.row_ptr, P.cap,
                          P.blk_shape, P.col_idx, P.row_cost);
     else
