@@ -71,6 +71,85 @@ def read_traffic(stage, workload):
     return float(vals["traffic_bytes_per_launch"])
 
 
+def _kernel_rows(path, counter):
+    """{kernel name: [(counter value, duration s), ...]} of a counter-collection CSV."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        key = "bitwise_not" if "bitwise_not" in name else name.split("(")[0].replace("void ", "")
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        out.setdefault(key, []).append((float(r["Counter_Value"]), dur))
+    return out
+
+
+def summarize_hbm_table(fetch_csv, write_csv, workload, cmds, out):
+    """Measured HBM traffic and rate of every library kernel in the two
+    counter passes (KiB per dispatch, calibrated by the copy)."""
+    f = _kernel_rows(fetch_csv, "FETCH_SIZE")
+    w = _kernel_rows(write_csv, "WRITE_SIZE")
+    fs = CALIB_BYTES / (f["bitwise_not"][0][0] * 1024)
+    ws = CALIB_BYTES / (w["bitwise_not"][0][0] * 1024)
+    lines = [f"# HBM traffic and rate of every kernel, {workload}", "",
+             "Same two counter passes as the dominant kernel's traffic summary "
+             f"(`FETCH_SIZE` x {fs:.4f}, `WRITE_SIZE` x {ws:.4f}, from the 1 GiB calibration "
+             "copy).  Durations are the profiled dispatches' own (counter collection "
+             "serialises dispatches); rates against the 8 TB/s HBM3E peak.", "",
+             "Commands (from /tmp, TMPDIR=/tmp):", "", *[f"    {c}" for c in cmds], "",
+             "| kernel | dispatches | time ms | fetch GB | write GB | TB/s | % of 8 TB/s |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    keys = [k for k in f if k.startswith("prism::")]
+    for k in sorted(keys, key=lambda k: -sum(d for _, d in f[k])):
+        t = sum(d for _, d in f[k])
+        fb = sum(v for v, _ in f[k]) * 1024 * fs
+        wb = sum(v for v, _ in w.get(k, [])) * 1024 * ws
+        rate = (fb + wb) / t / 1e12 if t > 0 else 0.0
+        lines.append(f"| `{k[7:]}` | {len(f[k])} | {t * 1e3:.2f} | {fb / 1e9:.2f} | "
+                     f"{wb / 1e9:.2f} | {rate:.2f} | {100 * rate / 8:.1f} |")
+    lines.append("")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def summarize_mfma(csv_path, agent_csv, workload, cmds, out):
+    """MFMA utilisation of the attention kernels from one counter pass of
+    SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16."""
+    import csv
+    busy = _kernel_rows(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = _kernel_rows(csv_path, "GRBM_GUI_ACTIVE")
+    mops = _kernel_rows(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    gpu = next(r for r in csv.DictReader(open(agent_csv)) if r.get("Simd_Count", "0") != "0")
+    simds, xcc = int(gpu["Simd_Count"]), int(gpu["Num_Xcc"])
+    lines = [f"# MFMA utilisation of the attention kernels, {workload}", "",
+             "One counter pass over a profiled step: `SQ_VALU_MFMA_BUSY_CYCLES` (summed over "
+             f"the {simds} SIMDs), `GRBM_GUI_ACTIVE` (busy cycles, summed over the {xcc} XCDs) "
+             "and `SQ_INSTS_VALU_MFMA_MOPS_BF16` (x 512 = bf16 MFMA flops).  Utilisation = "
+             f"busy / (active / {xcc} x {simds}), rocprofv3's MfmaUtil, i.e. against the "
+             "clock the chip actually ran; the clock is active / XCDs / duration.  The "
+             "bench line's fractions are against 2.5 PFLOP/s, the peak at 2.4 GHz.", "",
+             "Command (from /tmp, TMPDIR=/tmp):", "", *[f"    {c}" for c in cmds], "",
+             "| kernel | s | clock GHz | MFMA busy % | MFMA TFLOP/s (counted) | % of 2.5 PFLOP/s |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for stage, (sym, _) in KERNELS.items():
+        k = next((n for n in busy if sym in n), None)
+        if k is None:
+            continue
+        b = sum(v for v, _ in busy[k])
+        t = sum(d for _, d in busy[k])
+        g = sum(v for v, _ in gui[k]) / xcc
+        fl = sum(v for v, _ in mops[k]) * 512
+        lines.append(f"| `{sym}` ({stage}) | {t:.2f} | {g / t / 1e9:.2f} | "
+                     f"{100 * b / (g * simds):.1f} | {fl / t / 1e12:.1f} | "
+                     f"{100 * fl / t / 1e12 / PEAK_BF16_TFLOPS:.1f} |")
+    lines.append("")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def summarize_pmc(fetch_csv, write_csv, stage, workload, cmds, out):
     """Turns two rocprofv3 counter-collection CSVs (FETCH_SIZE, WRITE_SIZE,
     in KiB per dispatch) of a profiled step that ends with the calibration
@@ -139,6 +218,9 @@ def parse():
                     help="write the traffic summary of the dominant kernel from two "
                          "rocprofv3 counter-collection CSVs, then exit")
     ap.add_argument("--stage", default="bwd.dkdv", help="kernel stage for --summarize-pmc")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_CSV", "AGENT_CSV"),
+                    help="write the attention kernels' MFMA utilisation summary from one "
+                         "rocprofv3 counter pass (and its agent info), then exit")
     ap.add_argument("--cmd", action="append", default=[],
                     help="profiling command lines to record in the summary")
     return ap.parse_args()
@@ -187,6 +269,12 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.stage, args.workload, args.cmd,
                       traffic_file(args.stage, args.workload))
+        summarize_hbm_table(*args.summarize_pmc, args.workload, args.cmd,
+                            os.path.join(ROOT, "profiles", f"kernels_{args.workload}_hbm.md"))
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, args.workload, args.cmd,
+                       os.path.join(ROOT, "profiles", f"attention_{args.workload}_mfma.md"))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "

@@ -54,3 +54,48 @@ def test_summary_needs_exactly_one_calibration_copy(tmp_path):
 def test_missing_summary_reports_none(monkeypatch, tmp_path):
     monkeypatch.setattr(bench, "traffic_file", lambda stage, workload: str(tmp_path / "none.md"))
     assert bench.read_traffic("bwd.dkdv", "wl") is None
+
+
+def _write_rows(path, rows):
+    fields = ["Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(fields, r)))
+
+
+def test_hbm_table_rates(tmp_path):
+    gib_kib = (1 << 30) / 1024
+    # a kernel fetching 1 GB (its counter reads half) and writing 1 GB in 1 s
+    _write_rows(tmp_path / "f.csv", [
+        ("prism::k_x(int)", "FETCH_SIZE", 1e9 / 1024 / 2, 0, 10**9),
+        ("void at::native::bitwise_not_kernel", "FETCH_SIZE", gib_kib / 2, 0, 10**6)])
+    _write_rows(tmp_path / "w.csv", [
+        ("prism::k_x(int)", "WRITE_SIZE", 1e9 / 1024, 0, 10**9),
+        ("void at::native::bitwise_not_kernel", "WRITE_SIZE", gib_kib, 0, 10**6)])
+    out = tmp_path / "t.md"
+    bench.summarize_hbm_table(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "wl", [], str(out))
+    row = [l for l in out.read_text().splitlines() if l.startswith("| `k_x`")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    # time 1000 ms, fetch and write 1.00 GB each, 0.002 TB/s
+    assert float(cells[2]) == pytest.approx(1000.0)
+    assert cells[3] == "1.00" and cells[4] == "1.00" and cells[5] == "0.00"
+
+
+def test_mfma_summary_uses_the_xcd_count(tmp_path):
+    # 2 s at 2 GHz on 8 XCDs; half of 1024 SIMDs' cycles busy
+    t = 2 * 10**9
+    gui = 2.0e9 * 2 * 8
+    busy = 0.5 * 2.0e9 * 2 * 1024
+    _write_rows(tmp_path / "m.csv", [
+        ("prism::k_attn_fwd_bf16(x)", "SQ_VALU_MFMA_BUSY_CYCLES", busy, 0, t),
+        ("prism::k_attn_fwd_bf16(x)", "GRBM_GUI_ACTIVE", gui, 0, t),
+        ("prism::k_attn_fwd_bf16(x)", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e15 / 512, 0, t)])
+    with open(tmp_path / "a.csv", "w") as f:
+        f.write("Simd_Count,Num_Xcc\n0,0\n1024,8\n")
+    out = tmp_path / "m.md"
+    bench.summarize_mfma(str(tmp_path / "m.csv"), str(tmp_path / "a.csv"), "wl", [], str(out))
+    row = [l for l in out.read_text().splitlines() if "k_attn_fwd_bf16" in l][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[2] == "2.00" and cells[3] == "50.0" and cells[4] == "500.0"
