@@ -35,6 +35,9 @@ __host__ __device__ constexpr int wait_vm(int n) {
   return 0x0F70 | (n & 15) | ((n >> 4) << 14);
 }
 
+// s_waitcnt immediate for lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+constexpr int kWaitLgkm0 = 0xC07F;
+
 // LDS byte offset of a shared-memory object, opaque to alias analysis
 __device__ inline uint32_t lds_offset(const void* p) {
   return __builtin_amdgcn_readfirstlane(

@@ -99,6 +99,34 @@ __global__ __launch_bounds__(64) void k_zone_stats(const void* __restrict__ v, i
   RowVal<DT, CPL> cur[64], nxt[64];
   float PH[8][CPL], PW[8][CPL], sv[CPL], within[CPL];
 
+  // bf16 with 128 channels: a frame's 64 token rows (256 B each) travel
+  // HBM -> LDS as 16 direct loads of 1 KB (16 B per lane, four rows per
+  // load), two frames in flight; each lane then reads its two channels of
+  // every row back from LDS.  Other layouts load each row straight into
+  // registers, 4 or 8 B per lane.
+  constexpr bool kDma = DT == 1 && CPL == 2;
+  __shared__ __attribute__((aligned(16))) uint32_t sbuf[kDma ? 2 : 1][64][64];
+  const __amdgpu_buffer_rsrc_t rsv =
+      buffer_of((const uint16_t*)v + (int64_t)h * N * D, (uint32_t)(N * D * 2));
+  const uint32_t lbuf = lds_offset(sbuf);
+  auto row_of = [&](int t, int r) {  // token of row r (y = r / 8, w = r % 8) of frame t
+    return ((int64_t)((mt << 3) + t) * H + ((mh << 3) + (r >> 3))) * W + (mw << 3) + (r & 7);
+  };
+  auto stage = [&](int t) {  // frame t into buffer t % 2
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int r = 4 * i + (lane >> 4);
+      dma16(rsv, (uint32_t)(row_of(t, r) * D * 2 + (lane & 15) * 16),
+            lbuf + (uint32_t)((t & 1) * 16384 + i * 1024));
+    }
+  };
+  auto read_slice = [&](int t, RowVal<DT, CPL>* dst) {
+    if constexpr (kDma) {
+#pragma unroll
+      for (int r = 0; r < 64; r++) dst[r].v = sbuf[t & 1][r][lane];
+    }
+  };
+
   auto load_slice = [&](int t, RowVal<DT, CPL>* dst) {
 #pragma unroll
     for (int y = 0; y < 8; y++) {
@@ -108,11 +136,28 @@ __global__ __launch_bounds__(64) void k_zone_stats(const void* __restrict__ v, i
     }
   };
 
-  load_slice(0, cur);
+  if constexpr (kDma) {
+    stage(0);
+    stage(1);
+    __builtin_amdgcn_s_waitcnt(wait_vm(16));
+    asm volatile("" ::: "memory");
+    read_slice(0, cur);
+  } else {
+    load_slice(0, cur);
+  }
 #pragma unroll 1
   for (int t = 0; t < 8; t++) {
     const bool more = t < 7;
-    if (more) load_slice(t + 1, nxt);
+    if constexpr (kDma) {
+      // frame t's buffer is free once its reads have landed: it takes frame t + 2
+      if (t + 2 < 8) {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        asm volatile("" ::: "memory");
+        stage(t + 2);
+      }
+    } else {
+      if (more) load_slice(t + 1, nxt);
+    }
 #pragma unroll
     for (int k = 0; k < CPL; k++) {
       float Lw[8], Cy[8];
@@ -150,6 +195,17 @@ __global__ __launch_bounds__(64) void k_zone_stats(const void* __restrict__ v, i
       sv[k] = (t == 0) ? vt : sv[k] + vt;
       // frame difference t -> t+1
       if (more) {
+        if constexpr (kDma) {
+          if (k == 0) {
+            // frame t + 1 has landed (frame t + 2 may still be in flight)
+            if (t + 2 < 8)
+              __builtin_amdgcn_s_waitcnt(wait_vm(16));
+            else
+              __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            asm volatile("" ::: "memory");
+            read_slice(t + 1, nxt);
+          }
+        }
         float s = nxt[0].get(k) - cur[0].get(k);
 #pragma unroll
         for (int i = 1; i < 64; i++) s = s + (nxt[i].get(k) - cur[i].get(k));
