@@ -13,7 +13,9 @@
 //    Q and dO tiles with their LSE and Delta columns stream through a 4-slot
 //    LDS ring; per 32-query slice it forms S = Q K^T and dP = dO V^T, then
 //    dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by
-//    ds_read_b64_tr_b16;
+//    ds_read_b64_tr_b16.  One wave per SIMD: a tile's 64 MFMAs run in a
+//    fixed, fenced order with each fragment read a few MFMAs ahead and the
+//    dS arithmetic of one slice under the products of the other;
 //  * dQ: a work-group owns 256 permuted query rows (8 waves) and walks its
 //    key blocks as the forward does: S^T = K Q^T, dP^T = V dO^T,
 //    dQ^T += K^T dS^T.
@@ -187,73 +189,81 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
     const char* sd = sq + kTile;                            // dO tile
     const float* sl = ringc + (j & (kRing - 1)) * 128;      // log2(e) LSE
     const float* sdl = sl + 64;                             // Delta
-    // Two 32-query halves per tile, software-pipelined: the S and dP products
-    // of the second half are issued between the softmax of the first half
-    // and its dV/dK products, so one wave has independent MFMA and VALU work
-    // at hand.
+    // The tile's 64 MFMAs in a fixed order, one per slot:
+    //   ops  0..15  S = Q K^T and dP = dO V^T of query half 0 (alternating)
+    //   ops 16..31  the same for half 1, while half 0's dS is formed
+    //   ops 32..47  dV^T += dO^T P, dK^T += Q^T dS of half 0, while half 1's
+    //               dS is formed
+    //   ops 48..63  the same for half 1.
+    // Each op's fragment is read kWin slots ahead, and a scheduling fence
+    // closes every slot, so LDS latency and the VALU work hide under the
+    // MFMAs already issued.
+    constexpr int kWin = 6;
+    auto frag = [&](int t) -> bf16x8 {
+      if (t < 32) {
+        const char* base = (t & 1) ? sd : sq;
+        return ld_frag(base + (t >> 4) * 8192 + ro[(t & 15) >> 1]);
+      }
+      const int u = t - 32, cc = ((u >> 4) * 2 + ((u & 15) >> 3)) * 4096, db = (u & 7) >> 1;
+      const char* base = (t & 1) ? sq : sd;
+      return ld_tfrag(base + cc + to[db][0], base + cc + to[db][1]);
+    };
     f32x16 s[2], dp[2];
-    auto sdp = [&](int qb) {  // S = Q K^T, dP = dO V^T of half qb
-      // all sixteen fragments first, so that their reads overlap
+    uint32_t pp[2][8], ps[2][8];
+    f32x4 Lc[2][4], Dc[2][4];
+    float pv_prev = 0.0f, sv_prev = 0.0f;
+    bf16x8 win[kWin];
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        s[qb][r] = 0.0f;
-        dp[qb][r] = 0.0f;
+    for (int t = 0; t < kWin; t++) win[t] = frag(t);
+    auto slot = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      const bf16x8 f = win[t % kWin];
+      if constexpr (t + kWin < 64) win[t % kWin] = frag(t + kWin);
+      if constexpr (t >= 12 && t < 44 && (t & 3) == 0) {
+        // the LSE and Delta values of the dS rows formed four slots on
+        constexpr int qb = (t - 12) >> 4, jj = ((t - 12) & 15) >> 2;
+        Lc[qb][jj] = *(const f32x4*)(sl + 32 * qb + 8 * jj + 4 * hl);
+        Dc[qb][jj] = *(const f32x4*)(sdl + 32 * qb + 8 * jj + 4 * hl);
       }
-      bf16x8 fa[8], fb[8];
-#pragma unroll
-      for (int kk = 0; kk < 8; kk++) {
-        fa[kk] = ld_frag(sq + qb * 8192 + ro[kk]);
-        fb[kk] = ld_frag(sd + qb * 8192 + ro[kk]);
+      if constexpr (t < 32) {
+        constexpr int qb = t >> 4, kk = (t & 15) >> 1;
+        if constexpr (t & 1)
+          dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, vr[kk], kk ? dp[qb] : f32x16{}, 0,
+                                                           0, 0);
+        else
+          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, kr[kk], kk ? s[qb] : f32x16{}, 0, 0,
+                                                          0);
+      } else {
+        constexpr int u = t - 32, qb = u >> 4, c = (u & 15) >> 3, db = (u & 7) >> 1;
+        if constexpr (t & 1) {
+          const bf16x8 bs = __builtin_bit_cast(
+              bf16x8, make_uint4(ps[qb][4 * c], ps[qb][4 * c + 1], ps[qb][4 * c + 2],
+                                 ps[qb][4 * c + 3]));
+          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, bs, dkt[db], 0, 0, 0);
+        } else {
+          const bf16x8 bp = __builtin_bit_cast(
+              bf16x8, make_uint4(pp[qb][4 * c], pp[qb][4 * c + 1], pp[qb][4 * c + 2],
+                                 pp[qb][4 * c + 3]));
+          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, bp, dvt[db], 0, 0, 0);
+        }
       }
-#pragma unroll
-      for (int kk = 0; kk < 8; kk++) {
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk], kr[kk], s[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk], vr[kk], dp[qb], 0, 0, 0);
+      if constexpr (t >= 16 && t < 48) {
+        // one element of the dS of the half whose S and dP are complete:
+        // row q = 32qb + 8jj + 4hl + i of this lane, r = 4jj + i
+        constexpr int qb = (t - 16) >> 4, r = (t - 16) & 15, jj = r >> 2, i = r & 3;
+        const float pv =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c_log2, -Lc[qb][jj][i]));
+        const float sv = pv * (dp[qb][r] - Dc[qb][jj][i]);
+        if constexpr (r & 1) {
+          pp[qb][r >> 1] = pk2(pv_prev, pv);
+          ps[qb][r >> 1] = pk2(sv_prev, sv);
+        }
+        pv_prev = pv;
+        sv_prev = sv;
       }
+      __builtin_amdgcn_sched_barrier(0);
     };
-    // dS = P (dP - Delta); dV^T += dO^T P, dK^T += Q^T dS for half qb
-    auto rest = [&](int qb, bool next) {
-      // rows of s/dp held by this lane: q = 32qb + 8jj + 4hl + i (r = 4jj + i)
-      uint32_t pp[8], ps[8];
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const f32x4 Lv = *(const f32x4*)(sl + 32 * qb + 8 * jj + 4 * hl);
-        const f32x4 Dv = *(const f32x4*)(sdl + 32 * qb + 8 * jj + 4 * hl);
-        float pv[4], sv[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][4 * jj + i], c_log2, -Lv[i]));
-          sv[i] = pv[i] * (dp[qb][4 * jj + i] - Dv[i]);
-        }
-        pp[2 * jj] = pk2(pv[0], pv[1]);
-        pp[2 * jj + 1] = pk2(pv[2], pv[3]);
-        ps[2 * jj] = pk2(sv[0], sv[1]);
-        ps[2 * jj + 1] = pk2(sv[2], sv[3]);
-      }
-      if (next) sdp(1);
-#pragma unroll
-      for (int c = 0; c < 2; c++) {
-        const bf16x8 bp = __builtin_bit_cast(
-            bf16x8, make_uint4(pp[4 * c], pp[4 * c + 1], pp[4 * c + 2], pp[4 * c + 3]));
-        const bf16x8 bs = __builtin_bit_cast(
-            bf16x8, make_uint4(ps[4 * c], ps[4 * c + 1], ps[4 * c + 2], ps[4 * c + 3]));
-        const int cc = (2 * qb + c) * 4096;
-        bf16x8 ta[4], tb[4];
-#pragma unroll
-        for (int db = 0; db < 4; db++) {
-          ta[db] = ld_tfrag(sd + cc + to[db][0], sd + cc + to[db][1]);
-          tb[db] = ld_tfrag(sq + cc + to[db][0], sq + cc + to[db][1]);
-        }
-#pragma unroll
-        for (int db = 0; db < 4; db++) {
-          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[db], bp, dvt[db], 0, 0, 0);
-          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[db], bs, dkt[db], 0, 0, 0);
-        }
-      }
-    };
-    sdp(0);
-    rest(0, true);
-    rest(1, false);
+    unrolled<64>(slot);
     // pin the accumulators to the accumulation registers across the loop
     // (otherwise they are parked in ordinary registers and copied both ways
     // on every tile)

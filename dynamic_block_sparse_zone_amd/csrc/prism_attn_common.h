@@ -17,6 +17,7 @@
 // the compiler adds no conservative full drain of its own before LDS reads.
 #pragma once
 #include "prism_common.h"
+#include <utility>
 
 namespace prism {
 
@@ -94,6 +95,18 @@ __device__ inline bf16x8 ld_tfrag(const char* pa, const char* pb) {
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 r = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// f(std::integral_constant<int, t>{}) for t = 0 .. n-1 in order: the slot
+// index is a constant inside f, so register arrays indexed by it stay in
+// registers (a plain loop of this size is not always unrolled)
+template <class F, int... Ts>
+__device__ inline void unrolled_impl(F&& f, std::integer_sequence<int, Ts...>) {
+  (f(std::integral_constant<int, Ts>{}), ...);
+}
+template <int n, class F>
+__device__ inline void unrolled(F&& f) {
+  unrolled_impl(f, std::make_integer_sequence<int, n>{});
 }
 
 // two floats to packed bf16, one v_cvt_pk_bf16_f32 (round to nearest even)
