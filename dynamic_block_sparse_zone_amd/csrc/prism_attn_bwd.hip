@@ -18,7 +18,7 @@
 //    dS arithmetic of one slice under the products of the other;
 //  * dQ: a work-group owns 256 permuted query rows (8 waves) and walks its
 //    key blocks as the forward does: S^T = K Q^T, dP^T = V dO^T,
-//    dQ^T += K^T dS^T.
+//    dQ^T += K^T dS^T, the tile's 48 MFMAs again in a fenced order.
 #include "prism_attn_common.h"
 #include "prism_kernels.h"
 
@@ -395,42 +395,67 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
     ring_step(j);
     const char* sk = ringK + (j & (kRing - 1)) * kTile;
     const char* sv = ringV + (j & (kRing - 1)) * kTile;
-    // S^T = K Q^T and dP^T = V dO^T: lane holds query l32, keys 8r' + 4hl + i
+    // The tile's 48 MFMAs in a fixed order, one per slot:
+    //   ops  0..15  S^T = K Q^T and dP^T = V dO^T of keys 0..31 (alternating)
+    //   ops 16..31  the same for keys 32..63, while the dS of keys 0..31 is
+    //               formed (lane: query l32, keys 8r' + 4hl + i)
+    //   ops 32..47  dQ^T += K^T dS^T, 16 keys per group of four, while the
+    //               dS of keys 32..63 is formed.
+    // Each op's fragment is read kWin slots ahead and a scheduling fence
+    // closes every slot.
+    constexpr int kWin = 3;
+    auto frag = [&](auto tc) -> bf16x8 {
+      constexpr int t = decltype(tc)::value;
+      if constexpr (t < 32) {
+        return ld_frag(((t & 1) ? sv : sk) + (t >> 4) * 8192 + ro[(t & 15) >> 1]);
+      } else {
+        constexpr int c = (t - 32) >> 2, db = (t - 32) & 3;
+        return ld_tfrag(sk + c * 4096 + to[db][0], sk + c * 4096 + to[db][1]);
+      }
+    };
     f32x16 st[2], dpt[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        st[kb][r] = 0.0f;
-        dpt[kb][r] = 0.0f;
+    uint32_t pk[4][4];
+    float prev = 0.0f;
+    bf16x8 win[kWin];
+    unrolled<kWin>([&](auto tc) { win[decltype(tc)::value] = frag(tc); });
+    // dS element e (0..31): the B operand bs[e / 8], row r of key half e / 16
+    auto ds_elem = [&](auto ec) {
+      constexpr int e = decltype(ec)::value, c = e >> 3, i = e & 7;
+      constexpr int r = 8 * (c & 1) + i, kb = c >> 1;
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c_log2, -L));
+      const float sv = pv * (dpt[kb][r] - Dl);
+      if constexpr (i & 1) pk[c][i >> 1] = pk2(prev, sv);
+      prev = sv;
+    };
+    auto slot = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      const bf16x8 f = win[t % kWin];
+      if constexpr (t + kWin < 48)
+        win[t % kWin] = frag(std::integral_constant<int, t + kWin>{});
+      if constexpr (t < 32) {
+        constexpr int kb = t >> 4, kk = (t & 15) >> 1;
+        if constexpr (t & 1)
+          dpt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, df[kk], kk ? dpt[kb] : f32x16{},
+                                                            0, 0, 0);
+        else
+          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], kk ? st[kb] : f32x16{},
+                                                           0, 0, 0);
+      } else {
+        constexpr int c = (t - 32) >> 2, db = (t - 32) & 3;
+        const bf16x8 bs =
+            __builtin_bit_cast(bf16x8, make_uint4(pk[c][0], pk[c][1], pk[c][2], pk[c][3]));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, bs, acc[db], 0, 0, 0);
       }
-#pragma unroll
-    for (int kk = 0; kk < 8; kk++)
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++) {
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sk + kb * 8192 + ro[kk]),
-                                                         qf[kk], st[kb], 0, 0, 0);
-        dpt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_frag(sv + kb * 8192 + ro[kk]),
-                                                          df[kk], dpt[kb], 0, 0, 0);
+      // keys 0..31 one element a slot from slot 17, keys 32..63 two a slot
+      // from slot 33 (a slot after the last product they read)
+      if constexpr (t >= 17 && t < 33) ds_elem(std::integral_constant<int, t - 17>{});
+      if constexpr (t >= 33 && t < 41) {
+        ds_elem(std::integral_constant<int, 16 + 2 * (t - 33)>{});
+        ds_elem(std::integral_constant<int, 17 + 2 * (t - 33)>{});
       }
-    // dS = P (dP - Delta) as the B operand of dQ^T += K^T dS^T
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int r = 8 * (c & 1) + 2 * e;
-        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r], c_log2, -L));
-        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c >> 1][r + 1], c_log2, -L));
-        pk[e] = pk2(p0 * (dpt[c >> 1][r] - Dl), p1 * (dpt[c >> 1][r + 1] - Dl));
-      }
-      const bf16x8 bs = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-#pragma unroll
-      for (int db = 0; db < 4; db++)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            ld_tfrag(sk + c * 4096 + to[db][0], sk + c * 4096 + to[db][1]), bs, acc[db], 0, 0,
-            0);
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    unrolled<48>(slot);
     j++;
   }
   // no tile load may still be writing LDS when the work-group ends
