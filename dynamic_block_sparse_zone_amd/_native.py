@@ -24,7 +24,7 @@ PRISM_BF16 = 1
 ARRAYS = {
     "zone_stats": 0, "audio_stats": 1, "shape_id": 2, "blk_off": 3, "blk_start": 4,
     "qbar": 5, "kbar": 6, "qexp": 7, "kexp": 8, "row_ptr": 9, "col_idx": 10,
-    "colt_ptr": 11, "colt_idx": 12, "perm": 13, "qgrid": 14, "kgrid": 15,
+    "colt_ptr": 11, "colt_idx": 12, "perm": 13, "qgrid": 14, "kgrid": 15, "kv_order": 16,
 }
 
 EXPORTED = [

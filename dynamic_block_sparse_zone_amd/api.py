@@ -24,7 +24,7 @@ _NP = {
     "blk_off": np.int64, "blk_start": np.int32, "qbar": np.float32, "kbar": np.float32,
     "qexp": np.int32, "kexp": np.int32, "row_ptr": np.int64, "col_idx": np.int32,
     "colt_ptr": np.int64, "colt_idx": np.int32, "perm": np.int32, "qgrid": np.uint16,
-    "kgrid": np.uint16,
+    "kgrid": np.uint16, "kv_order": np.int32,
 }
 
 

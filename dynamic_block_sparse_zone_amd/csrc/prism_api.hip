@@ -139,10 +139,16 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
     P->colt_ptr = A.take<int64_t>(G + 1);
     P->colt_cnt = A.take<int32_t>(G);
     P->chunk_cnt = A.take<int32_t>((maxblk / 64 + 1) * maxblk);
+    P->korder = A.take<int32_t>((int64_t)c.heads * (N / 128));
+    P->colt_cost = A.take<int64_t>(G);
+    P->sync = A.take<int32_t>(128);
   } else {
     P->colt_ptr = nullptr;
     P->colt_cnt = nullptr;
     P->chunk_cnt = nullptr;
+    P->korder = nullptr;
+    P->colt_cost = nullptr;
+    P->sync = nullptr;
   }
   P->col_idx = A.take<int32_t>(cap);
   P->colt_idx = c.need_backward ? A.take<int32_t>(cap) : nullptr;
@@ -277,6 +283,12 @@ prism_status prism_plan_create(const prism_config* c, const void* q, const void*
     stage_end(st);
     if (!ok) return PRISM_EDEVICE;
   }
+  if (c->need_backward) {
+    stage_begin("plan.order", st);
+    ok = launch_unit_order_k(P, off, st);
+    stage_end(st);
+    if (!ok) return PRISM_EDEVICE;
+  }
   PRISM_HIP(hipGetLastError());
   prism_plan_s* pl = new prism_plan_s;
   pl->cfg = *c;
@@ -391,6 +403,9 @@ static const void* array_ptr(const prism_plan_t* pl, int which, size_t* bytes) {
     case PRISM_ARR_PERM: *bytes = sizeof(int32_t) * c.heads * P.N; return pl->perm;
     case PRISM_ARR_QGRID: *bytes = sizeof(uint16_t) * G * c.head_dim; return P.qgrid;
     case PRISM_ARR_KGRID: *bytes = sizeof(uint16_t) * G * c.head_dim; return P.kgrid;
+    case PRISM_ARR_KV_ORDER:
+      *bytes = c.need_backward ? sizeof(int32_t) * c.heads * (P.N / 128) : 0;
+      return P.korder;
     default: *bytes = 0; return nullptr;
   }
 }
@@ -399,13 +414,13 @@ prism_status prism_plan_array_bytes(const prism_plan_t* plan, int32_t which, siz
   if (!plan || !bytes) return PRISM_EINVAL;
   const void* p = array_ptr(plan, which, bytes);
   if (!p && *bytes) return PRISM_EINVAL;
-  if (which < 0 || which > PRISM_ARR_KGRID) return PRISM_EINVAL;
+  if (which < 0 || which > PRISM_ARR_KV_ORDER) return PRISM_EINVAL;
   return PRISM_OK;
 }
 
 prism_status prism_plan_export(const prism_plan_t* plan, int32_t which, void* dst,
                                size_t dst_bytes, void* stream) {
-  if (!plan || !dst || which < 0 || which > PRISM_ARR_KGRID) return PRISM_EINVAL;
+  if (!plan || !dst || which < 0 || which > PRISM_ARR_KV_ORDER) return PRISM_EINVAL;
   size_t bytes = 0;
   const void* p = array_ptr(plan, which, &bytes);
   if (dst_bytes < bytes) return PRISM_EINVAL;

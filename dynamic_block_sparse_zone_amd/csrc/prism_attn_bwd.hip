@@ -15,7 +15,11 @@
 //    dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by
 //    ds_read_b64_tr_b16.  One wave per SIMD: a tile's 64 MFMAs run in a
 //    fixed, fenced order with each fragment read a few MFMAs ahead and the
-//    dS arithmetic of one slice under the products of the other;
+//    dS arithmetic of one slice under the products of the other.  The launch
+//    is persistent: each XCD's work-groups take its units in the plan's
+//    order (longest walk first) a generation at a time, so that walks of
+//    equal length share the XCD's L2 (it fetches 2x the bytes per flop of
+//    the query-major kernels, which gained nothing from this);
 //  * dQ: a work-group owns 256 permuted query rows (8 waves) and walks its
 //    key blocks as the forward does: S^T = K Q^T, dP^T = V dO^T,
 //    dQ^T += K^T dS^T, the tile's 48 MFMAs again in a fenced order.
@@ -82,7 +86,8 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
     const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_start,
     const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ colt_ptr,
     const int32_t* __restrict__ colt_idx, int H, int W, int Z, int64_t N, float c_log2,
-    float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+    float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t nunits,
+    const int32_t* __restrict__ order, int32_t* sync) {
   // ring of query-tile slots: Q and dO tiles, and the LSE and Delta columns
   // (two objects, so that the reads of each carry their own alias scope)
   __shared__ __attribute__((aligned(16))) char ring[kRing * 2 * kTile];
@@ -90,7 +95,12 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   const int64_t upH = N / kKvRows;
-  const int64_t unit = xcd_unit(blockIdx.x, gridDim.x);
+  const UnitLoop L(nunits);
+  for (int gen = 0; gen < L.ngen; gen++) {
+  L.start(sync, gen);
+  const int64_t unit = L.unit(order, upH, gen);
+  if (unit < 0) continue;
+  {
   const int h = (int)(unit / upH);
   const int64_t r0 = (unit - (int64_t)h * upH) * kKvRows;
   const int m = (int)(r0 >> 9);
@@ -290,6 +300,8 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
       *(uint2*)(dkr + 32 * db + 8 * j + 4 * hl) = a;
       *(uint2*)(dvr + 32 * db + 8 * j + 4 * hl) = b;
     }
+  }
+  }
 }
 
 // ---------------------------------------------------------------- dQ
@@ -474,6 +486,22 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
     }
 }
 
+// ---------------------------------------------------------------- launch
+// dK/dV runs persistent: one work-group per compute unit (a multiple of 8:
+// one share per XCD).
+static int persistent_grid() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n = 256;
+  n &= ~7;
+  return n < 8 ? 8 : n;
+}
+
+// the start counters to zero (a fill kernel, not a memset, so that the
+// launch sequence can be captured into a graph)
+__global__ void k_clear_sync(int32_t* p) { p[threadIdx.x] = 0; }
+
 static const float kCLog2 = (float)(1.4426950408889634 / 11.313708498984761);
 static const float kScale = (float)(1.0 / 11.313708498984761);
 
@@ -489,12 +517,14 @@ bool launch_bwd_prep(const PlanDev& P, const BwdDev& Bd, const void* q, const vo
 
 bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& Bd, void* dk, void* dv, hipStream_t st) {
   if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
-  dim3 grid((unsigned)(P.heads * (P.N / kKvRows))), block(kKvWaves * 64);
+  hipLaunchKernelGGL(k_clear_sync, dim3(1), dim3(128), 0, st, P.sync);
+  dim3 grid((unsigned)persistent_grid()), block(kKvWaves * 64);
   hipLaunchKernelGGL(k_bwd_dkdv, grid, block, 0, st, (const uint16_t*)Bd.qp,
                      (const uint16_t*)Bd.dop, Bd.lse_p, Bd.delta, (const uint16_t*)P.kp,
                      (const uint16_t*)P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start,
                      P.blk_shape, P.colt_ptr, P.colt_idx, P.H, P.W, P.Z, P.N, kCLog2, kScale,
-                     (uint16_t*)dk, (uint16_t*)dv);
+                     (uint16_t*)dk, (uint16_t*)dv, P.heads * (P.N / kKvRows), P.korder,
+                     P.sync);
   return hipGetLastError() == hipSuccess;
 }
 

@@ -285,4 +285,46 @@ struct TileIter {
   }
 };
 
+// Persistent work loop (the dK/dV kernel).  A launch has one work-group per
+// compute unit.  The work-groups of one XCD (blockIdx % 8: the
+// hardware deals work-groups to the XCDs in turn) share that XCD's contiguous
+// part of the unit order -- per head, units by walk length, longest first --
+// and take its units in generations of gridDim.x / 8.  A generation starts
+// together: each work-group adds one to its XCD's counter and polls it, with
+// a bounded number of polls, until the whole generation has arrived.  The
+// wait only aligns start times, never a result, so the walks of a generation
+// (near-equal lengths, mostly the same tiles) pass over their shared tiles
+// close together and the XCD's L2 serves the repeats.
+constexpr int kStartPolls = 4000;
+struct UnitLoop {
+  int xg, wgi, per_x, ngen;
+  int64_t p0, p1;
+  __device__ explicit UnitLoop(int64_t total) {
+    xg = blockIdx.x & 7;
+    wgi = blockIdx.x >> 3;
+    per_x = gridDim.x >> 3;
+    p0 = xg * total / 8;
+    p1 = (xg + 1) * total / 8;
+    ngen = (int)((p1 - p0 + per_x - 1) / per_x);
+  }
+  // the unit (head * upH + index) of generation gen, or -1
+  __device__ int64_t unit(const int32_t* order, int64_t upH, int gen) const {
+    const int64_t p = p0 + (int64_t)gen * per_x + wgi;
+    if (p >= p1) return -1;
+    return (p / upH) * upH + order[p];
+  }
+  __device__ void start(int32_t* sync, int gen) const {
+    if (threadIdx.x == 0) {
+      int32_t* c = sync + xg * 16;
+      __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int target = per_x * (gen + 1);
+      for (int i = 0; i < kStartPolls &&
+                      __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target;
+           i++)
+        __builtin_amdgcn_s_sleep(8);
+    }
+    __syncthreads();
+  }
+};
+
 }  // namespace prism

@@ -142,6 +142,10 @@ struct PlanDev {
   int64_t* row_cost;   // [Gmax] B_i * sum_{j in S_i} B_j
   int64_t* counters;   // [8]: [0] nnz running total
   int64_t cap;
+  // dK/dV work units, per head longest walk first (backward plans)
+  int32_t* korder;     // [heads][N/128]
+  int64_t* colt_cost;  // [Gmax] B_j * sum_{i: j in S_i} B_i
+  int32_t* sync;       // [128] start counters of the persistent dK/dV kernel
 };
 
 }  // namespace prism

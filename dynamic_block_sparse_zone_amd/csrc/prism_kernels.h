@@ -1,6 +1,7 @@
 // Host-side launchers of the gfx950 kernels (one translation unit each).
 #pragma once
 #include "prism_common.h"
+#include <vector>
 
 namespace prism {
 
@@ -18,6 +19,8 @@ bool launch_select(const PlanDev& P, int64_t g0, int n, const prism_config& c, i
 bool launch_transpose(const PlanDev& P, int64_t g0, int n, int last, hipStream_t st);
 bool launch_perm_map(const PlanDev& P, int32_t* out, hipStream_t st);
 bool launch_sum_i64(const int64_t* in, int64_t n, int64_t* out, hipStream_t st);
+// the dK/dV work-unit order (after the transpose)
+bool launch_unit_order_k(const PlanDev& P, const std::vector<int64_t>& off, hipStream_t st);
 
 bool launch_attn_fwd(const PlanDev& P, const void* q, void* o, float* lse, hipStream_t st);
 

@@ -8,6 +8,7 @@
 // only where written as fmaf), so the plan is reproducible bit for bit.
 #include "prism_attn_common.h"
 #include "prism_kernels.h"
+#include <vector>
 
 namespace prism {
 
@@ -1291,7 +1292,102 @@ __global__ __launch_bounds__(256) void k_sum_i64(const int64_t* __restrict__ in,
   if (threadIdx.x == 0) *out = s;
 }
 
+// ============================================================ unit order
+// The dK/dV kernel's work units (128 key rows) are taken in an order of their
+// own: per head, by the length of the unit's walk, longest first (ties by
+// unit index).  Units that run side by side then walk lists of nearly equal
+// length, which over a dense-ish selection name mostly the same tiles, and
+// start and end together.
+
+// Cost of each key block's key-major list in token pairs, B_j * sum_i B_i
+// (the transpose of the rows' cost); one wave per block.
+__global__ __launch_bounds__(256) void k_colt_cost(const int64_t* __restrict__ colt_ptr,
+                                                   const int32_t* __restrict__ colt_idx,
+                                                   int64_t g0, int n,
+                                                   const uint8_t* __restrict__ blk_shape,
+                                                   int64_t* __restrict__ colt_cost) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= n) return;
+  const int64_t g = g0 + j;
+  int64_t c = 0;
+  for (int64_t e = colt_ptr[g] + lane; e < colt_ptr[g + 1]; e += 64)
+    c += volume_of_id(block_shape_at(blk_shape, g0 + colt_idx[e]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+  if (lane == 0) colt_cost[g] = c * (int64_t)volume_of_id(block_shape_at(blk_shape, g));
+}
+
+// One work-group per head: the walk length of every unit of U rows (the
+// longest list among the unit's blocks, in 64-row tiles: cost / B / 64),
+// keyed ((16383 - min(tiles, 16383)) << 17 | unit) and sorted ascending by a
+// bitonic sort in LDS.  Heads with more units than the LDS holds keep the
+// identity order.
+constexpr int kOrderMax = 32768;
+template <int U>
+__global__ __launch_bounds__(1024) void k_unit_order(const uint8_t* __restrict__ shape_id,
+                                                     const int32_t* __restrict__ zone_base,
+                                                     const int64_t* __restrict__ blk_off,
+                                                     const int64_t* __restrict__ cost, int Z,
+                                                     int64_t N, int32_t* __restrict__ order) {
+  __shared__ uint32_t key[kOrderMax];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int upH = (int)(N / U);
+  int32_t* out = order + (int64_t)h * upH;
+  if (upH > kOrderMax) {
+    for (int u = tid; u < upH; u += 1024) out[u] = u;
+    return;
+  }
+  int np = 1;
+  while (np < upH) np <<= 1;
+  const int64_t hoff = blk_off[h];
+  for (int u = tid; u < np; u += 1024) {
+    uint32_t k = 0xffffffffu;
+    if (u < upH) {
+      const int64_t r0 = (int64_t)u * U;
+      const int m = (int)(r0 >> 9);
+      const int B = d_shapes[shape_id[(int64_t)h * Z + m]].volume;
+      const int first = zone_base[(int64_t)h * Z + m] + (int)(r0 & 511) / B;
+      const int cnt = B >= U ? 1 : U / B;
+      int64_t w = 0;
+      for (int c = 0; c < cnt; c++) w = max(w, cost[hoff + first + c] / B);
+      const int t = (int)min<int64_t>(w >> 6, 16383);
+      k = ((uint32_t)(16383 - t) << 17) | (uint32_t)u;
+    }
+    key[u] = k;
+  }
+  __syncthreads();
+  for (int k2 = 2; k2 <= np; k2 <<= 1)
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < np; i += 1024) {
+        const int ij = i ^ j;
+        if (ij > i) {
+          const uint32_t a = key[i], b = key[ij];
+          if ((a > b) == ((i & k2) == 0)) {
+            key[i] = b;
+            key[ij] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int u = tid; u < upH; u += 1024) out[u] = (int32_t)(key[u] & 0x1ffffu);
+}
+
 // ============================================================ launchers
+bool launch_unit_order_k(const PlanDev& P, const std::vector<int64_t>& off, hipStream_t st) {
+  for (int h = 0; h < P.heads; h++) {
+    const int n = (int)(off[h + 1] - off[h]);
+    if (n > 0)
+      hipLaunchKernelGGL(k_colt_cost, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st,
+                         P.colt_ptr, P.colt_idx, off[h], n, P.blk_shape, P.colt_cost);
+  }
+  hipLaunchKernelGGL(k_unit_order<128>, dim3(P.heads), dim3(1024), 0, st, P.shape_id,
+                     P.zone_base, P.blk_off, P.colt_cost, P.Z, P.N, P.korder);
+  return hipGetLastError() == hipSuccess;
+}
+
+
 bool launch_blk_off(const PlanDev& P, hipStream_t st) {
   hipLaunchKernelGGL(k_blk_off, dim3(1), dim3(64), 0, st, P.nblk, P.heads, P.blk_off);
   return hipGetLastError() == hipSuccess;

@@ -165,7 +165,13 @@ typedef enum {
   PRISM_ARR_COLT_IDX = 12,    /* int32 [nnz]: query blocks selecting each key block, ascending */
   PRISM_ARR_PERM = 13,        /* int32 [heads][N]: original token of each permuted row */
   PRISM_ARR_QGRID = 14,       /* uint16 (bf16 bits) [G][head_dim]: integer grid of Qbar */
-  PRISM_ARR_KGRID = 15        /* uint16 (bf16 bits) [G][head_dim] */
+  PRISM_ARR_KGRID = 15,       /* uint16 (bf16 bits) [G][head_dim] */
+  PRISM_ARR_KV_ORDER = 16     /* int32 [heads][N/128] (need_backward): the dK/dV kernel's work
+                                 units (128 permuted key rows) of each head, in the order it
+                                 takes them: longest walk first (the longest key-major list
+                                 among the unit's blocks, in 64-row tiles, capped at 16383),
+                                 ties by unit index.  A scheduling order only: dK and dV do
+                                 not depend on it. */
 } prism_array;
 
 /* Size in bytes of a plan array. Host-only. */

@@ -146,3 +146,33 @@ def test_plan_deterministic(prism):
     b = gpu_plan(prism, wl, dx)
     for name in ("shape_id", "row_ptr", "col_idx", "colt_idx", "qbar", "zone_stats"):
         assert np.array_equal(a.export(name), b.export(name)), name
+
+
+@pytest.mark.parametrize("over", [{}, {"fixed_shape": (4, 4, 8)}, {"top_p": 1.0}])
+def test_kv_order(prism, over):
+    """The dK/dV kernel's unit order: per head a permutation of the 128-row
+    units, longest walk first (the longest key-major list among the unit's
+    key blocks, counted in 64-row tiles of the query blocks it names), ties
+    by unit index.  Recomputed here from the exported lists."""
+    wl = synth.WORKLOADS["small"]
+    print(f"[kv order] over={over}", flush=True)
+    dx = to_dev(synth.make_inputs(wl, device="cpu", with_grad=False), DEV)
+    pl = gpu_plan(prism, wl, dx, **over)
+    N = wl.T * wl.H * wl.W
+    upH = N // 128
+    order = pl.export("kv_order").reshape(wl.heads, upH)
+    off, start = pl.export("blk_off"), pl.export("blk_start")
+    cptr, cidx = pl.export("colt_ptr"), pl.export("colt_idx")
+    for h in range(wl.heads):
+        b0, b1 = int(off[h]), int(off[h + 1])
+        st = start[b0:b1].astype(np.int64)
+        tiles = np.diff(np.append(st, N)) // 64
+        work = np.array([tiles[cidx[cptr[b0 + j]:cptr[b0 + j + 1]]].sum() for j in range(b1 - b0)])
+        unit_work = np.zeros(upH, np.int64)
+        for u in range(upH):
+            r0 = u * 128
+            first = np.searchsorted(st, r0, side="right") - 1
+            last = np.searchsorted(st, r0 + 128, side="left")
+            unit_work[u] = work[first:max(last, first + 1)].max()
+        want = sorted(range(upH), key=lambda u: (-min(int(unit_work[u]), 16383), u))
+        np.testing.assert_array_equal(order[h], np.array(want, np.int32))
