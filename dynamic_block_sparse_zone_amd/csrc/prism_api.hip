@@ -78,6 +78,10 @@ int fixed_id_of(const prism_config& c) {
   return -2;
 }
 
+// selection density from which the dK/dV kernel runs persistent over the
+// planned unit order (measured: 0.86 gains 3-4 %, 0.15 loses 6 %)
+constexpr double kPersistDensity = 0.5;
+
 // Sequential sub-allocator over the caller's workspace (256-byte aligned);
 // with a null base it only measures.
 struct Arena {
@@ -150,6 +154,7 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
     P->colt_cost = nullptr;
     P->sync = nullptr;
   }
+  P->kv_persist = 0;
   P->col_idx = A.take<int32_t>(cap);
   P->colt_idx = c.need_backward ? A.take<int32_t>(cap) : nullptr;
   P->cap = cap;
@@ -289,6 +294,11 @@ prism_status prism_plan_create(const prism_config* c, const void* q, const void*
     stage_end(st);
     if (!ok) return PRISM_EDEVICE;
   }
+  // the dK/dV kernel takes the ordered persistent launch when at least half
+  // of all (query block, key block) pairs are selected
+  double pairs_all = 0.0;
+  for (int h = 0; h < c->heads; h++) pairs_all += (double)(off[h + 1] - off[h]) * (off[h + 1] - off[h]);
+  P.kv_persist = c->need_backward && (double)nnz >= kPersistDensity * pairs_all;
   PRISM_HIP(hipGetLastError());
   prism_plan_s* pl = new prism_plan_s;
   pl->cfg = *c;

@@ -15,11 +15,13 @@
 //    dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by
 //    ds_read_b64_tr_b16.  One wave per SIMD: a tile's 64 MFMAs run in a
 //    fixed, fenced order with each fragment read a few MFMAs ahead and the
-//    dS arithmetic of one slice under the products of the other.  The launch
-//    is persistent: each XCD's work-groups take its units in the plan's
-//    order (longest walk first) a generation at a time, so that walks of
-//    equal length share the XCD's L2 (it fetches 2x the bytes per flop of
-//    the query-major kernels, which gained nothing from this);
+//    dS arithmetic of one slice under the products of the other.  For dense
+//    selections the launch is persistent: each XCD's work-groups take its
+//    units in the plan's order (longest walk first) a generation at a time,
+//    so that walks of equal length share the XCD's L2 (it fetches 2x the
+//    bytes per flop of the query-major kernels, which gained nothing from
+//    this; sparse selections share too little and keep one unit per
+//    work-group);
 //  * dQ: a work-group owns 256 permuted query rows (8 waves) and walks its
 //    key blocks as the forward does: S^T = K Q^T, dP^T = V dO^T,
 //    dQ^T += K^T dS^T, the tile's 48 MFMAs again in a fenced order.
@@ -95,11 +97,16 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   const int64_t upH = N / kKvRows;
+  // persistent (sync given) or one unit per work-group
   const UnitLoop L(nunits);
-  for (int gen = 0; gen < L.ngen; gen++) {
-  L.start(sync, gen);
-  const int64_t unit = L.unit(order, upH, gen);
-  if (unit < 0) continue;
+  const int ngen = sync ? L.ngen : 1;
+  for (int gen = 0; gen < ngen; gen++) {
+  int64_t unit = xcd_unit(blockIdx.x, gridDim.x);
+  if (sync) {
+    L.start(sync, gen);
+    unit = L.unit(order, upH, gen);
+    if (unit < 0) continue;
+  }
   {
   const int h = (int)(unit / upH);
   const int64_t r0 = (unit - (int64_t)h * upH) * kKvRows;
@@ -517,14 +524,17 @@ bool launch_bwd_prep(const PlanDev& P, const BwdDev& Bd, const void* q, const vo
 
 bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& Bd, void* dk, void* dv, hipStream_t st) {
   if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
-  hipLaunchKernelGGL(k_clear_sync, dim3(1), dim3(128), 0, st, P.sync);
-  dim3 grid((unsigned)persistent_grid()), block(kKvWaves * 64);
+  // the ordered persistent launch pays where units share most of their
+  // tiles (dense selections); sparse plans take one unit per work-group
+  const int64_t nunits = P.heads * (P.N / kKvRows);
+  if (P.kv_persist) hipLaunchKernelGGL(k_clear_sync, dim3(1), dim3(128), 0, st, P.sync);
+  dim3 grid((unsigned)(P.kv_persist ? persistent_grid() : nunits)), block(kKvWaves * 64);
   hipLaunchKernelGGL(k_bwd_dkdv, grid, block, 0, st, (const uint16_t*)Bd.qp,
                      (const uint16_t*)Bd.dop, Bd.lse_p, Bd.delta, (const uint16_t*)P.kp,
                      (const uint16_t*)P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start,
                      P.blk_shape, P.colt_ptr, P.colt_idx, P.H, P.W, P.Z, P.N, kCLog2, kScale,
-                     (uint16_t*)dk, (uint16_t*)dv, P.heads * (P.N / kKvRows), P.korder,
-                     P.sync);
+                     (uint16_t*)dk, (uint16_t*)dv, nunits, P.korder,
+                     P.kv_persist ? P.sync : nullptr);
   return hipGetLastError() == hipSuccess;
 }
 

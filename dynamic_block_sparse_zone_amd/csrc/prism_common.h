@@ -146,6 +146,7 @@ struct PlanDev {
   int32_t* korder;     // [heads][N/128]
   int64_t* colt_cost;  // [Gmax] B_j * sum_{i: j in S_i} B_i
   int32_t* sync;       // [128] start counters of the persistent dK/dV kernel
+  int kv_persist;      // dK/dV launch: ordered persistent (dense selections) or per unit
 };
 
 }  // namespace prism
