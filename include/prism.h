@@ -32,7 +32,10 @@
  *   - no call aborts or prints; failures are returned as prism_status.
  *     Asynchronous device faults surface as PRISM_EDEVICE from a later call.
  *   - plans may be used from any host thread, but two calls that use one
- *     plan must not run concurrently on different streams.
+ *     plan must not run concurrently on different streams (prism_attn_bwd
+ *     keeps the start counters of its dK/dV launch in the plan workspace;
+ *     two overlapping backward calls on one plan would share them, which
+ *     slows both and changes no result).
  */
 #ifndef PRISM_H
 #define PRISM_H
@@ -136,7 +139,9 @@ prism_status prism_attn_bwd_workspace_size(const prism_config* cfg, size_t* byte
  * o and lse are those prism_attn_fwd produced for the same plan and inputs.
  * Needs a plan built with need_backward; key blocks that no query block
  * selected receive zero gradient.  Deterministic (no floating-point
- * atomics). */
+ * atomics; the dK/dV launch orders its work by the plan's unit order and, for
+ * plans selecting at least half of all block pairs, starts the work-groups of
+ * each XCD together, which affects timing only). */
 prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void* k,
                             const void* v, const void* o, const float* lse, const void* d_o,
                             void* dq, void* dk, void* dv, void* workspace,
@@ -201,7 +206,8 @@ prism_status prism_candidate(int32_t id, int32_t* out4);
 /* Measurement support.  While enabled, every kernel stage the library
  * enqueues is bracketed by a pair of HIP events recorded on the stage's own
  * stream (stage names: plan.stats, plan.shapes, plan.permute, plan.scores,
- * plan.select, plan.transpose, attn.fwd, bwd.prep, bwd.dkdv, bwd.dq).
+ * plan.select, plan.transpose, plan.order, attn.fwd, bwd.prep, bwd.dkdv,
+ * bwd.dq).
  * Host-only; off by default. */
 prism_status prism_timing_enable(int32_t enable);
 
