@@ -14,8 +14,9 @@
 //    LDS ring; per 32-query slice it forms S = Q K^T and dP = dO V^T, then
 //    dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by
 //    ds_read_b64_tr_b16.  One wave per SIMD: a tile's 64 MFMAs run in a
-//    fixed, fenced order with each fragment read a few MFMAs ahead and the
-//    dS arithmetic of one slice under the products of the other.  For dense
+//    fixed, fenced order with each fragment read eight MFMAs ahead (the
+//    next tile's first ones during this tile's last products) and the dS
+//    arithmetic of one slice under the products of the other.  For dense
 //    selections the launch is persistent: each XCD's work-groups take its
 //    units in the plan's order (longest walk first) a generation at a time,
 //    so that walks of equal length share the XCD's L2 (it fetches 2x the
@@ -188,13 +189,21 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
   issue(1);
   issue(2);
   // one ring step per tile, in every wave
+  // step j: tiles j and j + 1 have landed, so the first fragments of tile
+  // j + 1 can be read during the last slots of tile j
   auto ring_step = [&](int j) {
-    __builtin_amdgcn_s_waitcnt(wait_vm(2 * kKvLoads));
+    __builtin_amdgcn_s_waitcnt(wait_vm(kKvLoads));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue((j + kRing - 1) & (kRing - 1));
   };
   auto listed = [&](int j) { return ((ring_f >> (8 * (j & (kRing - 1)) + mylist)) & 1u) != 0; };
+  // fragments read ahead of their MFMA; a divisor of the tile's 64 slots,
+  // so that slot t and the next tile's slot t + kWin - 64 share win[t % kWin]
+  constexpr int kWin = 8;
+  static_assert(64 % kWin == 0, "window must divide the slots of a tile");
+  bf16x8 win[kWin];
+  int pre_tile = -1;  // the tile whose first kWin fragments win holds
   int j = 0;
   while (true) {
     // tiles whose query block does not list this wave's key block only move
@@ -204,6 +213,8 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
     ring_step(j);
     const char* sq = ring + (j & (kRing - 1)) * 2 * kTile;  // Q tile
     const char* sd = sq + kTile;                            // dO tile
+    const char* sqn = ring + ((j + 1) & (kRing - 1)) * 2 * kTile;  // next tile
+    const char* sdn = sqn + kTile;
     const float* sl = ringc + (j & (kRing - 1)) * 128;      // log2(e) LSE
     const float* sdl = sl + 64;                             // Delta
     // The tile's 64 MFMAs in a fixed order, one per slot:
@@ -212,10 +223,10 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
     //   ops 32..47  dV^T += dO^T P, dK^T += Q^T dS of half 0, while half 1's
     //               dS is formed
     //   ops 48..63  the same for half 1.
-    // Each op's fragment is read kWin slots ahead, and a scheduling fence
-    // closes every slot, so LDS latency and the VALU work hide under the
-    // MFMAs already issued.
-    constexpr int kWin = 6;
+    // Each op's fragment is read kWin slots ahead (the last slots read the
+    // first fragments of the next tile), and a scheduling fence closes every
+    // slot, so LDS latency and the VALU work hide under the MFMAs already
+    // issued.
     auto frag = [&](int t) -> bf16x8 {
       if (t < 32) {
         const char* base = (t & 1) ? sd : sq;
@@ -229,13 +240,19 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
     uint32_t pp[2][8], ps[2][8];
     f32x4 Lc[2][4], Dc[2][4];
     float pv_prev = 0.0f, sv_prev = 0.0f;
-    bf16x8 win[kWin];
+    if (pre_tile != j) {
 #pragma unroll
-    for (int t = 0; t < kWin; t++) win[t] = frag(t);
+      for (int t = 0; t < kWin; t++) win[t] = frag(t);
+    }
     auto slot = [&](auto tc) {
       constexpr int t = decltype(tc)::value;
       const bf16x8 f = win[t % kWin];
-      if constexpr (t + kWin < 64) win[t % kWin] = frag(t + kWin);
+      if constexpr (t + kWin < 64) {
+        win[t % kWin] = frag(t + kWin);
+      } else {
+        constexpr int n = t + kWin - 64;  // an S/dP fragment of the next tile
+        win[t % kWin] = ld_frag(((n & 1) ? sdn : sqn) + (n >> 4) * 8192 + ro[(n & 15) >> 1]);
+      }
       if constexpr (t >= 12 && t < 44 && (t & 3) == 0) {
         // the LSE and Delta values of the dS rows formed four slots on
         constexpr int qb = (t - 12) >> 4, jj = ((t - 12) & 15) >> 2;
@@ -281,6 +298,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
       __builtin_amdgcn_sched_barrier(0);
     };
     unrolled<64>(slot);
+    pre_tile = j + 1;
     // pin the accumulators to the accumulation registers across the loop
     // (otherwise they are parked in ordinary registers and copied both ways
     // on every tile)
