@@ -302,7 +302,7 @@ struct UnitLoop {
   __device__ explicit UnitLoop(int64_t total) {
     xg = blockIdx.x & 7;
     wgi = blockIdx.x >> 3;
-    per_x = gridDim.x >> 3;
+    per_x = gridDim.x >= 8 ? gridDim.x >> 3 : 1;  // (a per-unit launch may be smaller)
     p0 = xg * total / 8;
     p1 = (xg + 1) * total / 8;
     ngen = (int)((p1 - p0 + per_x - 1) / per_x);

@@ -116,3 +116,19 @@ def test_bwd_deterministic(prism):
     b = prism.attn_bwd(pl, x["q"], x["k"], x["v"], o, lse, x["do"])
     for u, w in zip(a, b):
         assert torch.equal(u, w)
+
+
+def test_bwd_one_zone(prism, orc):
+    """One 8x8x8 zone and one head: fewer dK/dV work units (4) than a
+    persistent launch has work-groups per XCD."""
+    wl = synth.WORKLOADS["bwdcheck"].with_(name="onezone", T=8, H=8, W=8, heads=1)
+    print("[bwd parity] one zone", flush=True)
+    x = synth.make_inputs(wl, device="cpu", with_grad=True)
+    dx = to_dev(x, DEV)
+    for over in ({"top_p": 0.0, "top_k": 1}, {"top_p": 1.0}):
+        pl = gpu_plan(prism, wl, dx, **over)
+        o, lse = prism.attn_fwd(pl, dx["q"], dx["k"], dx["v"])
+        dq, dk, dv = prism.attn_bwd(pl, dx["q"], dx["k"], dx["v"], o, lse, dx["do"])
+        torch.cuda.synchronize()
+        grads = tuple(t.float().cpu().numpy() for t in (dq, dk, dv))
+        check_heads(orc, wl, x, grads, [0], **over)
