@@ -551,3 +551,47 @@ def test_backward_finite_differences(orc):
             lm = loss(args["q"], args["k"], args["v"])
             fd = (lp - lm) / (2 * hstep)
             assert abs(fd - grad[0, n, c]) <= 2e-3 * max(1.0, abs(fd)), (which, n, c)
+
+
+def _bf16_bits(x):
+    """float32 -> bf16 bit patterns (round to nearest even) and their values."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    b = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return b, (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("case", [
+    dict(top_k=2, top_p=0.3),                                   # two heads, mixed volumes
+    dict(T=8, H=16, W=16, heads=1, top_k=1, top_p=0.0, seed=31),  # Top-1 only: very sparse
+    dict(T=8, H=8, W=16, heads=1, top_k=3, top_p=0.5, seed=5, bf16=True),
+])
+def test_backward_head_matches_autograd_and_blockwise(orc, case):
+    """The whole-head backward (the reference of the GPU gradient checks)
+    equals fp64 autograd of the explicitly masked attention and the
+    per-block oracle functions, which autograd and finite differences pin
+    separately (paper.rainbus.top "技术新颖性": the plan is a constant and
+    gradients flow only through attention on the selected blocks)."""
+    case = dict(case)
+    bf16 = case.pop("bf16", False)
+    cfg, q, k, v, do, pl = _tiny(orc, **case)
+    if bf16:
+        (qb, q), (kb, k), (vb, v), (dob, do) = (_bf16_bits(x) for x in (q, k, v, do))
+        pl = orc.plan(qb, kb, vb, None, cfg)
+        args = (qb, kb, vb, dob)
+    else:
+        args = (q, k, v, do)
+    ref = _loss_grads_torch(q, k, v, do, pl, cfg)
+    items = _all_items(pl)
+    dq_b = _scatter(pl, items, orc.attn_bwd_q(*args, pl, items))
+    dk_i, dv_i = orc.attn_bwd_kv(*args, pl, items)
+    dk_b, dv_b = _scatter(pl, items, dk_i), _scatter(pl, items, dv_i)
+    sparse = False
+    for h in range(cfg.heads):
+        dq, dk, dv = orc.attn_bwd_head(*args, pl, h)
+        for got, want, blk in ((dq, ref[h][0], dq_b[h]), (dk, ref[h][1], dk_b[h]),
+                               (dv, ref[h][2], dv_b[h])):
+            np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-11)
+            np.testing.assert_allclose(got, blk, rtol=1e-9, atol=1e-11)
+        sparse |= bool(np.any(np.all(dv == 0, axis=1)))
+    if case.get("top_p") == 0.0:
+        assert sparse      # some key tokens received no gradient at all
