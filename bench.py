@@ -1,8 +1,8 @@
 """Benchmark of one Prism sparse-attention layer on one MI355X.
 
 A step is the whole hot path over one batch of synthetic input: the plan
-(zone statistics, shapes, re-layout and pooling, block scores, Top-k U Top-p
-selection, key-major lists), the sparse attention forward and the backward.
+(zone statistics, shapes, block table and pooling, block scores, Top-k U
+Top-p selection, key-major lists), the sparse attention forward and the backward.
 Default workload: the 2K training-scale layer (72 x 120 x 120 = 1,036,800
 tokens, 40 heads of 128, bf16, k = 16, p = 0.9).
 
@@ -20,6 +20,7 @@ import os
 import sys
 import time
 
+T_PROCESS = time.time()     # the wall-clock budget counts from here
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -205,8 +206,13 @@ def summarize_pmc(fetch_csv, write_csv, stage, workload, cmds, out):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed steps (an upper bound: as many as fit the time budget)")
+    ap.add_argument("--warmup", type=int, default=1,
+                    help="full-size warm-up steps (an upper bound, at most 1 when a step "
+                         "takes more than a minute)")
+    ap.add_argument("--time-budget", type=float, default=520.0,
+                    help="seconds from process start by which the JSON line is printed")
     ap.add_argument("--workload", default="train2k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-blocks", type=int, default=0,
@@ -226,12 +232,17 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(wl, x, nblocks):
-    """The oracle as it is, on a bounded sample: the forward of `nblocks`
-    query blocks of head 0 (smallest volumes first), fp64, OpenMP over
-    blocks.  Rate in TFLOP/s of the same 4 * D * B_i * B_j accounting."""
+def cpu_baseline(wl, x, nblocks, threads, step_flops):
+    """The oracle as it is, timed on a bounded sample of the same workload:
+    the plan of head 0 up to the pooled block means (zone statistics, shapes,
+    block table, permutation, pooling), the block scores and Top-k U Top-p
+    selection of the sampled query blocks, then the fp64 attention forward
+    of `nblocks` 64-token query blocks of head 0 drawn at random (OpenMP over
+    blocks, one block per thread).  The rate is in TFLOP/s of the metric's
+    accounting (4 * D * B_i * B_j per selected pair for the forward); the
+    oracle's time for the whole fwd+bwd layer at that rate is an
+    extrapolation and labelled as one."""
     import numpy as np
-    import torch
 
     from dynamic_block_sparse_zone_amd import synth
     from oracle import oracle as O
@@ -242,26 +253,34 @@ def cpu_baseline(wl, x, nblocks):
     cfg = O.Config(wl.T, wl.H, wl.W, 1, wl.head_dim, top_k=wl.top_k, top_p=wl.top_p,
                    top_k_frac=wl.top_k_frac,
                    volume_mask=wl.volume_mask, fixed_shape=tuple(wl.fixed_shape))
+    t0 = time.perf_counter()
     pl = O.plan(bits["q"], bits["k"], bits["v"], av, cfg)
+    t_plan = time.perf_counter() - t0
     lens = pl.blk_len[: pl.nblk(0)]
-    order = np.argsort(lens, kind="stable")
     rng = np.random.default_rng(0)
-    small = order[: max(nblocks * 8, nblocks)]
-    pick = sorted(rng.choice(small, min(nblocks, len(small)), replace=False).tolist())
+    pool = np.nonzero(lens == lens.min())[0]
+    pick = sorted(rng.choice(pool, min(nblocks, len(pool)), replace=False).tolist())
     items = [(0, int(i)) for i in pick]
+    t0 = time.perf_counter()
     pairs = 0
     for _, i in items:
         sel = O.select_row(pl, 0, i)
         pairs += int(lens[i]) * int(pl.blk_len[sel].sum())
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t_sel = time.perf_counter() - t0
     t0 = time.perf_counter()
     O.attn_fwd(bits["q"], bits["k"], bits["v"], pl, items)
     dt = time.perf_counter() - t0
-    flops = 4.0 * wl.head_dim * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, len(items)),
-            "kind": "oracle",
-            "sample": f"fp64 oracle forward of {len(items)} query blocks of head 0 "
-                      f"({pairs} selected token pairs, {dt:.1f} s)"}
+    rate = 4.0 * wl.head_dim * pairs / dt
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s",
+            "cores": min(threads, len(items)), "kind": "oracle",
+            "sample": f"fp64 oracle forward of {len(items)} random {int(lens.min())}-token "
+                      f"query blocks of head 0 ({pairs} selected token pairs, {dt:.1f} s on "
+                      f"{min(threads, len(items))} threads); oracle plan of head 0 to the "
+                      f"pooled means {t_plan:.1f} s, scores + selection of the "
+                      f"{len(items)} rows {t_sel:.2f} s",
+            "extrapolated_layer_s": round(step_flops / rate, 1),
+            "extrapolated_layer_note": "fwd+bwd flops of the whole layer at the sampled "
+                                       "forward rate (an extrapolation, not a measurement)"}
 
 
 def main():
@@ -309,6 +328,8 @@ def main():
     del pl
 
     long_steps = wl.N >= 500_000
+    deadline = T_PROCESS + args.time_budget
+    cpu_reserve = 0.0 if args.no_cpu else 30.0
 
     def note(msg):
         # progress of multi-second steps (the plan already synchronises)
@@ -326,37 +347,77 @@ def main():
             note("backward done")
         return p
 
+    # warm-up, part one: a small grid through every kernel of the step, so
+    # that no code object is loaded inside a timed step
+    sw = synth.WORKLOADS["check"]
+    xs = synth.make_inputs(sw, device=dev, with_grad=True)
+    ps = prism.plan(xs["q"], xs["k"], xs["v"], xs["av"], T=sw.T, H=sw.H, W=sw.W,
+                    top_k=sw.top_k, top_p=sw.top_p, need_backward=not args.fwd_only)
+    os_, ls_ = prism.attn_fwd(ps, xs["q"], xs["k"], xs["v"])
+    if grads is not None:
+        prism.attn_bwd(ps, xs["q"], xs["k"], xs["v"], os_, ls_, xs["do"])
+    torch.cuda.synchronize()
+    ps.close()
+    del ps, xs, os_, ls_
+    print(f"[bench] small-grid warm-up done at {time.time() - T_PROCESS:.1f}s", file=sys.stderr,
+          flush=True)
+
+    # warm-up, part two: full-size steps while the requested timed steps
+    # still fit the budget after one more
+    warm_done, d_step = 0, None
     for i in range(args.warmup):
+        if d_step is not None and \
+                deadline - time.time() - cpu_reserve < (1 + args.steps) * d_step:
+            break
+        tw = time.time()
         step().close()
         torch.cuda.synchronize()
-        print(f"[bench] warmup step {i} done", file=sys.stderr, flush=True)
+        d_step = time.time() - tw
+        warm_done += 1
+        print(f"[bench] warmup step {i} done in {d_step:.1f}s", file=sys.stderr, flush=True)
+
+    # timed steps: up to --steps, as many as fit before the deadline (at
+    # least one); each bracketed by its own events, all on the stream the
+    # library launches on
     prism.timing_enable(True)
     prism.timing_read()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = []
     t_start = time.perf_counter()
-    ev0.record()
     last = None
     for i in range(args.steps):
+        if i > 0 and deadline - time.time() - cpu_reserve < 1.05 * d_step:
+            break
         if last is not None:
             last.close()
+        ts = time.time()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         last = step()
-    ev1.record()
-    torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        d_step = time.time() - ts
+        evs.append((e0, e1))
+        if long_steps:
+            print(f"[bench] timed step {i} done in {d_step:.1f}s", file=sys.stderr, flush=True)
     wall = time.perf_counter() - t_start
     stages = prism.timing_read()
     prism.timing_enable(False)
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    n_steps = len(evs)
+    per_step = sorted(a.elapsed_time(b) for a, b in evs)
+    ms_step = evs[0][0].elapsed_time(evs[-1][1]) / n_steps
+    ms_median = per_step[n_steps // 2] if n_steps % 2 else \
+        0.5 * (per_step[n_steps // 2 - 1] + per_step[n_steps // 2])
     info = last.info()
-    print(f"[bench] timed {args.steps} step(s): {ms_step:.1f} ms/step (wall {wall:.1f}s)",
-          file=sys.stderr, flush=True)
+    print(f"[bench] timed {n_steps} step(s): {ms_step:.1f} ms/step, median {ms_median:.1f} "
+          f"(wall {wall:.1f}s)", file=sys.stderr, flush=True)
 
     D = wl.head_dim
     pairs = info["pair_tokens"]
     per_pair = 4 + (0 if args.fwd_only else 10)
     flops = per_pair * D * pairs
     value = flops / (ms_step * 1e-3) / 1e12
-    ms = {name: tot / args.steps for name, (cnt, tot) in stages.items()}
+    ms = {name: tot / n_steps for name, (cnt, tot) in stages.items()}
     attn_ms = sum(ms.get(s, 0.0) for s in ("attn.fwd", "bwd.prep", "bwd.dkdv", "bwd.dq"))
     # dominant kernel and its roofline
     cand = {s: stages[s] for s in FLOP_PER_PAIR if s in stages}
@@ -377,9 +438,16 @@ def main():
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": n_steps,
+        "warmup": warm_done,
         "ms_per_step": round(ms_step, 2),
+        "steps_requested": args.steps,
+        "warmup_requested": args.warmup,
+        "warmup_note": "a small-grid pass through every kernel, then full-size warm-up steps "
+                       "while the timed steps still fit the time budget",
+        "ms_per_step_median": round(ms_median, 2),
+        "ms_per_step_all": [round(t, 2) for t in per_step],
+        "time_budget_s": args.time_budget,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -403,8 +471,8 @@ def main():
         "plan_ms": round(plan_ms, 2),
         "plan_stats_gbs": round(tensor_bytes / (ms["plan.stats"] * 1e-3) / 1e9, 1)
         if ms.get("plan.stats") else None,
-        "plan_permute_gbs": round(5 * tensor_bytes / (ms["plan.permute"] * 1e-3) / 1e9, 1)
-        if ms.get("plan.permute") else None,
+        "plan_pool_gbs": round(2 * tensor_bytes / (ms["plan.pool"] * 1e-3) / 1e9, 1)
+        if ms.get("plan.pool") else None,
         "selected_pairs": info["nnz"],
         "selected_token_pairs": pairs,
         "density": round(info["nnz"] / nblk2, 4) if nblk2 else None,
@@ -421,11 +489,17 @@ def main():
         torch.cuda.synchronize()
         del a, b
     if not args.no_cpu:
-        nb = args.cpu_blocks or max(1, min(16, os.cpu_count() or 1))
-        print(f"[bench] cpu baseline: oracle on {nb} query blocks", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, x, nb)
+        threads = int(os.environ.get("OMP_NUM_THREADS", 0) or os.cpu_count() or 1)
+        nb = args.cpu_blocks or threads
+        print(f"[bench] cpu baseline: oracle on {nb} query blocks, {threads} threads",
+              file=sys.stderr, flush=True)
+        tc = time.time()
+        out["cpu_baseline"] = cpu_baseline(wl, x, nb, threads, flops)
+        print(f"[bench] cpu baseline done in {time.time() - tc:.1f}s", file=sys.stderr,
+              flush=True)
     else:
         out["cpu_baseline"] = None
+    out["process_s"] = round(time.time() - T_PROCESS, 1)
     print(json.dumps(out), flush=True)
 
 

@@ -21,17 +21,24 @@ PRISM_ESTATE = 5
 PRISM_F32 = 0
 PRISM_BF16 = 1
 
+SHAPE_MAPS = {"power": 0, "isotropic": 1, "softmax": 2, "rank": 3, "entropy": 4}
+SCHEDULES = {"constant": 0, "linear": 1, "cosine": 2}
+
+
 ARRAYS = {
     "zone_stats": 0, "audio_stats": 1, "shape_id": 2, "blk_off": 3, "blk_start": 4,
     "qbar": 5, "kbar": 6, "qexp": 7, "kexp": 8, "row_ptr": 9, "col_idx": 10,
     "colt_ptr": 11, "colt_idx": 12, "perm": 13, "qgrid": 14, "kgrid": 15, "kv_order": 16,
+    "blk_org": 17, "cuts": 18,
 }
 
 EXPORTED = [
     "prism_config_default", "prism_config_check", "prism_plan_workspace_size",
     "prism_plan_create", "prism_plan_destroy", "prism_attn_fwd",
-    "prism_attn_bwd_workspace_size", "prism_attn_bwd", "prism_block_scores",
+    "prism_attn_bwd_workspace_size", "prism_attn_bwd", "prism_av_cross_attn",
+    "prism_block_scores",
     "prism_plan_array_bytes", "prism_plan_export", "prism_plan_info", "prism_candidate",
+    "prism_schedule_value",
     "prism_status_str", "prism_timing_enable", "prism_timing_read",
 ]
 
@@ -43,7 +50,8 @@ class PrismConfig(ctypes.Structure):
         ("top_k", ctypes.c_int32), ("top_k_frac", ctypes.c_float), ("top_p", ctypes.c_float),
         ("volume_mask", ctypes.c_uint32), ("fixed_shape", ctypes.c_int32 * 3),
         ("eps", ctypes.c_float), ("tau128", ctypes.c_float), ("tau256", ctypes.c_float),
-        ("need_backward", ctypes.c_int32),
+        ("need_backward", ctypes.c_int32), ("shape_map", ctypes.c_int32),
+        ("alpha", ctypes.c_float), ("cut_threshold", ctypes.c_float),
     ]
 
 
@@ -51,7 +59,7 @@ class PrismPlanInfo(ctypes.Structure):
     _fields_ = [
         ("total_blocks", ctypes.c_int64), ("nnz", ctypes.c_int64),
         ("max_blocks_per_head", ctypes.c_int64), ("pair_tokens", ctypes.c_double),
-        ("shape_hist", ctypes.c_int64 * 16),
+        ("shape_hist", ctypes.c_int64 * 16), ("kv_persistent", ctypes.c_int32),
     ]
 
 
@@ -90,11 +98,14 @@ def lib() -> ctypes.CDLL:
         L.prism_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.prism_attn_bwd_workspace_size.argtypes = [cfgp, ctypes.POINTER(sz)]
         L.prism_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.prism_av_cross_attn.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp]
         L.prism_block_scores.argtypes = [vp, i32, vp, vp]
         L.prism_plan_array_bytes.argtypes = [vp, i32, ctypes.POINTER(sz)]
         L.prism_plan_export.argtypes = [vp, i32, vp, sz, vp]
         L.prism_plan_info.argtypes = [vp, ctypes.POINTER(PrismPlanInfo), vp]
         L.prism_candidate.argtypes = [i32, ctypes.POINTER(ctypes.c_int32)]
+        L.prism_schedule_value.argtypes = [i32, i64, i64, ctypes.c_float, ctypes.c_float,
+                                           ctypes.POINTER(ctypes.c_float)]
         L.prism_timing_enable.argtypes = [i32]
         L.prism_timing_read.argtypes = [ctypes.POINTER(PrismStageTime), i32,
                                         ctypes.POINTER(ctypes.c_int32)]

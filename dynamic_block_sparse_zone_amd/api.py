@@ -24,7 +24,7 @@ _NP = {
     "blk_off": np.int64, "blk_start": np.int32, "qbar": np.float32, "kbar": np.float32,
     "qexp": np.int32, "kexp": np.int32, "row_ptr": np.int64, "col_idx": np.int32,
     "colt_ptr": np.int64, "colt_idx": np.int32, "perm": np.int32, "qgrid": np.uint16,
-    "kgrid": np.uint16, "kv_order": np.int32,
+    "kgrid": np.uint16, "kv_order": np.int32, "blk_org": np.int32, "cuts": np.uint8,
 }
 
 
@@ -38,7 +38,8 @@ def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
 
 def make_config(T, H, W, heads, head_dim, dtype, *, top_k=16, top_k_frac=0.0, top_p=0.9,
                 volume_mask=7, fixed_shape=(0, 0, 0), eps=1e-4, tau128=0.5, tau256=0.25,
-                need_backward=True) -> nat.PrismConfig:
+                need_backward=True, shape_map="power", alpha=0.5,
+                cut_threshold=0.0) -> nat.PrismConfig:
     c = nat.PrismConfig()
     nat.lib().prism_config_default(ctypes.byref(c))
     c.T, c.H, c.W, c.heads, c.head_dim = T, H, W, heads, head_dim
@@ -49,6 +50,9 @@ def make_config(T, H, W, heads, head_dim, dtype, *, top_k=16, top_k_frac=0.0, to
         c.fixed_shape[i] = int(fixed_shape[i])
     c.eps, c.tau128, c.tau256 = float(eps), float(tau128), float(tau256)
     c.need_backward = 1 if need_backward else 0
+    c.shape_map = nat.SHAPE_MAPS[shape_map] if isinstance(shape_map, str) else int(shape_map)
+    c.alpha = float(alpha)
+    c.cut_threshold = float(cut_threshold)
     return c
 
 
@@ -68,7 +72,7 @@ class Plan:
         self.workspace = workspace
         self.nnz = nnz
         self.device = q.device
-        self._k, self._v = k, v  # kept alive: the plan holds their permuted copies
+        self._k, self._v = k, v  # the tensors the plan was built from
 
     def close(self):
         if self.handle:
@@ -97,13 +101,18 @@ class Plan:
                                             _stream(self.device)), "prism_plan_info")
         return {"total_blocks": inf.total_blocks, "nnz": inf.nnz,
                 "max_blocks_per_head": inf.max_blocks_per_head,
-                "pair_tokens": inf.pair_tokens, "shape_hist": list(inf.shape_hist)}
+                "pair_tokens": inf.pair_tokens, "shape_hist": list(inf.shape_hist),
+                "kv_persistent": bool(inf.kv_persistent)}
 
 
 def plan(q, k, v, av_norm=None, *, T, H, W, top_k=16, top_k_frac=0.0, top_p=0.9,
          volume_mask=7, fixed_shape=(0, 0, 0), eps=1e-4, tau128=0.5, tau256=0.25,
-         need_backward=True, nnz_capacity=None, workspace=None) -> Plan:
-    """Stages one to three (shapes, re-layout, pooling, selection)."""
+         need_backward=True, shape_map="power", alpha=0.5, cut_threshold=0.0,
+         nnz_capacity=None, workspace=None) -> Plan:
+    """Stages one to three (shapes, block table, pooling, selection).
+    shape_map: "power" (b_d ~ g_d^-alpha; alpha = 1/2 is the pages' method),
+    "isotropic", "softmax", "rank" or "entropy" (the pages' ablations).
+    cut_threshold > 0: shot-cut-aware temporal zones."""
     heads, N, D = q.shape
     assert N == T * H * W and k.shape == q.shape and v.shape == q.shape
     assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
@@ -112,7 +121,8 @@ def plan(q, k, v, av_norm=None, *, T, H, W, top_k=16, top_k_frac=0.0, top_p=0.9,
         assert av_norm.dtype == torch.float32 and av_norm.numel() == N and av_norm.is_contiguous()
     cfg = make_config(T, H, W, heads, D, q.dtype, top_k=top_k, top_k_frac=top_k_frac,
                       top_p=top_p, volume_mask=volume_mask, fixed_shape=fixed_shape, eps=eps,
-                      tau128=tau128, tau256=tau256, need_backward=need_backward)
+                      tau128=tau128, tau256=tau256, need_backward=need_backward,
+                      shape_map=shape_map, alpha=alpha, cut_threshold=cut_threshold)
     nat.check(nat.lib().prism_config_check(ctypes.byref(cfg)), "prism_config_check")
     Z = (T // 8) * (H // 8) * (W // 8)
     worst = heads * (8 * Z) ** 2
@@ -168,12 +178,44 @@ def attn_bwd(pl: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace
     return dq, dk, dv
 
 
+def av_cross_attn(q, ka, va, o=None, norm=None, want_o=False):
+    """The A->V norm map: h_hat = softmax(q ka^T / sqrt(D)) va per head for
+    the video queries q [heads, N, D] over the audio keys and values
+    [heads, Na, D], and norm [N] = ||h_hat_n||_2 over heads and channels (the
+    av_norm of the next layer's plan).  Returns (norm, o); o is None unless
+    given or want_o."""
+    heads, N, D = q.shape
+    assert ka.shape == va.shape and ka.shape[0] == heads and ka.shape[2] == D
+    assert q.is_contiguous() and ka.is_contiguous() and va.is_contiguous()
+    assert q.dtype == ka.dtype == va.dtype
+    if o is None and want_o:
+        o = torch.empty_like(q)
+    if norm is None:
+        norm = torch.empty(N, dtype=torch.float32, device=q.device)
+    dt = nat.PRISM_BF16 if q.dtype == torch.bfloat16 else nat.PRISM_F32
+    nat.check(nat.lib().prism_av_cross_attn(_ptr(q), _ptr(ka), _ptr(va), heads, N,
+                                            ka.shape[1], D, dt, _ptr(o), _ptr(norm),
+                                            _stream(q.device)), "prism_av_cross_attn")
+    return norm, o
+
+
 def block_scores(pl: Plan, head: int) -> torch.Tensor:
     nblk = int(pl.export("blk_off")[head + 1] - pl.export("blk_off")[head])
     out = torch.empty((nblk, nblk), dtype=torch.float32, device=pl.device)
     nat.check(nat.lib().prism_block_scores(pl.handle, int(head), _ptr(out), _stream(pl.device)),
               "prism_block_scores")
     return out
+
+
+def schedule_value(kind, step: int, steps: int, v0: float, v1: float) -> float:
+    """A per-step sparsity schedule (prism_schedule_value): the value at step
+    `step` of `steps`, from v0 at the first step to v1 at the last; kind is
+    "constant", "linear" or "cosine"."""
+    out = ctypes.c_float()
+    k = nat.SCHEDULES[kind] if isinstance(kind, str) else int(kind)
+    nat.check(nat.lib().prism_schedule_value(k, int(step), int(steps), float(v0), float(v1),
+                                             ctypes.byref(out)), "prism_schedule_value")
+    return out.value
 
 
 def candidate(i: int) -> tuple:

@@ -104,7 +104,6 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
   const int64_t maxblk = 8 * Z;
   const int64_t G = (int64_t)c.heads * maxblk;
   const int D = c.head_dim;
-  const int es = c.dtype == PRISM_BF16 ? 2 : 4;
   P->T = c.T;
   P->H = c.H;
   P->W = c.W;
@@ -120,6 +119,7 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
   P->nblk = A.take<int32_t>(c.heads);
   P->blk_off = A.take<int64_t>(c.heads + 1);
   P->blk_start = A.take<int32_t>(G);
+  P->blk_org = A.take<int32_t>(G);
   P->blk_shape = A.take<uint8_t>(G);
   P->blk_head = A.take<int32_t>(G);
   P->qbar = A.take<float>(G * D);
@@ -128,8 +128,6 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
   P->kgrid = A.take<uint16_t>(G * D);
   P->qexp = A.take<int32_t>(G);
   P->kexp = A.take<int32_t>(G);
-  P->kp = A.take<char>((int64_t)c.heads * N * D * es);
-  P->vp = A.take<char>((int64_t)c.heads * N * D * es);
   P->scores = A.take<float>(maxblk * maxblk);
   P->row_cnt = A.take<int32_t>(G);
   P->row_key = A.take<uint32_t>(G);
@@ -155,6 +153,10 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
     P->sync = nullptr;
   }
   P->kv_persist = 0;
+  P->cut_part = A.take<double>((int64_t)c.T * c.heads);
+  P->cut_energy = A.take<double>(c.T);
+  P->cuts = A.take<uint8_t>(c.T);
+  P->zt_cap = A.take<int32_t>(c.T / 8);
   P->col_idx = A.take<int32_t>(cap);
   P->colt_idx = c.need_backward ? A.take<int32_t>(cap) : nullptr;
   P->cap = cap;
@@ -182,6 +184,9 @@ void prism_config_default(prism_config* c) {
   c->tau128 = 0.5f;
   c->tau256 = 0.25f;
   c->need_backward = 1;
+  c->shape_map = PRISM_MAP_POWER;
+  c->alpha = 0.5f;
+  c->cut_threshold = 0.0f;
 }
 
 prism_status prism_config_check(const prism_config* c) {
@@ -202,6 +207,9 @@ prism_status prism_config_check(const prism_config* c) {
   if (!(c->eps > 0.0f) || !isfinite(c->eps)) return PRISM_EINVAL;
   if (!(c->tau256 >= 0.0f) || !(c->tau128 >= c->tau256) || !isfinite(c->tau128))
     return PRISM_EINVAL;
+  if (c->shape_map < PRISM_MAP_POWER || c->shape_map > PRISM_MAP_ENTROPY) return PRISM_EINVAL;
+  if (!(c->alpha >= 0.0f) || !isfinite(c->alpha)) return PRISM_EINVAL;
+  if (!(c->cut_threshold >= 0.0f) || !isfinite(c->cut_threshold)) return PRISM_EINVAL;
   return PRISM_OK;
 }
 
@@ -247,6 +255,7 @@ prism_status prism_plan_create(const prism_config* c, const void* q, const void*
     ok = ok && launch_audio_stats(av_norm, c->H, c->W, P.Z, P.astats, st);
   else
     PRISM_HIP(hipMemsetAsync(P.astats, 0, sizeof(float) * 4 * P.Z, st));
+  if (c->cut_threshold > 0.0f) ok = ok && launch_cuts(P, v, c->cut_threshold, st);
   stage_end(st);
   stage_begin("plan.shapes", st);
   ok = ok && launch_shapes(P, av_norm != nullptr, *c, fixed_id, st);
@@ -260,8 +269,8 @@ prism_status prism_plan_create(const prism_config* c, const void* q, const void*
   int64_t maxb = 0;
   for (int h = 0; h < c->heads; h++) maxb = std::max(maxb, off[h + 1] - off[h]);
 
-  stage_begin("plan.permute", st);
-  ok = launch_permute_pool(P, q, k, v, st);
+  stage_begin("plan.pool", st);
+  ok = launch_pool(P, q, k, st);
   stage_end(st);
   PRISM_HIP(hipMemsetAsync(P.counters, 0, sizeof(int64_t) * 8, st));
   for (int h = 0; h < c->heads && ok; h++) {
@@ -324,7 +333,7 @@ prism_status prism_attn_fwd(const prism_plan_t* plan, const void* q, const void*
     return PRISM_EUNSUPPORTED;
   PRISM_HIP(hipGetLastError());
   stage_begin("attn.fwd", (hipStream_t)stream);
-  bool ok = launch_attn_fwd(plan->P, q, o, lse, (hipStream_t)stream);
+  bool ok = launch_attn_fwd(plan->P, q, k, v, o, lse, (hipStream_t)stream);
   stage_end((hipStream_t)stream);
   return ok ? PRISM_OK : PRISM_EDEVICE;
 }
@@ -337,16 +346,21 @@ prism_status prism_attn_bwd_workspace_size(const prism_config* c, size_t* bytes)
   Arena A{nullptr};
   A.take<float>((int64_t)c->heads * N);
   A.take<float>((int64_t)c->heads * N);
-  A.take<uint16_t>((int64_t)c->heads * N * c->head_dim);
-  A.take<uint16_t>((int64_t)c->heads * N * c->head_dim);
   *bytes = A.off + 256;
   return PRISM_OK;
 }
 
-prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void* k,
-                            const void* v, const void* o, const float* lse, const void* d_o,
-                            void* dq, void* dk, void* dv, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward with its scratch (Delta and log2(e) * LSE per token) carved
+// from `workspace`.  `timed`: record the stage events of the
+// measurement support (which may create HIP events).
+prism_status bwd_run(const prism_plan_t* plan, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* d_o, void* dq, void* dk,
+                     void* dv, void* workspace, size_t workspace_bytes, hipStream_t st,
+                     bool timed) {
   if (!plan || !q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv || !workspace)
     return PRISM_EINVAL;
   if (k != plan->k || v != plan->v) return PRISM_ESTATE;
@@ -359,20 +373,51 @@ prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void*
   const int64_t N = plan->P.N;
   Arena A{(char*)workspace};
   BwdDev B;
+  B.q = q;
+  B.k = k;
+  B.v = v;
+  B.d_o = d_o;
   B.delta = A.take<float>((int64_t)c.heads * N);
-  B.lse_p = A.take<float>((int64_t)c.heads * N);
-  B.qp = A.take<uint16_t>((int64_t)c.heads * N * c.head_dim);
-  B.dop = A.take<uint16_t>((int64_t)c.heads * N * c.head_dim);
+  B.lse2 = A.take<float>((int64_t)c.heads * N);
   PRISM_HIP(hipGetLastError());
-  hipStream_t st = (hipStream_t)stream;
-  stage_begin("bwd.prep", st);
-  bool ok = launch_bwd_prep(plan->P, B, q, o, lse, d_o, st);
-  stage_end(st);
-  stage_begin("bwd.dkdv", st);
+  if (timed) stage_begin("bwd.prep", st);
+  bool ok = launch_bwd_prep(plan->P, B, o, lse, st);
+  if (timed) stage_end(st);
+  if (timed) stage_begin("bwd.dkdv", st);
   ok = ok && launch_bwd_dkdv(plan->P, B, dk, dv, st);
-  stage_end(st);
-  stage_begin("bwd.dq", st);
+  if (timed) stage_end(st);
+  if (timed) stage_begin("bwd.dq", st);
   ok = ok && launch_bwd_dq(plan->P, B, dq, st);
+  if (timed) stage_end(st);
+  return ok ? PRISM_OK : PRISM_EDEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void* k,
+                            const void* v, const void* o, const float* lse, const void* d_o,
+                            void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return bwd_run(plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes,
+                 (hipStream_t)stream, true);
+}
+
+prism_status prism_av_cross_attn(const void* q, const void* ka, const void* va, int32_t heads,
+                                 int64_t n_video, int32_t n_audio, int32_t head_dim,
+                                 int32_t dtype, void* o, float* norm_out, void* stream) {
+  if (!q || !ka || !va || !norm_out || heads <= 0 || n_video <= 0 || n_audio <= 0)
+    return PRISM_EINVAL;
+  if (dtype != PRISM_BF16 || head_dim != 128) return PRISM_EUNSUPPORTED;
+  // rows come in work-groups of 256 and audio keys in tiles of 64; one
+  // head's rows are addressed with 32-bit byte offsets
+  if (n_video % 256 || n_audio % 64) return PRISM_EINVAL;
+  if (n_video >= ((int64_t)1 << 24) || n_audio >= (1 << 24)) return PRISM_EUNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  PRISM_HIP(hipGetLastError());
+  stage_begin("av.cross", st);
+  const bool ok = launch_av_cross(q, ka, va, heads, n_video, n_audio, o, norm_out, st);
   stage_end(st);
   return ok ? PRISM_OK : PRISM_EDEVICE;
 }
@@ -416,6 +461,8 @@ static const void* array_ptr(const prism_plan_t* pl, int which, size_t* bytes) {
     case PRISM_ARR_KV_ORDER:
       *bytes = c.need_backward ? sizeof(int32_t) * c.heads * (P.N / 128) : 0;
       return P.korder;
+    case PRISM_ARR_BLK_ORG: *bytes = sizeof(int32_t) * G; return P.blk_org;
+    case PRISM_ARR_CUTS: *bytes = c.cut_threshold > 0.0f ? (size_t)c.T : 0; return P.cuts;
     default: *bytes = 0; return nullptr;
   }
 }
@@ -424,13 +471,13 @@ prism_status prism_plan_array_bytes(const prism_plan_t* plan, int32_t which, siz
   if (!plan || !bytes) return PRISM_EINVAL;
   const void* p = array_ptr(plan, which, bytes);
   if (!p && *bytes) return PRISM_EINVAL;
-  if (which < 0 || which > PRISM_ARR_KV_ORDER) return PRISM_EINVAL;
+  if (which < 0 || which > PRISM_ARR_CUTS) return PRISM_EINVAL;
   return PRISM_OK;
 }
 
 prism_status prism_plan_export(const prism_plan_t* plan, int32_t which, void* dst,
                                size_t dst_bytes, void* stream) {
-  if (!plan || !dst || which < 0 || which > PRISM_ARR_KV_ORDER) return PRISM_EINVAL;
+  if (!plan || !dst || which < 0 || which > PRISM_ARR_CUTS) return PRISM_EINVAL;
   size_t bytes = 0;
   const void* p = array_ptr(plan, which, &bytes);
   if (dst_bytes < bytes) return PRISM_EINVAL;
@@ -452,6 +499,7 @@ prism_status prism_plan_info(const prism_plan_t* plan, prism_plan_info_t* info, 
   info->total_blocks = G;
   info->nnz = plan->nnz;
   info->max_blocks_per_head = plan->max_blocks;
+  info->kv_persistent = plan->P.kv_persist;
   PRISM_HIP(hipGetLastError());
   if (!launch_sum_i64(plan->P.row_cost, G, plan->P.counters + 4, st)) return PRISM_EDEVICE;
   int64_t pt = 0;
@@ -462,6 +510,23 @@ prism_status prism_plan_info(const prism_plan_t* plan, prism_plan_info_t* info, 
   PRISM_HIP(hipStreamSynchronize(st));
   info->pair_tokens = (double)pt;
   for (uint8_t s : sid) info->shape_hist[s < 16 ? s : 0]++;
+  return PRISM_OK;
+}
+
+prism_status prism_schedule_value(int32_t kind, int64_t step, int64_t steps, float v0, float v1,
+                                  float* out) {
+  if (!out || steps < 1 || !isfinite(v0) || !isfinite(v1)) return PRISM_EINVAL;
+  double s = steps > 1 ? (double)step / (double)(steps - 1) : 0.0;
+  s = s < 0.0 ? 0.0 : s > 1.0 ? 1.0 : s;
+  const double a = v0, b = v1;
+  double v;
+  switch (kind) {
+    case PRISM_SCHED_CONSTANT: v = a; break;
+    case PRISM_SCHED_LINEAR: v = a + (b - a) * s; break;
+    case PRISM_SCHED_COSINE: v = b + (a - b) * (1.0 + cos(M_PI * s)) * 0.5; break;
+    default: return PRISM_EINVAL;
+  }
+  *out = (float)v;
   return PRISM_OK;
 }
 

@@ -5,8 +5,9 @@
 //   dV = P^T dO,  dK = dS^T Q / sqrt(D),  dQ = dS K / sqrt(D).
 //
 // gfx950 design (bf16, head_dim 128), deterministic (no atomics):
-//  * prep: Q and dO gathered into the permuted, swizzled tile layout of K/V;
-//    Delta and log2(e) * LSE per permuted row;
+//  * prep: Delta and log2(e) * LSE per token (original order); every tile of
+//    Q, dO, K, V and every LSE / Delta column is gathered straight from the
+//    caller's tensors through the block -> token map;
 //  * dK/dV: a work-group owns 128 permuted key rows (4 waves x 32 keys, K and
 //    V of its keys in registers, dK/dV accumulators pinned to AGPRs) and
 //    walks the query blocks whose S_i holds its key blocks (key-major lists);
@@ -45,48 +46,36 @@ constexpr int kDqWaves = kDqRows / 32;
 constexpr int kDqLoads = 2 * kTile / (kDqWaves * 1024);
 
 // ---------------------------------------------------------------- prep
-// One block of 256 threads per 64-row tile; wave w handles rows w, w+4, ...
-__global__ __launch_bounds__(256) void k_bwd_prep(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ o,
-    const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
-    const uint8_t* __restrict__ shape_id, int H, int W, int Z, int64_t N,
-    uint16_t* __restrict__ qp, uint16_t* __restrict__ dop, float* __restrict__ delta,
-    float* __restrict__ lse2) {
-  const int64_t tpH = N >> 6;
-  const int h = (int)(blockIdx.x / tpH);
-  const int64_t r0 = (blockIdx.x - (int64_t)h * tpH) << 6;
-  const int m = (int)(r0 >> 9);
-  const Shape sh = d_shapes[shape_id[(int64_t)h * Z + m]];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int i = wv; i < 64; i += 4) {
-    const int64_t p = r0 + i;
-    const int64_t tok = token_of(sh, m, (int)(p & 511), H, W);
-    const int64_t src = ((int64_t)h * N + tok) * 128 + lane * 2;
-    const uint32_t qv = *(const uint32_t*)(q + src);
-    const uint32_t dv = *(const uint32_t*)(d_o + src);
-    const uint32_t ov = *(const uint32_t*)(o + src);
-    const int64_t dst = ((int64_t)h * N + p) * 128 +
-                        (((lane >> 2) ^ chunk_swizzle(i)) << 3) + (lane & 3) * 2;
-    *(uint32_t*)(qp + dst) = qv;
-    *(uint32_t*)(dop + dst) = dv;
-    float s = __uint_as_float(dv << 16) * __uint_as_float(ov << 16);
-    s = __builtin_fmaf(__uint_as_float(dv & 0xffff0000u), __uint_as_float(ov & 0xffff0000u), s);
+// Per token row (all heads, original order): Delta = rowsum(dO * O) and
+// log2(e) * LSE.  One wave per row, 8 rows per block of 512 threads; lane l
+// holds channels 2l, 2l + 1.
+__global__ __launch_bounds__(512) void k_bwd_prep(const uint16_t* __restrict__ o,
+                                                  const uint16_t* __restrict__ d_o,
+                                                  const float* __restrict__ lse, int64_t rows,
+                                                  float* __restrict__ delta,
+                                                  float* __restrict__ lse2) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint32_t dv = *(const uint32_t*)(d_o + row * 128 + lane * 2);
+  const uint32_t ov = *(const uint32_t*)(o + row * 128 + lane * 2);
+  float s = __uint_as_float(dv << 16) * __uint_as_float(ov << 16);
+  s = __builtin_fmaf(__uint_as_float(dv & 0xffff0000u), __uint_as_float(ov & 0xffff0000u), s);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (lane == 0) {
-      delta[(int64_t)h * N + p] = s;
-      lse2[(int64_t)h * N + p] = lse[(int64_t)h * N + tok] * 1.44269504088896340736f;
-    }
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) {
+    delta[row] = s;
+    lse2[row] = lse[row] * 1.44269504088896340736f;
   }
 }
 
 // ---------------------------------------------------------------- dK, dV
 __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
-    const uint16_t* __restrict__ qp, const uint16_t* __restrict__ dop,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse2, const float* __restrict__ delta,
-    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint8_t* __restrict__ shape_id, const int32_t* __restrict__ zone_base,
-    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_start,
+    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_org,
     const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ colt_ptr,
     const int32_t* __restrict__ colt_idx, int H, int W, int Z, int64_t N, float c_log2,
     float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t nunits,
@@ -121,12 +110,12 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
 
   // this wave's 32 keys: K and V rows as MFMA B operands (k = channel)
   const int64_t hrow = (int64_t)h * N;
-  const int64_t krow = hrow + r0 + wv * 32 + l32;
+  const int64_t ktok = token_of(sh, m, (int)((r0 + wv * 32 + l32) & 511), H, W);
   bf16x8 kr[8], vr[8];
 #pragma unroll
   for (int kk = 0; kk < 8; kk++) {
-    kr[kk] = row_chunk(kp, krow, 2 * kk + hl);
-    vr[kk] = row_chunk(vp, krow, 2 * kk + hl);
+    kr[kk] = row_chunk(k, hrow + ktok, 2 * kk + hl);
+    vr[kk] = row_chunk(v, hrow + ktok, 2 * kk + hl);
   }
   // the key fragments land before any tile load is issued, so the ring's
   // waits only ever concern tiles (the empty asm consumes them here)
@@ -147,43 +136,46 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
   tr_offsets(lane, to);
 
   TileIter it;
-  it.init(colt_ptr, colt_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_start,
+  it.init(colt_ptr, colt_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_org,
           blk_shape, hoff);
-  const __amdgpu_buffer_rsrc_t rsQ = buffer_of(qp + hrow * 128, (uint32_t)(N * 256));
-  const __amdgpu_buffer_rsrc_t rsD = buffer_of(dop + hrow * 128, (uint32_t)(N * 256));
+  const __amdgpu_buffer_rsrc_t rsQ = buffer_of(q + hrow * 128, (uint32_t)(N * 256));
+  const __amdgpu_buffer_rsrc_t rsD = buffer_of(d_o + hrow * 128, (uint32_t)(N * 256));
   // waves 0 and 2 bring the LSE column, waves 1 and 3 Delta (both pairs write
   // the same values), so that every wave issues the same nine loads per tile
   const __amdgpu_buffer_rsrc_t rsC =
       buffer_of((wvu & 1) ? delta + hrow : lse2 + hrow, (uint32_t)(N * 4));
   const uint32_t lring = lds_offset(ring);
   const uint32_t lcol = lds_offset(ringc) + (wvu & 1) * 256;
-  auto stage = [&](int b, int64_t row) {
+  // tile t of the query block (first token org, shape sid) from Q and dO,
+  // with its LSE or Delta column, into slot b
+  auto stage = [&](int b, uint32_t org, int sid, int t) {
     const uint32_t o = lring + b * 2 * kTile;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const uint32_t piece = i * 256 + wvu * 64;
-      const uint32_t src = (uint32_t)row * 256 + (piece + lane) * 16;
+      const uint32_t src = tile_src16(org, sid, t, piece + lane, H, W);
       dma16(rsQ, src, o + piece * 16);
       dma16(rsD, src, o + kTile + piece * 16);
     }
-    dma4(rsC, ((uint32_t)row + lane) * 4, lcol + b * 512);
+    dma4(rsC, tile_src4(org, sid, t, lane, H, W), lcol + b * 512);
   };
 
   uint32_t ring_f = 0;  // list masks of the tiles in the ring, a byte per slot
   int nreal = 0;        // real tiles issued; later slots re-read the last one
-  int64_t last_row = 0;
+  uint32_t last_org = 0;
+  int last_sid = 0, last_t = 0;
   auto issue = [&](int b) {
-    int64_t row = last_row;
     uint32_t f = 0;
     if (it.valid) {
-      row = it.row();
+      last_org = it.org();
+      last_sid = it.sid();
+      last_t = it.t;
       f = (uint32_t)it.mask;
-      last_row = row;
       nreal++;
       it.advance();
     }
     ring_f = (ring_f & ~(0xffu << (8 * b))) | (f << (8 * b));
-    stage(b, row);
+    stage(b, last_org, last_sid, last_t);
   };
   issue(0);
   issue(1);
@@ -331,11 +323,11 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
 
 // ---------------------------------------------------------------- dQ
 __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
-    const uint16_t* __restrict__ qp, const uint16_t* __restrict__ dop,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse2, const float* __restrict__ delta,
-    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint8_t* __restrict__ shape_id, const int32_t* __restrict__ zone_base,
-    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_start,
+    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_org,
     const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, int H, int W, int Z, int64_t N, float c_log2,
     float scale, uint16_t* __restrict__ dq) {
@@ -356,18 +348,19 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
   const int mylist = (32 * wvu) / B < nlists ? (32 * wvu) / B : 0;
 
   TileIterS it;
-  it.init(row_ptr, col_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_start,
+  it.init(row_ptr, col_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_org,
           blk_shape, hoff);
 
   // this wave's 32 query rows: Q and dO as MFMA B operands, LSE and Delta of
   // the lane's row
   const int64_t hrow = (int64_t)h * N;
-  const int64_t qrow = hrow + r0 + wv * 32 + l32;
+  const int64_t qtok = token_of(sh, m, (int)((r0 + wv * 32 + l32) & 511), H, W);
+  const int64_t qrow = hrow + qtok;
   bf16x8 qf[8], df[8];
 #pragma unroll
   for (int kk = 0; kk < 8; kk++) {
-    qf[kk] = row_chunk(qp, qrow, 2 * kk + hl);
-    df[kk] = row_chunk(dop, qrow, 2 * kk + hl);
+    qf[kk] = row_chunk(q, qrow, 2 * kk + hl);
+    df[kk] = row_chunk(d_o, qrow, 2 * kk + hl);
   }
   float L = lse2[qrow];
   float Dl = delta[qrow];
@@ -385,33 +378,34 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[db][r] = 0.0f;
 
-  const __amdgpu_buffer_rsrc_t rsK = buffer_of(kp + hrow * 128, (uint32_t)(N * 256));
-  const __amdgpu_buffer_rsrc_t rsV = buffer_of(vp + hrow * 128, (uint32_t)(N * 256));
+  const __amdgpu_buffer_rsrc_t rsK = buffer_of(k + hrow * 128, (uint32_t)(N * 256));
+  const __amdgpu_buffer_rsrc_t rsV = buffer_of(v + hrow * 128, (uint32_t)(N * 256));
   const uint32_t lK = lds_offset(ringK), lV = lds_offset(ringV);
-  auto stage = [&](int b, int64_t row) {
+  auto stage = [&](int b, uint32_t org, int sid, int t) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const uint32_t piece = i * 512 + wvu * 64;
-      const uint32_t src = (uint32_t)row * 256 + (piece + lane) * 16;
+      const uint32_t src = tile_src16(org, sid, t, piece + lane, H, W);
       dma16(rsK, src, lK + b * kTile + piece * 16);
       dma16(rsV, src, lV + b * kTile + piece * 16);
     }
   };
   uint32_t ring_mask = 0;  // list masks of the tiles in the ring, a byte per slot
   int nreal = 0;           // real tiles issued
-  int64_t last_row = 0;
+  uint32_t last_org = 0;
+  int last_sid = 0, last_t = 0;
   auto issue = [&](int b) {
-    int64_t row = last_row;
     uint32_t mask = 0;
     if (it.valid) {
-      row = it.row();
+      last_org = it.org();
+      last_sid = it.sid();
+      last_t = it.t;
       mask = (uint32_t)it.mask;
-      last_row = row;
       nreal++;
       it.advance();
     }
     ring_mask = (ring_mask & ~(0xffu << (8 * b))) | (mask << (8 * b));
-    stage(b, row);
+    stage(b, last_org, last_sid, last_t);
   };
   auto ring_step = [&](int j) {
     __builtin_amdgcn_s_waitcnt(wait_vm(2 * kDqLoads));
@@ -497,9 +491,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
   }
   // no tile load may still be writing LDS when the work-group ends
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
-  const int64_t p = r0 + wv * 32 + l32;
-  const int64_t tok = token_of(sh, m, (int)(p & 511), H, W);
-  uint16_t* row = dq + (hrow + tok) * 128;
+  uint16_t* row = dq + qrow * 128;
 #pragma unroll
   for (int db = 0; db < 4; db++)
 #pragma unroll
@@ -530,13 +522,12 @@ __global__ void k_clear_sync(int32_t* p) { p[threadIdx.x] = 0; }
 static const float kCLog2 = (float)(1.4426950408889634 / 11.313708498984761);
 static const float kScale = (float)(1.0 / 11.313708498984761);
 
-bool launch_bwd_prep(const PlanDev& P, const BwdDev& Bd, const void* q, const void* o,
-                     const float* lse, const void* d_o, hipStream_t st) {
+bool launch_bwd_prep(const PlanDev& P, const BwdDev& Bd, const void* o, const float* lse,
+                     hipStream_t st) {
   if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
-  hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)(P.heads * (P.N >> 6))), dim3(256), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)o, (const uint16_t*)d_o, lse,
-                     P.shape_id, P.H, P.W, P.Z, P.N, (uint16_t*)Bd.qp, (uint16_t*)Bd.dop,
-                     Bd.delta, Bd.lse_p);
+  const int64_t rows = P.heads * P.N;
+  hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)((rows + 7) / 8)), dim3(512), 0, st,
+                     (const uint16_t*)o, (const uint16_t*)Bd.d_o, lse, rows, Bd.delta, Bd.lse2);
   return hipGetLastError() == hipSuccess;
 }
 
@@ -547,9 +538,9 @@ bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& Bd, void* dk, void* dv, hip
   const int64_t nunits = P.heads * (P.N / kKvRows);
   if (P.kv_persist) hipLaunchKernelGGL(k_clear_sync, dim3(1), dim3(128), 0, st, P.sync);
   dim3 grid((unsigned)(P.kv_persist ? persistent_grid() : nunits)), block(kKvWaves * 64);
-  hipLaunchKernelGGL(k_bwd_dkdv, grid, block, 0, st, (const uint16_t*)Bd.qp,
-                     (const uint16_t*)Bd.dop, Bd.lse_p, Bd.delta, (const uint16_t*)P.kp,
-                     (const uint16_t*)P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start,
+  hipLaunchKernelGGL(k_bwd_dkdv, grid, block, 0, st, (const uint16_t*)Bd.q,
+                     (const uint16_t*)Bd.d_o, Bd.lse2, Bd.delta, (const uint16_t*)Bd.k,
+                     (const uint16_t*)Bd.v, P.shape_id, P.zone_base, P.blk_off, P.blk_org,
                      P.blk_shape, P.colt_ptr, P.colt_idx, P.H, P.W, P.Z, P.N, kCLog2, kScale,
                      (uint16_t*)dk, (uint16_t*)dv, nunits, P.korder,
                      P.kv_persist ? P.sync : nullptr);
@@ -559,9 +550,9 @@ bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& Bd, void* dk, void* dv, hip
 bool launch_bwd_dq(const PlanDev& P, const BwdDev& Bd, void* dq, hipStream_t st) {
   if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
   dim3 grid((unsigned)(P.heads * (P.N / kDqRows))), block(kDqWaves * 64);
-  hipLaunchKernelGGL(k_bwd_dq, grid, block, 0, st, (const uint16_t*)Bd.qp,
-                     (const uint16_t*)Bd.dop, Bd.lse_p, Bd.delta, (const uint16_t*)P.kp,
-                     (const uint16_t*)P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start,
+  hipLaunchKernelGGL(k_bwd_dq, grid, block, 0, st, (const uint16_t*)Bd.q,
+                     (const uint16_t*)Bd.d_o, Bd.lse2, Bd.delta, (const uint16_t*)Bd.k,
+                     (const uint16_t*)Bd.v, P.shape_id, P.zone_base, P.blk_off, P.blk_org,
                      P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W, P.Z, P.N, kCLog2, kScale,
                      (uint16_t*)dq);
   return hipGetLastError() == hipSuccess;

@@ -1,10 +1,15 @@
 // Device pieces shared by the sparse-attention kernels (forward, dK/dV, dQ):
 // the walk over selected key blocks, the LDS tile ring and its fragment reads.
 //
-// Tiles.  Permuted K, V (and, in the backward, Q, dO) rows are stored
-// [heads][N][128] bf16 with the 16-byte chunks of every row swizzled
-// (chunk c of row rho at c ^ chunk_swizzle(rho)), so one 64-row tile is a
-// contiguous 16 KB block that is copied verbatim into LDS.
+// Tiles.  A 64-row tile is 64 consecutive rows of one block in the
+// block-contiguous order of the plan, and every block is a whole number of
+// tiles.  Its rows are gathered straight from the caller's [heads][N][128]
+// bf16 tensors (K, V, and in the backward Q, dO) through the closed-form
+// block -> token map (block_row_offset from the block's first token), so no
+// re-laid copy of any tensor exists.  Each lane moves one 16-byte chunk per
+// load and picks the chunk so that LDS row rho holds logical chunk c at
+// c ^ chunk_swizzle(rho); a row is 256 contiguous bytes in HBM, and a wave's
+// load covers four whole rows.
 //
 // Ring.  A work-group keeps kRing tile slots in LDS with kRing - 1 tiles in
 // flight.  Every step issues exactly one tile (past the end of the lists it
@@ -62,6 +67,21 @@ __device__ inline void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t o
       rs, (__attribute__((address_space(3))) void*)(uintptr_t)o, 4, voff, 0, 0, 0);
 }
 
+// Byte offset, in one head's original [N][128] bf16 rows, of the 16-byte
+// chunk that LDS slot `slot` (0..1023: tile row slot >> 4, stored chunk
+// slot & 15) takes for tile t of a block of shape sid whose first token is
+// org.
+__device__ inline uint32_t tile_src16(uint32_t org, int sid, int t, uint32_t slot, int H,
+                                      int W) {
+  const uint32_t rho = slot >> 4;
+  const uint32_t c = (slot & 15u) ^ (uint32_t)chunk_swizzle((int)rho);
+  return (org + block_row_offset(sid, 64u * t + rho, H, W)) * 256u + c * 16u;
+}
+// Byte offset of row rho (0..63) of that tile in a per-token [N] float array.
+__device__ inline uint32_t tile_src4(uint32_t org, int sid, int t, uint32_t rho, int H, int W) {
+  return (org + block_row_offset(sid, 64u * t + rho, H, W)) * 4u;
+}
+
 // Per-lane byte offsets inside a swizzled 64-row tile (row stride 256 B).
 // ro[kk]: the 16-byte chunk 2kk + hl of row l32 -- the MFMA operand whose
 // rows are the tile's rows (row l32 + 32 adds 8192).  to[db][0/1]: the two
@@ -117,10 +137,9 @@ __device__ inline uint32_t pk2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// one row chunk (16 B) of a permuted, swizzled [rows][128] bf16 buffer
+// chunk `chunk` (16 B, 8 channels) of row `row` of an [rows][128] bf16 tensor
 __device__ inline bf16x8 row_chunk(const uint16_t* buf, int64_t row, int chunk) {
-  return __builtin_bit_cast(
-      bf16x8, *(const uint4*)(buf + row * 128 + ((chunk ^ chunk_swizzle((int)(row & 63))) << 3)));
+  return __builtin_bit_cast(bf16x8, *(const uint4*)(buf + row * 128 + chunk * 8));
 }
 
 // The same walk with plain (scalar) loads, for the dQ kernel, where it runs
@@ -158,19 +177,22 @@ struct UnionIterS {
   }
 };
 
-// The 64-row tiles of the blocks of a merged walk, in order (scalar loads).
+// The 64-row tiles of the blocks of a merged walk, in order (scalar loads):
+// per tile the block's first token, its shape id and the tile's index in it.
 struct TileIterS {
   UnionIterS U;
-  const int32_t* blk_start;
+  const int32_t* blk_org;
   const uint8_t* blk_shape;
   int64_t hoff;
-  int64_t row_;  // first permuted row of the current tile
-  __device__ int64_t row() const { return row_; }
+  uint32_t org_;
+  int sid_;
+  __device__ uint32_t org() const { return org_; }
+  __device__ int sid() const { return sid_; }
   int t, nt, mask;
   bool valid;
   // lists ptr[g0 + i] .. ptr[g0 + i + 1] for i < nl
   __device__ void init(const int64_t* ptr, const int32_t* col, int64_t g0, int nl,
-                       const int32_t* bs, const uint8_t* bsh, int64_t off) {
+                       const int32_t* borg, const uint8_t* bsh, int64_t off) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int64_t g = g0 + (i < nl ? i : 0);
@@ -178,7 +200,7 @@ struct TileIterS {
       U.e[i] = ptr[g + 1];
     }
     U.init(col, nl);
-    blk_start = bs;
+    blk_org = borg;
     blk_shape = bsh;
     hoff = off;
     valid = true;
@@ -189,14 +211,14 @@ struct TileIterS {
   __device__ void advance() {
     if (valid && t + 1 < nt) {
       t++;
-      row_ += 64;
       return;
     }
     int j;
     valid = U.next(j, mask);
     if (valid) {
-      row_ = blk_start[hoff + j];
-      nt = d_shapes[block_shape_at(blk_shape, hoff + j)].volume >> 6;
+      org_ = (uint32_t)blk_org[hoff + j];
+      sid_ = block_shape_at(blk_shape, hoff + j);
+      nt = d_shapes[sid_].volume >> 6;
       t = 0;
     }
   }
@@ -207,9 +229,9 @@ struct TileIterS {
 // blocks in the key-major transpose), in block order; each block comes once,
 // with a bit mask of the lists that hold it.
 //
-// The list entries, block starts and shape ids are read with buffer (vector
-// memory) loads whose values are only needed a step later (the next head of
-// a list, the next tile's row and the block's tile count), so their latency
+// The list entries, block first tokens and shape ids are read with buffer
+// (vector memory) loads whose values are only needed a step later (the next
+// head of a list, the next tile's rows and the block's tile count), so their latency
 // hides behind the tile in between; scalar loads would share the counter of
 // the LDS reads, and every LDS wait of the tile would then wait for them too.
 // The loaded values stay in vector registers (the load offsets carry an
@@ -217,18 +239,18 @@ struct TileIterS {
 // registers at once, which would wait for the load, and with it for every
 // earlier tile load) and are read out with readfirstlane where they are used.
 struct TileIter {
-  __amdgpu_buffer_rsrc_t rcol, rstart, rshape;
+  __amdgpu_buffer_rsrc_t rcol, rorg, rshape;
   int a[4], e[4];  // list positions relative to the first list's start
   int opq;
   int head_v[4];         // next entry of each list (0x7fffffff: exhausted)
-  int start_v, sid_v;    // the current block's start row and shape id
+  int org_v, sid_v;      // the current block's first token and shape id
   int t, mask;
   bool valid;
   // lists ptr[g0 + i] .. ptr[g0 + i + 1] for i < nl (consecutive, so one
-  // buffer covers them); block j's start and shape id at bs[off + j],
-  // bsh[off + j]
+  // buffer covers them); block j's first token and shape id at
+  // borg[off + j], bsh[off + j]
   __device__ void init(const int64_t* ptr, const int32_t* col, int64_t g0, int nl,
-                       const int32_t* bs, const uint8_t* bsh, int64_t off) {
+                       const int32_t* borg, const uint8_t* bsh, int64_t off) {
     asm volatile("v_mov_b32 %0, 0" : "=v"(opq));
     const int64_t base = ptr[g0];
 #pragma unroll
@@ -237,7 +259,7 @@ struct TileIter {
       e[i] = i < nl ? (int)(ptr[g0 + i + 1] - base) : 0;
     }
     rcol = buffer_of(col + base, (uint32_t)(ptr[g0 + nl] - base) * 4u);
-    rstart = buffer_of(bs + off, 0xffffffffu);
+    rorg = buffer_of(borg + off, 0xffffffffu);
     rshape = buffer_of(bsh + off, 0xffffffffu);
 #pragma unroll
     for (int i = 0; i < 4; i++) head_v[i] = a[i] < e[i] ? load_col(i) : 0x7fffffff;
@@ -254,10 +276,9 @@ struct TileIter {
     const int sid = __builtin_amdgcn_readfirstlane(sid_v);
     return sid < 7 ? 1 : sid < 13 ? 2 : 4;
   }
-  // first permuted row of the current tile
-  __device__ int64_t row() const {
-    return (int64_t)__builtin_amdgcn_readfirstlane(start_v) + 64 * t;
-  }
+  // the current block's first token and shape id
+  __device__ uint32_t org() const { return (uint32_t)__builtin_amdgcn_readfirstlane(org_v); }
+  __device__ int sid() const { return __builtin_amdgcn_readfirstlane(sid_v); }
   __device__ void advance() {
     if (valid && t + 1 < tiles()) {
       t++;
@@ -279,7 +300,7 @@ struct TileIter {
         a[i]++;
         head_v[i] = a[i] < e[i] ? load_col(i) : 0x7fffffff;
       }
-    start_v = __builtin_amdgcn_raw_buffer_load_b32(rstart, best * 4 + opq, 0, 0);
+    org_v = __builtin_amdgcn_raw_buffer_load_b32(rorg, best * 4 + opq, 0, 0);
     sid_v = __builtin_amdgcn_raw_buffer_load_b8(rshape, best + opq, 0, 0);
     t = 0;
   }

@@ -13,7 +13,8 @@
 //    holds one query row's scores and the softmax needs one cross-lane step;
 //  * O^T += V^T P^T takes the bf16 probabilities as the B operand directly;
 //    the V^T fragments come from the row-major V tile by ds_read_b64_tr_b16;
-//  * K/V tiles of 64 keys stream through a 4-slot LDS ring: the barrier of
+//  * K/V tiles of 64 keys are gathered from the caller's K and V through the
+//    block -> token map and stream through a 4-slot LDS ring: the barrier of
 //    step j publishes tile j + 1 and frees the slot of tile j - 1 for tile
 //    j + 3, so while tile j is computed the next one is already readable;
 //  * the fragment reads that open each matrix stretch are issued one stretch
@@ -36,10 +37,10 @@ constexpr int kFwdWaves = kFwdRows / 32;  // one wave per 32 rows
 constexpr int kFwdLoads = 2 * kTile / (kFwdWaves * 1024);
 
 __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
-    const uint16_t* __restrict__ vp, const uint8_t* __restrict__ shape_id,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint8_t* __restrict__ shape_id,
     const int32_t* __restrict__ zone_base, const int64_t* __restrict__ blk_off,
-    const int32_t* __restrict__ blk_start, const uint8_t* __restrict__ blk_shape,
+    const int32_t* __restrict__ blk_org, const uint8_t* __restrict__ blk_shape,
     const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int H, int W,
     int Z, int64_t N, float c_log2, uint16_t* __restrict__ o, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char ringK[kRing * kTile];
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
   const int mylist = (32 * wvu) / B < nlists ? (32 * wvu) / B : 0;
 
   TileIter it;
-  it.init(row_ptr, col_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_start,
+  it.init(row_ptr, col_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_org,
           blk_shape, hoff);
 
   // query fragments: row p of this wave, 8 chunks of 16 channels
@@ -85,36 +86,38 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
     for (int r = 0; r < 16; r++) acc[db][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // this head's K and V (N rows of 256 B) as buffers
-  const __amdgpu_buffer_rsrc_t rsK = buffer_of(kp + (int64_t)h * N * 128, (uint32_t)(N * 256));
-  const __amdgpu_buffer_rsrc_t rsV = buffer_of(vp + (int64_t)h * N * 128, (uint32_t)(N * 256));
+  // this head's K and V (N original rows of 256 B) as buffers
+  const __amdgpu_buffer_rsrc_t rsK = buffer_of(k + (int64_t)h * N * 128, (uint32_t)(N * 256));
+  const __amdgpu_buffer_rsrc_t rsV = buffer_of(v + (int64_t)h * N * 128, (uint32_t)(N * 256));
   const uint32_t lK = lds_offset(ringK), lV = lds_offset(ringV);
-  // one K tile and one V tile (already in LDS layout) into slot b: wave w
-  // moves the 1 KB pieces w, w + 8 of each
-  auto stage = [&](int b, int64_t row) {
+  // tile t of the block (first token org, shape sid) from K and from V into
+  // slot b: wave w fills the 1 KB pieces w, w + 8 of each (the same chunks of
+  // the same rows of both)
+  auto stage = [&](int b, uint32_t org, int sid, int t) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const uint32_t piece = i * 512 + wvu * 64;
-      const uint32_t src = (uint32_t)row * 256 + (piece + lane) * 16;
+      const uint32_t src = tile_src16(org, sid, t, piece + lane, H, W);
       dma16(rsK, src, lK + b * kTile + piece * 16);
       dma16(rsV, src, lV + b * kTile + piece * 16);
     }
   };
   uint32_t ring_mask = 0;  // list masks of the tiles in the ring, a byte per slot
   int nreal = 0;           // real tiles issued
-  int64_t last_row = 0;
+  uint32_t last_org = 0;   // the last real tile (re-read past the end)
+  int last_sid = 0, last_t = 0;
   auto issue = [&](int b) {
-    int64_t row = last_row;
     uint32_t mask = 0;
     if (it.valid) {
-      row = it.row();
+      last_org = it.org();
+      last_sid = it.sid();
+      last_t = it.t;
       mask = (uint32_t)it.mask;
-      last_row = row;
       nreal++;
       it.advance();
     }
     ring_mask = (ring_mask & ~(0xffu << (8 * b))) | (mask << (8 * b));
-    stage(b, row);
+    stage(b, last_org, last_sid, last_t);
   };
   // step j: tiles j and j + 1 have landed (each wave waits for its own
   // pieces, the barrier for everybody's), every wave is done with tile
@@ -242,16 +245,18 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
 
 // ---------------------------------------------------------------- fp32 path
 // Plain fp32 kernel (small problems, fp32 inputs): one thread per query row,
-// K/V tiles of 64 rows staged in LDS, exact expf online softmax.
+// K/V tiles of 64 rows gathered into LDS through the block -> token map,
+// exact expf online softmax.
 template <int D>
 __global__ __launch_bounds__(64) void k_attn_fwd_f32(
-    const float* __restrict__ q, const float* __restrict__ kp, const float* __restrict__ vp,
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const uint8_t* __restrict__ shape_id, const int32_t* __restrict__ zone_base,
-    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_start,
+    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_org,
     const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, int H, int W, int Z, int64_t N, float scale,
     float* __restrict__ o, float* __restrict__ lse) {
   __shared__ float Ks[64][D], Vs[64][D];
+  __shared__ int64_t rowtok[64];
   const int64_t tpH = N >> 6;
   const int h = (int)(blockIdx.x / tpH);
   const int64_t r0 = (blockIdx.x - (int64_t)h * tpH) << 6;
@@ -269,13 +274,17 @@ __global__ __launch_bounds__(64) void k_attn_fwd_f32(
   float mrun = -INFINITY, lrun = 0.0f;
   for (int64_t e = row_ptr[g]; e < row_ptr[g + 1]; e++) {
     int j = col_idx[e];
-    int64_t start = blk_start[hoff + j];
-    int nt = d_shapes[block_shape_at(blk_shape, hoff + j)].volume >> 6;
+    const uint32_t org = (uint32_t)blk_org[hoff + j];
+    const int sid = block_shape_at(blk_shape, hoff + j);
+    int nt = d_shapes[sid].volume >> 6;
     for (int t = 0; t < nt; t++) {
       __syncthreads();
+      rowtok[threadIdx.x] =
+          (int64_t)h * N + org + block_row_offset(sid, 64u * t + threadIdx.x, H, W);
+      __syncthreads();
       for (int i = threadIdx.x; i < 64 * D; i += 64) {
-        Ks[i / D][i % D] = kp[((int64_t)h * N + start + 64 * t) * D + i];
-        Vs[i / D][i % D] = vp[((int64_t)h * N + start + 64 * t) * D + i];
+        Ks[i / D][i % D] = k[rowtok[i / D] * D + i % D];
+        Vs[i / D][i % D] = v[rowtok[i / D] * D + i % D];
       }
       __syncthreads();
       for (int r = 0; r < 64; r++) {
@@ -299,26 +308,27 @@ __global__ __launch_bounds__(64) void k_attn_fwd_f32(
   lse[(int64_t)h * N + tok] = lrun > 0.0f ? mrun + logf(lrun) : -INFINITY;
 }
 
-bool launch_attn_fwd(const PlanDev& P, const void* q, void* o, float* lse, hipStream_t st) {
+bool launch_attn_fwd(const PlanDev& P, const void* q, const void* k, const void* v, void* o,
+                     float* lse, hipStream_t st) {
   if (P.dtype == PRISM_BF16 && P.D == 128) {
     dim3 grid((unsigned)(P.heads * (P.N / kFwdRows))), block(kFwdWaves * 64);
     float c_log2 = (float)(1.4426950408889634 / sqrt(128.0));
     hipLaunchKernelGGL(k_attn_fwd_bf16, grid, block, 0, st, (const uint16_t*)q,
-                       (const uint16_t*)P.kp, (const uint16_t*)P.vp, P.shape_id, P.zone_base,
-                       P.blk_off, P.blk_start, P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W, P.Z,
+                       (const uint16_t*)k, (const uint16_t*)v, P.shape_id, P.zone_base,
+                       P.blk_off, P.blk_org, P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W, P.Z,
                        P.N, c_log2, (uint16_t*)o, lse);
   } else if (P.dtype == PRISM_F32 && (P.D == 64 || P.D == 128)) {
     dim3 grid((unsigned)(P.heads * (P.N >> 6))), block(64);
     float scale = (float)(1.0 / sqrt((double)P.D));
     if (P.D == 64)
       hipLaunchKernelGGL((k_attn_fwd_f32<64>), grid, block, 0, st, (const float*)q,
-                         (const float*)P.kp, (const float*)P.vp, P.shape_id, P.zone_base,
-                         P.blk_off, P.blk_start, P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W,
+                         (const float*)k, (const float*)v, P.shape_id, P.zone_base,
+                         P.blk_off, P.blk_org, P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W,
                          P.Z, P.N, scale, (float*)o, lse);
     else
       hipLaunchKernelGGL((k_attn_fwd_f32<128>), grid, block, 0, st, (const float*)q,
-                         (const float*)P.kp, (const float*)P.vp, P.shape_id, P.zone_base,
-                         P.blk_off, P.blk_start, P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W,
+                         (const float*)k, (const float*)v, P.shape_id, P.zone_base,
+                         P.blk_off, P.blk_org, P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W,
                          P.Z, P.N, scale, (float*)o, lse);
   } else {
     return false;

@@ -37,6 +37,32 @@ __host__ __device__ inline int shape_count(int volume) {
 
 static __constant__ Shape d_shapes[kNumShapes] = PRISM_SHAPES;
 static const Shape h_shapes[kNumShapes] = PRISM_SHAPES;
+static constexpr Shape kShapeTable[kNumShapes] = PRISM_SHAPES;
+
+// log2 of one edge of every candidate, two bits per shape id, so that a
+// kernel can look an edge up by arithmetic alone (no memory access):
+// log2(edge) = (kLog2X >> 2 * id) & 3.
+constexpr uint32_t pack_edge_log2(int axis) {
+  uint32_t r = 0;
+  for (int i = 0; i < kNumShapes; i++) {
+    const Shape& s = kShapeTable[i];
+    r |= (uint32_t)(axis == 0 ? s.log2_bt : axis == 1 ? s.log2_bh : s.log2_bw) << (2 * i);
+  }
+  return r;
+}
+constexpr uint32_t kLog2H = pack_edge_log2(1);
+constexpr uint32_t kLog2W = pack_edge_log2(2);
+
+// Token offset of row u (0..B-1, raster order t, h, w inside the block) of a
+// block of shape `sid` from the block's first token, on a grid of H x W
+// tokens per frame.  With the block's first token this is the closed-form
+// map from a block-contiguous row to its original token, so kernels can read
+// a block's rows straight from the original [N][D] layout.
+__host__ __device__ inline uint32_t block_row_offset(int sid, uint32_t u, int H, int W) {
+  const uint32_t lw = (kLog2W >> (2 * sid)) & 3u, lh = (kLog2H >> (2 * sid)) & 3u;
+  return (u >> (lh + lw)) * (uint32_t)(H * W) + ((u >> lw) & ((1u << lh) - 1u)) * (uint32_t)W +
+         (u & ((1u << lw) - 1u));
+}
 
 // Original token of permuted row r (0..511) of zone m for a zone shape:
 // blocks in raster order over the zone's block grid, tokens in raster order
@@ -60,8 +86,8 @@ __host__ __device__ inline int64_t token_of(const Shape& s, int m, int r, int H,
   return ((int64_t)t * H + y) * W + w;
 }
 
-// Permuted K/V rows of the bf16, head_dim 128 layout hold 16 chunks of 16 B;
-// logical chunk c of the row at position rho inside its 64-row tile is
+// A 64-row tile staged in LDS (bf16, head_dim 128) holds 16 chunks of 16 B
+// per row; logical chunk c of the row at position rho inside the tile is
 // stored at chunk c ^ chunk_swizzle(rho).  With this map, 16 consecutive rows
 // read at one logical chunk, and 4 consecutive rows read as two adjacent
 // chunks, both touch distinct LDS banks.
@@ -126,8 +152,7 @@ struct PlanDev {
   uint16_t* kgrid;
   int32_t* qexp;       // [Gmax]
   int32_t* kexp;
-  void* kp;            // [heads][N][D] permuted K (row-major, 16 B chunks XOR-swizzled per tile row)
-  void* vp;            // [heads][N][D] permuted V (same layout)
+  int32_t* blk_org;    // [Gmax]  original token of the block's first row (within head)
   // selection
   float* scores;       // [maxblk][maxblk] scratch for one head
   int32_t* row_cnt;    // [Gmax]
@@ -147,6 +172,11 @@ struct PlanDev {
   int64_t* colt_cost;  // [Gmax] B_j * sum_{i: j in S_i} B_i
   int32_t* sync;       // [128] start counters of the persistent dK/dV kernel
   int kv_persist;      // dK/dV launch: ordered persistent (dense selections) or per unit
+  // shot-cut-aware temporal zones (cut_threshold > 0)
+  double* cut_part;    // [T][heads] frame-difference energy per head
+  double* cut_energy;  // [T] mean energy per frame
+  uint8_t* cuts;       // [T] 1 where a shot cut starts
+  int32_t* zt_cap;     // [T/8] longest block edge in time per temporal row of zones
 };
 
 }  // namespace prism

@@ -353,6 +353,144 @@ __device__ inline bool shape_nearer(const float* g, int a, int b) {
   return lhs < rhs;
 }
 
+// ---- Shape mappings other than b ~ g^(-1/2), the ablations the pages name
+// (paper.rainbus.top "技术新颖性", Table 10): alpha in b ~ g^(-alpha),
+// isotropic, softmax, rank and entropy mappings.  Each gives a target point l
+// in log2 space with sum_d l_d = log2 B:
+//   power(alpha): l_d = -alpha log2 g_d + (S + alpha sum_d log2 g_d) / 3
+//   isotropic:    l_d = S / 3
+//   softmax:      l_d = S softmax(-g)_d
+//   rank:         l_d = S / 3 + rank_d - 1  (rank 0: the largest g_d; equal
+//                 values rank the earlier axis first)
+//   entropy:      l_d = S i_d / sum i,  i_d = -ln(g_d / sum g)
+// and the shape is the candidate of volume B nearest to l (squared
+// Euclidean distance, a later candidate replaces the best only when strictly
+// nearer).  Evaluated in fp64 with plain operations in a fixed order and the
+// logarithm and exponential written below, so the decisions are reproducible.
+constexpr double kLn2 = 0.69314718055994530942;
+constexpr double kInvLn2 = 1.4426950408889634074;
+
+// x = m 2^e with m in [1, 2), exactly
+__device__ inline double mant_exp(double x, int* e) {
+  const double m = frexp(x, e);
+  *e -= 1;
+  return m * 2.0;
+}
+// ln m for m in [1, 2): 2 atanh(z), z = (m - 1) / (m + 1), by the odd series
+// 2 z sum_{k=0..16} z^(2k) / (2k + 1) in Horner form
+__device__ inline double ln_mantissa(double m) {
+  const double z = (m - 1.0) / (m + 1.0);
+  const double z2 = z * z;
+  double s = 1.0 / 33.0;
+  for (int k = 15; k >= 0; k--) s = s * z2 + 1.0 / (double)(2 * k + 1);
+  return (2.0 * z) * s;
+}
+__device__ inline double log2_w(double x) {
+  int e;
+  const double m = mant_exp(x, &e);
+  return (double)e + ln_mantissa(m) * kInvLn2;
+}
+__device__ inline double ln_w(double x) {
+  int e;
+  const double m = mant_exp(x, &e);
+  return (double)e * kLn2 + ln_mantissa(m);
+}
+// e^x = 2^k 2^f, k = rint(x log2 e), 2^f by its Taylor series in f ln 2 to
+// degree 14 (coefficients (ln 2)^n / n! by the recurrence c_n = c_{n-1} ln2 / n)
+__device__ inline double exp_w(double x) {
+  const double y = x * kInvLn2;
+  const double k = rint(y);
+  const double f = y - k;
+  double c[15];
+  c[0] = 1.0;
+  for (int n = 1; n < 15; n++) c[n] = c[n - 1] * kLn2 / (double)n;
+  double p = c[14];
+  for (int n = 13; n >= 0; n--) p = p * f + c[n];
+  return ldexp(p, (int)k);
+}
+
+__device__ inline void map_target(const float* g, int B, int map, float alpha, double* l) {
+  const double S = B == 64 ? 6.0 : B == 128 ? 7.0 : 8.0;
+  if (map == PRISM_MAP_POWER) {
+    const double a = (double)alpha;
+    double L[3];
+    for (int d = 0; d < 3; d++) L[d] = log2_w((double)g[d]);
+    const double Ls = (L[0] + L[1]) + L[2];
+    const double c = (S + a * Ls) / 3.0;
+    for (int d = 0; d < 3; d++) l[d] = (-a) * L[d] + c;
+  } else if (map == PRISM_MAP_ISOTROPIC) {
+    for (int d = 0; d < 3; d++) l[d] = S / 3.0;
+  } else if (map == PRISM_MAP_SOFTMAX) {
+    double gm = (double)g[0];
+    for (int d = 1; d < 3; d++) gm = (double)g[d] < gm ? (double)g[d] : gm;
+    double w[3];
+    for (int d = 0; d < 3; d++) w[d] = exp_w(gm - (double)g[d]);
+    const double ws = (w[0] + w[1]) + w[2];
+    for (int d = 0; d < 3; d++) l[d] = S * (w[d] / ws);
+  } else if (map == PRISM_MAP_RANK) {
+    for (int d = 0; d < 3; d++) {
+      int r = 0;
+      for (int e = 0; e < 3; e++) r += (g[e] > g[d] || (g[e] == g[d] && e < d)) ? 1 : 0;
+      l[d] = S / 3.0 + (double)(r - 1);
+    }
+  } else {  // PRISM_MAP_ENTROPY
+    const double gs = ((double)g[0] + (double)g[1]) + (double)g[2];
+    const double lgs = ln_w(gs);
+    double inf[3];
+    for (int d = 0; d < 3; d++) inf[d] = lgs - ln_w((double)g[d]);
+    const double is = (inf[0] + inf[1]) + inf[2];
+    for (int d = 0; d < 3; d++) l[d] = S * (inf[d] / is);
+  }
+}
+
+__device__ inline int nearest_mapped(const float* g, int B, int map, float alpha) {
+  double l[3];
+  map_target(g, B, map, alpha, l);
+  const int first = shape_first(B), cnt = shape_count(B);
+  int best = first;
+  double bestd = 0.0;
+  for (int c = first; c < first + cnt; c++) {
+    const Shape& s = d_shapes[c];
+    const double d0 = l[0] - (double)s.log2_bt;
+    const double d1 = l[1] - (double)s.log2_bh;
+    const double d2 = l[2] - (double)s.log2_bw;
+    const double dist = (d0 * d0 + d1 * d1) + d2 * d2;
+    if (c == first || dist < bestd) {
+      best = c;
+      bestd = dist;
+    }
+  }
+  return best;
+}
+
+// The same choices restricted to candidates with b_T <= cap (a zone that a
+// shot cut splits in time).
+__device__ inline int nearest_capped(const float* g, int B, int map, float alpha, int cap) {
+  const int first = shape_first(B), cnt = shape_count(B);
+  int best = -1;
+  if (map == PRISM_MAP_POWER && alpha == 0.5f) {
+    for (int c = first; c < first + cnt; c++)
+      if (d_shapes[c].bt <= cap && (best < 0 || shape_nearer(g, c, best))) best = c;
+    return best;
+  }
+  double l[3];
+  map_target(g, B, map, alpha, l);
+  double bestd = 0.0;
+  for (int c = first; c < first + cnt; c++) {
+    const Shape& s = d_shapes[c];
+    if (s.bt > cap) continue;
+    const double d0 = l[0] - (double)s.log2_bt;
+    const double d1 = l[1] - (double)s.log2_bh;
+    const double d2 = l[2] - (double)s.log2_bw;
+    const double dist = (d0 * d0 + d1 * d1) + d2 * d2;
+    if (best < 0 || dist < bestd) {
+      best = c;
+      bestd = dist;
+    }
+  }
+  return best;
+}
+
 __device__ inline int volume_tier(float rr, float rmax, float tau128, float tau256,
                                   uint32_t mask) {
   int B;
@@ -387,7 +525,9 @@ __device__ inline float block_max(float v, float* sh) {
 __global__ __launch_bounds__(256) void k_shapes(const float* __restrict__ vstats,
                                                 const float* __restrict__ astats, int have_audio,
                                                 int Z, float eps, float tau128, float tau256,
-                                                uint32_t vmask, int fixed_id,
+                                                uint32_t vmask, int fixed_id, int map,
+                                                float alpha, const int32_t* __restrict__ zt_cap,
+                                                int zones_per_t,
                                                 uint8_t* __restrict__ shape_id,
                                                 int32_t* __restrict__ zone_base,
                                                 int32_t* __restrict__ nblk) {
@@ -429,10 +569,20 @@ __global__ __launch_bounds__(256) void k_shapes(const float* __restrict__ vstats
           for (int d = 0; d < 3; d++) g[d] = r[d] + eps;
         }
         B = volume_tier(s[3] + s[4], rmax, tau128, tau256, vmask);
-        int first = shape_first(B), cnt = shape_count(B);
-        id = first;
-        for (int c = first + 1; c < first + cnt; c++)
-          if (shape_nearer(g, c, id)) id = c;
+        const int cap = zt_cap ? zt_cap[m / zones_per_t] : 8;
+        if (cap < 8) {
+          // a shot cut inside the zone: blocks no longer in time than cap
+          // (b_T = 2 allows at most 128 tokens)
+          if (cap == 2 && B > 128) B = 128;
+          id = nearest_capped(g, B, map, alpha, cap);
+        } else if (map == PRISM_MAP_POWER && alpha == 0.5f) {
+          int first = shape_first(B), cnt = shape_count(B);
+          id = first;
+          for (int c = first + 1; c < first + cnt; c++)
+            if (shape_nearer(g, c, id)) id = c;
+        } else {
+          id = nearest_mapped(g, B, map, alpha);
+        }
       }
       shape_id[(int64_t)h * Z + m] = (uint8_t)id;
       nb = 512 / B;
@@ -453,23 +603,25 @@ __global__ __launch_bounds__(256) void k_shapes(const float* __restrict__ vstats
   if (threadIdx.x == 0) nblk[h] = carry;
 }
 
-// ============================================================ K4: re-layout + pooling
-// One block of 512 threads (8 waves) per (head, zone); wave w owns permuted
-// rows [64w, 64w+64) of the zone.  K and V rows are copied to the permuted
-// buffers; Q and K are summed per 64-row tile (rows in permuted order), then
-// per block (tiles in order), scaled by 1/B and written with their integer
-// grid: q_c = rint(x_c 2^-E), E = exponent(max_c |x_c|) - 8.
-template <int DT, int CPL, bool SWZ>
-__global__ __launch_bounds__(512) void k_permute_pool(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, int H,
-    int W, int Z, int64_t N, const uint8_t* __restrict__ shape_id,
-    const int32_t* __restrict__ zone_base, const int64_t* __restrict__ blk_off,
-    void* __restrict__ kp, void* __restrict__ vp, int32_t* __restrict__ blk_start,
-    uint8_t* __restrict__ blk_shape, int32_t* __restrict__ blk_head, float* __restrict__ qbar,
-    float* __restrict__ kbar, uint16_t* __restrict__ qgrid, uint16_t* __restrict__ kgrid,
-    int32_t* __restrict__ qexp, int32_t* __restrict__ kexp) {
+// ============================================================ K4: block table + pooling
+// One block of 512 threads (8 waves) per (head, zone); wave w owns the rows
+// [64w, 64w+64) of the zone in block-contiguous order (the re-layout of
+// stage two, which no kernel materialises: attention gathers each block's
+// rows from the original layout through the block -> token map).  Q and K are
+// summed per 64-row tile (rows in that order), then per block (tiles in
+// order), scaled by 1/B and written with their integer grid:
+// q_c = rint(x_c 2^-E), E = exponent(max_c |x_c|) - 8.  Each block's first
+// row, first token and shape go to the block table.
+template <int DT, int CPL>
+__global__ __launch_bounds__(512) void k_pool(
+    const void* __restrict__ q, const void* __restrict__ k, int H, int W, int Z, int64_t N,
+    const uint8_t* __restrict__ shape_id, const int32_t* __restrict__ zone_base,
+    const int64_t* __restrict__ blk_off, int32_t* __restrict__ blk_start,
+    int32_t* __restrict__ blk_org, uint8_t* __restrict__ blk_shape,
+    int32_t* __restrict__ blk_head, float* __restrict__ qbar, float* __restrict__ kbar,
+    uint16_t* __restrict__ qgrid, uint16_t* __restrict__ kgrid, int32_t* __restrict__ qexp,
+    int32_t* __restrict__ kexp) {
   constexpr int D = 64 * CPL;
-  constexpr int ES = DT == 1 ? 2 : 4;  // element size
   __shared__ float tsum[2][8][D];
   const int hm = blockIdx.x;
   const int h = hm / Z, m = hm - h * Z;
@@ -485,31 +637,10 @@ __global__ __launch_bounds__(512) void k_permute_pool(
     const int64_t src = (hb + n) * D + lane * CPL;
     RowVal<DT, CPL> rq = RowVal<DT, CPL>::load(q, src);
     RowVal<DT, CPL> rk = RowVal<DT, CPL>::load(k, src);
-    RowVal<DT, CPL> rv = RowVal<DT, CPL>::load(v, src);
 #pragma unroll
     for (int c = 0; c < CPL; c++) {
       aq[c] = (i == 0) ? rq.get(c) : aq[c] + rq.get(c);
       ak[c] = (i == 0) ? rk.get(c) : ak[c] + rk.get(c);
-    }
-    const int64_t p = (int64_t)m * 512 + r;  // permuted row within the head
-    int64_t dst_byte;
-    if (SWZ) {  // bf16, D = 128: 4 bytes per lane inside chunk lane/4
-      int rho = (int)(p & 63);
-      int chunk = (lane >> 2) ^ chunk_swizzle(rho);
-      dst_byte = ((hb + p) * D) * 2 + chunk * 16 + (lane & 3) * 4;
-    } else {
-      dst_byte = ((hb + p) * D + lane * CPL) * ES;
-    }
-    constexpr int VB = CPL * ES;  // bytes per lane
-    if (VB == 4) {
-      *(uint32_t*)((char*)kp + dst_byte) = *(const uint32_t*)((const char*)k + src * ES);
-      *(uint32_t*)((char*)vp + dst_byte) = *(const uint32_t*)((const char*)v + src * ES);
-    } else if (VB == 2) {
-      *(uint16_t*)((char*)kp + dst_byte) = *(const uint16_t*)((const char*)k + src * ES);
-      *(uint16_t*)((char*)vp + dst_byte) = *(const uint16_t*)((const char*)v + src * ES);
-    } else {
-      *(uint2*)((char*)kp + dst_byte) = *(const uint2*)((const char*)k + src * ES);
-      *(uint2*)((char*)vp + dst_byte) = *(const uint2*)((const char*)v + src * ES);
     }
   }
 #pragma unroll
@@ -524,6 +655,7 @@ __global__ __launch_bounds__(512) void k_permute_pool(
     const int64_t g = blk_off[h] + zone_base[hm] + wv;
     if (lane == 0) {
       blk_start[g] = m * 512 + wv * B;
+      blk_org[g] = (int32_t)token_of(sh, m, wv * B, H, W);
       blk_shape[g] = (uint8_t)sid;
       blk_head[g] = h;
     }
@@ -1405,6 +1537,93 @@ bool launch_sum_i64(const int64_t* in, int64_t n, int64_t* out, hipStream_t st) 
   return hipGetLastError() == hipSuccess;
 }
 
+// ============================================================ shot cuts
+// Shot-cut-aware temporal zones (paper.rainbus.top "独立分析的弱点" (1)):
+// the frame-difference energy e_t = mean over heads, tokens of the frame and
+// channels of (V_t - V_{t-1})^2, a cut where e_t > kappa * mean_t e_t, and
+// per temporal row of zones the longest block edge in time that keeps the
+// blocks off the cut (the largest power of two dividing the cut's offset in
+// the zone, at least 2; 8 without a cut).
+//
+// One block of 256 threads per (frame t >= 1, head): frame t of head h is
+// the contiguous run of H*W*D elements at (h*N + t*H*W)*D.  fp64; each
+// thread sums a fixed strided set of elements in order, then a fixed tree.
+template <int DT>
+__global__ __launch_bounds__(256) void k_frame_energy(const void* __restrict__ v, int64_t N,
+                                                      int64_t HW, int D, int heads,
+                                                      double* __restrict__ part) {
+  __shared__ double red[256];
+  const int t = blockIdx.x + 1, h = blockIdx.y;
+  const int64_t fe = HW * D;
+  const int64_t cur = ((int64_t)h * N + (int64_t)t * HW) * D;
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < fe; i += 256) {
+    double a, b;
+    if (DT == 1) {
+      a = (double)bf16_to_f32(((const uint16_t*)v)[cur + i]);
+      b = (double)bf16_to_f32(((const uint16_t*)v)[cur - fe + i]);
+    } else {
+      a = (double)((const float*)v)[cur + i];
+      b = (double)((const float*)v)[cur - fe + i];
+    }
+    const double d = a - b;
+    s = s + d * d;
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] = red[threadIdx.x] + red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[(int64_t)t * heads + h] = red[0];
+}
+
+// One thread: heads summed in order, the mean over frames, the cut
+// decisions and the per-row caps.
+__global__ void k_cuts(const double* __restrict__ part, int T, int heads, double denom,
+                       float kappa, double* __restrict__ energy, uint8_t* __restrict__ cuts,
+                       int32_t* __restrict__ zt_cap) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  double mean = 0.0;
+  energy[0] = 0.0;
+  for (int t = 1; t < T; t++) {
+    double e = 0.0;
+    for (int h = 0; h < heads; h++) e = e + part[(int64_t)t * heads + h];
+    energy[t] = e / denom;
+    mean = mean + energy[t];
+  }
+  mean = T > 1 ? mean / (double)(T - 1) : 0.0;
+  cuts[0] = 0;
+  for (int t = 1; t < T; t++) cuts[t] = (kappa > 0.0f && energy[t] > (double)kappa * mean) ? 1 : 0;
+  for (int zt = 0; zt < T / 8; zt++) {
+    int cap = 8;
+    for (int c = 1; c < 8; c++) {
+      if (!cuts[8 * zt + c]) continue;
+      int p = c & (-c);
+      p = p < 2 ? 2 : p;
+      cap = p < cap ? p : cap;
+    }
+    zt_cap[zt] = cap;
+  }
+}
+
+bool launch_cuts(const PlanDev& P, const void* v, float kappa, hipStream_t st) {
+  const int64_t HW = (int64_t)P.H * P.W;
+  if (P.T > 1) {
+    dim3 grid((unsigned)(P.T - 1), (unsigned)P.heads), block(256);
+    if (P.dtype == PRISM_BF16)
+      hipLaunchKernelGGL((k_frame_energy<1>), grid, block, 0, st, v, P.N, HW, P.D, P.heads,
+                         P.cut_part);
+    else
+      hipLaunchKernelGGL((k_frame_energy<0>), grid, block, 0, st, v, P.N, HW, P.D, P.heads,
+                         P.cut_part);
+  }
+  const double denom = ((double)P.heads * (double)HW) * (double)P.D;
+  hipLaunchKernelGGL(k_cuts, dim3(1), dim3(64), 0, st, P.cut_part, P.T, P.heads, denom, kappa,
+                     P.cut_energy, P.cuts, P.zt_cap);
+  return hipGetLastError() == hipSuccess;
+}
+
 bool launch_zone_stats(const void* v, int dtype, int D, int H, int W, int Z, int heads,
                        int64_t N, float* out, hipStream_t st) {
   dim3 grid(heads * Z), block(64);
@@ -1429,25 +1648,26 @@ bool launch_audio_stats(const float* a, int H, int W, int Z, float* out, hipStre
 bool launch_shapes(const PlanDev& P, int have_audio, const prism_config& c, int fixed_id,
                    hipStream_t st) {
   hipLaunchKernelGGL(k_shapes, dim3(P.heads), dim3(256), 0, st, P.vstats, P.astats, have_audio,
-                     P.Z, c.eps, c.tau128, c.tau256, c.volume_mask, fixed_id, P.shape_id,
+                     P.Z, c.eps, c.tau128, c.tau256, c.volume_mask, fixed_id, c.shape_map,
+                     c.alpha, c.cut_threshold > 0.0f ? P.zt_cap : nullptr,
+                     (P.H / 8) * (P.W / 8), P.shape_id,
                      P.zone_base, P.nblk);
   return hipGetLastError() == hipSuccess;
 }
 
-bool launch_permute_pool(const PlanDev& P, const void* q, const void* k, const void* v,
-                         hipStream_t st) {
+bool launch_pool(const PlanDev& P, const void* q, const void* k, hipStream_t st) {
   dim3 grid(P.heads * P.Z), block(512);
-#define PP_ARGS                                                                           \
-  q, k, v, P.H, P.W, P.Z, P.N, P.shape_id, P.zone_base, P.blk_off, P.kp, P.vp, P.blk_start, \
+#define PP_ARGS                                                                          \
+  q, k, P.H, P.W, P.Z, P.N, P.shape_id, P.zone_base, P.blk_off, P.blk_start, P.blk_org, \
       P.blk_shape, P.blk_head, P.qbar, P.kbar, P.qgrid, P.kgrid, P.qexp, P.kexp
   if (P.dtype == PRISM_BF16 && P.D == 128)
-    hipLaunchKernelGGL((k_permute_pool<1, 2, true>), grid, block, 0, st, PP_ARGS);
+    hipLaunchKernelGGL((k_pool<1, 2>), grid, block, 0, st, PP_ARGS);
   else if (P.dtype == PRISM_BF16 && P.D == 64)
-    hipLaunchKernelGGL((k_permute_pool<1, 1, false>), grid, block, 0, st, PP_ARGS);
+    hipLaunchKernelGGL((k_pool<1, 1>), grid, block, 0, st, PP_ARGS);
   else if (P.dtype == PRISM_F32 && P.D == 64)
-    hipLaunchKernelGGL((k_permute_pool<0, 1, false>), grid, block, 0, st, PP_ARGS);
+    hipLaunchKernelGGL((k_pool<0, 1>), grid, block, 0, st, PP_ARGS);
   else if (P.dtype == PRISM_F32 && P.D == 128)
-    hipLaunchKernelGGL((k_permute_pool<0, 2, false>), grid, block, 0, st, PP_ARGS);
+    hipLaunchKernelGGL((k_pool<0, 2>), grid, block, 0, st, PP_ARGS);
   else
     return false;
 #undef PP_ARGS

@@ -32,12 +32,13 @@ class Workload:
     top_p: float
     volume_mask: int = 7   # bit0 = 64, bit1 = 128, bit2 = 256
     fixed_shape: tuple = (0, 0, 0)
-    kind: str = "structured"   # "iid" | "structured" | "background"
+    kind: str = "structured"   # "iid" | "structured" | "background" | "smooth"
     active_frac: float = 1.0   # share of zones with content in "background"
     seed: int = 1001
     backward: bool = False
     unit_var: bool = False
     top_k_frac: float = 0.0    # > 0: k = ceil(frac * N_blk) per head instead of top_k
+    cut_frames: tuple = ()     # shot cuts: from each listed frame on, new content
 
     @property
     def N(self) -> int:
@@ -80,6 +81,10 @@ WORKLOADS = {
     # zones of every volume, a ragged number of blocks per head
     "check": Workload("check", 16, 24, 32, 3, 128, "bf16", top_k=3, top_p=0.9, seed=1006,
                       backward=True),
+    # two shot cuts, at frame offsets 4 and 3 of their zones, for the
+    # shot-cut-aware temporal zone boundaries
+    "cuts": Workload("cuts", 24, 32, 32, 2, 128, "bf16", top_k=4, top_p=0.9, seed=1010,
+                     kind="smooth", cut_frames=(12, 19)),
     # smallest bf16 grid with zones of every volume, for full backward checks
     "bwdcheck": Workload("bwdcheck", 8, 16, 32, 2, 128, "bf16", top_k=3, top_p=0.9, seed=1007,
                          backward=True),
@@ -142,6 +147,11 @@ def _structured_head(wl: Workload, h: int, coords, act, device) -> torch.Tensor:
     A = torch.randn(Z, D, 3, generator=g, device=device) / math.sqrt(3.0)
     phi = torch.rand(Z, D, 3, generator=g, device=device) * (2 * math.pi)
     out = torch.randn(wl.N, D, generator=g, device=device) * 0.1
+    if wl.kind == "smooth":
+        # one set of frequencies, amplitudes and phases for the whole grid:
+        # content continuous across zone boundaries (slow, f in [0, 0.15))
+        zone = torch.zeros_like(zone)
+        f = f * 0.3
     xs = (t.float(), y.float(), x.float())
     for d in range(3):
         arg = (2 * math.pi) * f[zone, d].unsqueeze(1) * xs[d].unsqueeze(1) + phi[zone, :, d]
@@ -203,6 +213,15 @@ def make_inputs(wl: Workload | str, device="cpu", with_grad: bool | None = None)
             q[h].copy_(qh)
             k[h].copy_(kh)
             del vh, qh, kh
+        for i, tc in enumerate(wl.cut_frames):
+            # a shot cut at frame tc: every later frame comes from a fresh draw
+            # (other per-zone frequencies, phases and projection)
+            cut = make_inputs(wl.with_(seed=wl.seed + 7919 * (i + 1), cut_frames=()),
+                              device=device, with_grad=False)
+            rows = slice(tc * wl.H * wl.W, wl.N)
+            for name, tns in (("q", q), ("k", k), ("v", v)):
+                tns[:, rows] = cut[name][:, rows]
+            del cut
         if wl.unit_var:
             for tns in (q, k, v):
                 sd = _global_std(tns)
@@ -214,6 +233,21 @@ def make_inputs(wl: Workload | str, device="cpu", with_grad: bool | None = None)
             do[h].copy_(torch.randn(shape[1:], generator=g, device=device))
     av = _av_norm(wl, coords, device).float().contiguous()
     return {"q": q, "k": k, "v": v, "do": do, "av": av, "wl": wl}
+
+
+def make_audio(wl: Workload | str, n_audio: int, device="cpu") -> dict:
+    """Audio keys and values [heads, n_audio, head_dim] for the A->V
+    cross-attention, iid N(0, 1) from the workload's seed, in its dtype.
+    (The pages give no audio token count; n_audio is a parameter.)"""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    device = torch.device(device)
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    g = _gen(device, wl.seed * 1000 + 501)
+    shape = (wl.heads, n_audio, wl.head_dim)
+    ka = torch.randn(shape, generator=g, device=device).to(dt)
+    va = torch.randn(shape, generator=g, device=device).to(dt)
+    return {"ka": ka, "va": va}
 
 
 def _global_std(x: torch.Tensor) -> float:

@@ -58,6 +58,28 @@ typedef enum {
 
 typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
 
+/* Block-shape mapping from the indicator g_d to the target point l in log2
+ * space (sum_d l_d = S = log2 B); the shape is the candidate of volume B
+ * nearest to l.  PRISM_MAP_POWER with alpha = 1/2 is the pages' method,
+ * b_d ~ g_d^(-1/2) (xyznot.com/id "Metode" 2).  The others are the
+ * ablations that paper.rainbus.top "技术新颖性" (Table 10) names without
+ * formulas, in these readings:
+ *   PRISM_MAP_POWER      l_d = -alpha log2 g_d + (S + alpha sum log2 g) / 3
+ *                        (b_d ~ g_d^(-alpha); the pages try 1/3, 1/2, 2)
+ *   PRISM_MAP_ISOTROPIC  l_d = S / 3 (the most cubic candidate)
+ *   PRISM_MAP_SOFTMAX    l_d = S softmax(-g)_d
+ *   PRISM_MAP_RANK       l_d = S / 3 + rank_d - 1, rank 0 = largest g_d
+ *   PRISM_MAP_ENTROPY    l_d = S i_d / sum i, i_d = -ln(g_d / sum g)
+ * Every mapping other than alpha = 1/2 is evaluated in fp64 in a fixed
+ * order with a written logarithm and exponential. */
+typedef enum {
+  PRISM_MAP_POWER = 0,
+  PRISM_MAP_ISOTROPIC = 1,
+  PRISM_MAP_SOFTMAX = 2,
+  PRISM_MAP_RANK = 3,
+  PRISM_MAP_ENTROPY = 4
+} prism_shape_map;
+
 /* Hyper-parameters and problem size.  Defaults (prism_config_default) are
  * the pages' constants: eps = 1e-4, tau_128 = 0.5, tau_256 = 0.25
  * (paper.rainbus.top "方法步骤详情" and "复现评估"). */
@@ -75,6 +97,16 @@ typedef struct {
   float tau128;           /* rho < tau128 -> volume >= 128 */
   float tau256;           /* rho < tau256 -> volume 256 */
   int32_t need_backward;  /* nonzero: also build the key-major lists prism_attn_bwd needs */
+  int32_t shape_map;      /* prism_shape_map (default PRISM_MAP_POWER) */
+  float alpha;            /* exponent of PRISM_MAP_POWER, >= 0 (default 1/2) */
+  float cut_threshold;    /* > 0: shot-cut-aware temporal zones (paper.rainbus.top
+                             "独立分析的弱点" (1)): frame t starts a shot cut when its
+                             frame-difference energy of V, e_t = mean over heads, tokens
+                             and channels of (V_t - V_{t-1})^2 (fp64), exceeds
+                             cut_threshold * mean_t e_t; a zone with a cut at offset c
+                             of its 8 frames takes only blocks with b_T <= the largest
+                             power of two dividing c (at least 2), and at most 128 tokens
+                             when that is 2.  0 (default): fixed 8-frame zones. */
 } prism_config;
 
 /* Opaque plan: block shapes, block table and selected key-block lists of
@@ -83,7 +115,8 @@ typedef struct {
 typedef struct prism_plan_s prism_plan_t;
 
 /* Fill *cfg with the defaults above (T=H=W=8, heads=1, head_dim=128, bf16,
- * top_k=16, top_p=0.9, all volumes, dynamic shapes, need_backward=1). */
+ * top_k=16, top_p=0.9, all volumes, dynamic shapes, need_backward=1,
+ * PRISM_MAP_POWER with alpha = 1/2). */
 void prism_config_default(prism_config* cfg);
 
 /* Host-only validation of a configuration; no device work.  PRISM_EINVAL for
@@ -99,7 +132,11 @@ prism_status prism_config_check(const prism_config* cfg);
 prism_status prism_plan_workspace_size(const prism_config* cfg, int64_t nnz_capacity,
                                        size_t* bytes);
 
-/* Stages 1-3 plus the re-layout of K and V (stage 2): builds a plan.
+/* Stages 1-3: builds a plan (zone statistics, shapes, the block table of the
+ * block-contiguous re-layout of stage 2, pooled means, block scores and the
+ * selected key-block lists).  The re-layout itself is never materialised:
+ * the attention kernels gather each block's rows from q, k, v (and dO)
+ * through the block -> token map, so the plan holds no copy of any tensor.
  *   q, k, v       device [heads][N][head_dim] of cfg->dtype
  *   av_norm       device [N] float32 A->V norm map cached from the previous
  *                 layer, or NULL for the first layer (g = r + eps)
@@ -112,9 +149,8 @@ prism_status prism_plan_workspace_size(const prism_config* cfg, int64_t nnz_capa
  * Reads back two small arrays to the host (per-head block counts and the
  * pair count), so it synchronises `stream` twice.  If the selection does not
  * fit the workspace it returns PRISM_ENOMEM_WORKSPACE with *nnz_out set to
- * the pair count needed and no plan.  The permuted K/V kept in the
- * workspace are read by prism_attn_fwd/bwd: k and v must not change while
- * the plan is used. */
+ * the pair count needed and no plan.  prism_attn_fwd/bwd read q, k and v
+ * themselves: they must be the tensors the plan was built from, unchanged. */
 prism_status prism_plan_create(const prism_config* cfg, const void* q, const void* k,
                                const void* v, const float* av_norm, void* workspace,
                                size_t workspace_bytes, void* stream, prism_plan_t** plan_out,
@@ -131,7 +167,8 @@ void prism_plan_destroy(prism_plan_t* plan);
 prism_status prism_attn_fwd(const prism_plan_t* plan, const void* q, const void* k,
                             const void* v, void* o, float* lse, void* stream);
 
-/* Bytes of device workspace prism_attn_bwd needs.  Host-only. */
+/* Bytes of device workspace prism_attn_bwd needs (8 per token and head:
+ * Delta = rowsum(dO * O) and log2(e) * LSE).  Host-only. */
 prism_status prism_attn_bwd_workspace_size(const prism_config* cfg, size_t* bytes);
 
 /* Backward with the plan held constant: given dO = dL/dO, writes
@@ -146,6 +183,48 @@ prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void*
                             const void* v, const void* o, const float* lse, const void* d_o,
                             void* dq, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* The A->V norm map of the next layer: the audio-to-video cross-attention
+ * h_hat = CrossAttn(h, K_a, V_a) of the video tokens over the audio tokens
+ * and, in its epilogue, the L2 norm of each video position's output
+ * (paper.rainbus.top "双分支视频-音频 DiT 与跨模态交叉注意力" and
+ * "核心方法": the norm says how much audio a position absorbed; the norms of
+ * one layer are cached and guide the block shapes of the next).
+ *   q         device [heads][n_video][head_dim]: the video queries
+ *             (n_video = T*H*W tokens, row-major t, h, w)
+ *   ka, va    device [heads][n_audio][head_dim]: audio keys and values
+ *   o         device [heads][n_video][head_dim] output h_hat per head
+ *             (softmax(q ka^T / sqrt(head_dim)) va), or NULL to skip it
+ *   norm_out  device [n_video] float32: a_n = sqrt(sum over heads and
+ *             channels of h_hat^2), the concatenated head outputs before any
+ *             output projection; it is the av_norm argument of the next
+ *             layer's prism_plan_create
+ * bf16 with head_dim 128 only (PRISM_EUNSUPPORTED otherwise); n_video a
+ * multiple of 256 (any T, H, W that are multiples of 8), n_audio a multiple
+ * of 64, both below 2^24 (PRISM_EINVAL / PRISM_EUNSUPPORTED).  Dense
+ * attention over every audio token, deterministic, no scratch. */
+prism_status prism_av_cross_attn(const void* q, const void* ka, const void* va, int32_t heads,
+                                 int64_t n_video, int32_t n_audio, int32_t head_dim,
+                                 int32_t dtype, void* o, float* norm_out, void* stream);
+
+/* Per-step sparsity schedules (paper.rainbus.top "独立分析的弱点" (4): a loose
+ * Top-p early and a tighter one later, or a value that follows the denoising
+ * step).  The value of a hyper-parameter (top_p, top_k_frac, ...) at step
+ * `step` of `steps` (progress s = step / (steps - 1), clamped to [0, 1]; a
+ * single step is s = 0), going from v0 at the first step to v1 at the last:
+ *   PRISM_SCHED_CONSTANT  v0
+ *   PRISM_SCHED_LINEAR    v0 + (v1 - v0) s
+ *   PRISM_SCHED_COSINE    v1 + (v0 - v1) (1 + cos(pi s)) / 2
+ * evaluated in double and rounded to float.  The caller sets the value into
+ * the prism_config of that step's plan.  Host-only; PRISM_EINVAL for an
+ * unknown kind, steps < 1 or non-finite ends. */
+typedef enum {
+  PRISM_SCHED_CONSTANT = 0,
+  PRISM_SCHED_LINEAR = 1,
+  PRISM_SCHED_COSINE = 2
+} prism_schedule_kind;
+prism_status prism_schedule_value(int32_t kind, int64_t step, int64_t steps, float v0, float v1,
+                                  float* out);
 
 /* Block scores of one head (stage 3): out_scores device float32
  * [N_blk(head)][N_blk(head)], s_ij = Qbar_i . Kbar_j / sqrt(head_dim) with
@@ -171,12 +250,16 @@ typedef enum {
   PRISM_ARR_PERM = 13,        /* int32 [heads][N]: original token of each permuted row */
   PRISM_ARR_QGRID = 14,       /* uint16 (bf16 bits) [G][head_dim]: integer grid of Qbar */
   PRISM_ARR_KGRID = 15,       /* uint16 (bf16 bits) [G][head_dim] */
-  PRISM_ARR_KV_ORDER = 16     /* int32 [heads][N/128] (need_backward): the dK/dV kernel's work
+  PRISM_ARR_KV_ORDER = 16,    /* int32 [heads][N/128] (need_backward): the dK/dV kernel's work
                                  units (128 permuted key rows) of each head, in the order it
                                  takes them: longest walk first (the longest key-major list
                                  among the unit's blocks, in 64-row tiles, capped at 16383),
                                  ties by unit index.  A scheduling order only: dK and dV do
                                  not depend on it. */
+  PRISM_ARR_BLK_ORG = 17,     /* int32 [G]: original token (within its head) of each block's
+                                 first row: with the block's shape this gives every row's
+                                 token in closed form */
+  PRISM_ARR_CUTS = 18         /* uint8 [T] (cut_threshold > 0): 1 where a shot cut starts */
 } prism_array;
 
 /* Size in bytes of a plan array. Host-only. */
@@ -194,6 +277,9 @@ typedef struct {
   int64_t max_blocks_per_head;
   double pair_tokens;         /* sum over selected pairs of B_i * B_j */
   int64_t shape_hist[16];     /* zones per candidate shape, over all heads */
+  int32_t kv_persistent;      /* 1: prism_attn_bwd runs dK/dV as the ordered persistent
+                                 launch (plans selecting at least half of all block pairs);
+                                 0: one work-group per unit */
 } prism_plan_info_t;
 
 /* Fills *info; pair_tokens needs one device read-back (synchronises). */
@@ -205,9 +291,9 @@ prism_status prism_candidate(int32_t id, int32_t* out4);
 
 /* Measurement support.  While enabled, every kernel stage the library
  * enqueues is bracketed by a pair of HIP events recorded on the stage's own
- * stream (stage names: plan.stats, plan.shapes, plan.permute, plan.scores,
+ * stream (stage names: plan.stats, plan.shapes, plan.pool, plan.scores,
  * plan.select, plan.transpose, plan.order, attn.fwd, bwd.prep, bwd.dkdv,
- * bwd.dq).
+ * bwd.dq, av.cross).
  * Host-only; off by default. */
 prism_status prism_timing_enable(int32_t enable);
 

@@ -54,8 +54,19 @@ def lib():
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p]
         _lib.orc_shapes.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
-            ctypes.c_float, ctypes.c_float, ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p,
-            ctypes.c_void_p, ctypes.c_void_p]
+            ctypes.c_float, ctypes.c_float, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+            ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p]
+        _lib.orc_detect_cuts.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+        _lib.orc_nearest_shape_map.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_float]
+        _lib.orc_map_target.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_void_p]
+        for name in ("orc_wlog2", "orc_wln", "orc_wexp"):
+            getattr(_lib, name).restype = ctypes.c_double
+            getattr(_lib, name).argtypes = [ctypes.c_double]
         _lib.orc_score_row.argtypes = [
             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_int, ctypes.c_void_p]
@@ -108,6 +119,34 @@ def exp2(x: float) -> float:
     return lib().orc_exp2(float(x))
 
 
+# shape mappings (ids as in include/prism.h's prism_shape_map)
+MAP_POWER, MAP_ISOTROPIC, MAP_SOFTMAX, MAP_RANK, MAP_ENTROPY = range(5)
+
+
+def map_target(g, B: int, shape_map: int, alpha: float = 0.5) -> np.ndarray:
+    g = np.ascontiguousarray(g, np.float32)
+    out = np.zeros(3, np.float64)
+    assert lib().orc_map_target(_p(g), B, shape_map, np.float32(alpha), _p(out)) == 0
+    return out
+
+
+def nearest_shape_map(g, B: int, shape_map: int, alpha: float = 0.5) -> int:
+    g = np.ascontiguousarray(g, np.float32)
+    return lib().orc_nearest_shape_map(_p(g), B, shape_map, np.float32(alpha))
+
+
+def wlog2(x: float) -> float:
+    return lib().orc_wlog2(float(x))
+
+
+def wln(x: float) -> float:
+    return lib().orc_wln(float(x))
+
+
+def wexp(x: float) -> float:
+    return lib().orc_wexp(float(x))
+
+
 # ---------------------------------------------------------------- config
 
 @dataclass
@@ -125,6 +164,9 @@ class Config:
     eps: float = 1e-4
     tau128: float = 0.5
     tau256: float = 0.25
+    shape_map: int = 0       # MAP_POWER
+    alpha: float = 0.5
+    cut_threshold: float = 0.0   # > 0: shot-cut-aware temporal zones
 
     @property
     def N(self) -> int:
@@ -162,6 +204,7 @@ class Plan:
     kgrid: np.ndarray
     kexp: np.ndarray
     rows: dict = field(default_factory=dict)   # (head, local block) -> selected local key ids
+    cuts: np.ndarray | None = None             # [T] uint8 shot cuts (cut_threshold > 0)
 
     def nblk(self, h: int) -> int:
         return int(self.blk_off[h + 1] - self.blk_off[h])
@@ -183,14 +226,35 @@ def audio_stats(a: np.ndarray, cfg: Config) -> np.ndarray:
     return out
 
 
-def shapes(vstats, astats, cfg: Config):
+def detect_cuts(v: np.ndarray, cfg: Config):
+    """Shot cuts from the frame-difference energy of V: (cuts [T] uint8,
+    energy [T] fp64)."""
+    cuts = np.zeros(cfg.T, np.uint8)
+    energy = np.zeros(cfg.T, np.float64)
+    rc = lib().orc_detect_cuts(_p(v), _dtype_code(v), cfg.T, cfg.H, cfg.W, cfg.heads,
+                               cfg.head_dim, np.float32(cfg.cut_threshold), _p(cuts),
+                               _p(energy))
+    assert rc == 0
+    return cuts, energy
+
+
+def cut_caps(cuts: np.ndarray, T: int) -> np.ndarray:
+    cap = np.zeros(T // 8, np.int32)
+    lib().orc_cut_caps(_p(np.ascontiguousarray(cuts, np.uint8)), T, _p(cap))
+    return cap
+
+
+def shapes(vstats, astats, cfg: Config, zt_cap=None):
     fixed = -1 if tuple(cfg.fixed_shape) == (0, 0, 0) else shape_id_of(*cfg.fixed_shape)
     sid = np.zeros((cfg.heads, cfg.Z), np.uint8)
     g = np.zeros((cfg.heads, cfg.Z, 3), np.float32)
     vol = np.zeros((cfg.heads, cfg.Z), np.int32)
+    cap = None if zt_cap is None else np.ascontiguousarray(zt_cap, np.int32)
+    zpt = (cfg.H // 8) * (cfg.W // 8)
     rc = lib().orc_shapes(_p(vstats), _p(astats), cfg.heads, cfg.Z, np.float32(cfg.eps),
                           np.float32(cfg.tau128), np.float32(cfg.tau256), cfg.volume_mask,
-                          fixed, _p(sid), _p(g), _p(vol))
+                          fixed, cfg.shape_map, np.float32(cfg.alpha), _p(cap), zpt, _p(sid),
+                          _p(g), _p(vol))
     assert rc == 0
     return sid, g, vol
 
@@ -231,14 +295,19 @@ def plan(q, k, v, av_norm, cfg: Config) -> Plan:
     """Stages one to three up to the pooled, integer-grid block means."""
     vs = zone_stats(v, cfg)
     ast = None if av_norm is None else audio_stats(av_norm, cfg)
-    sid, g, vol = shapes(vs, ast, cfg)
+    cuts = None
+    if cfg.cut_threshold > 0:
+        cuts, _ = detect_cuts(v, cfg)
+    sid, g, vol = shapes(vs, ast, cfg, None if cuts is None else cut_caps(cuts, cfg.T))
     off, start, ln = block_table(sid, cfg)
     perm = perm_map(sid, cfg)
     qbar = pool(q, sid, off, cfg)
     kbar = pool(k, sid, off, cfg)
     qg, qe = quantize(qbar)
     kg, ke = quantize(kbar)
-    return Plan(cfg, vs, ast, g, vol, sid, off, start, ln, perm, qbar, kbar, qg, qe, kg, ke)
+    pl = Plan(cfg, vs, ast, g, vol, sid, off, start, ln, perm, qbar, kbar, qg, qe, kg, ke)
+    pl.cuts = cuts
+    return pl
 
 
 def score_row(pl: Plan, h: int, i: int) -> np.ndarray:
@@ -268,18 +337,25 @@ def select_row(pl: Plan, h: int, i: int) -> np.ndarray:
     return pl.rows[key]
 
 
-def select_all(pl: Plan, heads=None):
+def select_all(pl: Plan, heads=None, threads: int = 1):
     """Full CSR over the listed heads: (row_ptr [G+1] int64 over all blocks,
-    col_idx int32).  Rows of heads not listed are empty."""
+    col_idx int32).  Rows of heads not listed are empty.  Rows are
+    independent; with threads > 1 they are computed by that many host
+    threads (the C calls release the interpreter lock), which changes no
+    result."""
     heads = range(pl.cfg.heads) if heads is None else heads
     G = int(pl.blk_off[-1])
     counts = np.zeros(G, np.int64)
     lists = {}
-    for h in heads:
-        for i in range(pl.nblk(h)):
-            r = select_row(pl, h, i)
-            lists[int(pl.blk_off[h]) + i] = r
-            counts[int(pl.blk_off[h]) + i] = len(r)
+    todo = [(h, i) for h in heads for i in range(pl.nblk(h))]
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda hi: select_row(pl, *hi), todo, chunksize=64))
+    for h, i in todo:
+        r = select_row(pl, h, i)
+        lists[int(pl.blk_off[h]) + i] = r
+        counts[int(pl.blk_off[h]) + i] = len(r)
     row_ptr = np.zeros(G + 1, np.int64)
     np.cumsum(counts, out=row_ptr[1:])
     col = np.zeros(int(row_ptr[-1]), np.int32)
@@ -325,29 +401,41 @@ def attn_bwd_q(q, k, v, do, pl: Plan, items):
     return dq
 
 
-def attn_bwd_kv(q, k, v, do, pl: Plan, items):
+def attn_bwd_kv(q, k, v, do, pl: Plan, items, threads: int = 1, split: int = 1):
     """dK, dV for (head, local key block) items; needs every row of the
-    items' heads, so it selects those heads in full."""
+    items' heads, so it selects those heads in full.  A key block's gradient
+    is a sum over the query blocks that selected it; with split > 1 that list
+    is cut into up to `split` parts computed as separate items (in parallel)
+    whose fp64 results are then added, which changes only the order of the
+    fp64 additions."""
     cfg = pl.cfg
     heads = sorted({h for h, _ in items})
-    row_ptr, col = select_all(pl, heads)
-    tq = []
-    for h, j in items:
+    row_ptr, col = select_all(pl, heads, threads=threads)
+    subs = []     # (item index, head, key block, query blocks)
+    for it, (h, j) in enumerate(items):
         o = int(pl.blk_off[h])
         lst = [i for i in range(pl.nblk(h))
                if np.any(col[row_ptr[o + i]:row_ptr[o + i + 1]] == j)]
-        tq.append(np.array(lst, np.int32))
-    tptr = np.zeros(len(items) + 1, np.int64)
-    np.cumsum([len(t) for t in tq], out=tptr[1:])
-    tidx = np.ascontiguousarray(np.concatenate(tq).astype(np.int32)) if tq else np.zeros(0, np.int32)
-    ih = np.array([h for h, _ in items], np.int32)
-    ib = np.array([b for _, b in items], np.int32)
-    dk = np.zeros((len(items), 256, cfg.head_dim), np.float64)
-    dv = np.zeros((len(items), 256, cfg.head_dim), np.float64)
+        parts = max(1, min(split, len(lst)))
+        for part in np.array_split(np.array(lst, np.int32), parts):
+            subs.append((it, h, j, part))
+    tptr = np.zeros(len(subs) + 1, np.int64)
+    np.cumsum([len(s[3]) for s in subs], out=tptr[1:])
+    tidx = (np.ascontiguousarray(np.concatenate([s[3] for s in subs]).astype(np.int32))
+            if subs else np.zeros(0, np.int32))
+    ih = np.array([s[1] for s in subs], np.int32)
+    ib = np.array([s[2] for s in subs], np.int32)
+    sdk = np.zeros((len(subs), 256, cfg.head_dim), np.float64)
+    sdv = np.zeros((len(subs), 256, cfg.head_dim), np.float64)
     lib().orc_attn_bwd_kv(_p(q), _p(k), _p(v), _p(do), _dtype_code(q), ctypes.c_int64(cfg.N),
                           cfg.head_dim, _p(pl.perm), _p(pl.blk_off), _p(pl.blk_start),
-                          _p(pl.blk_len), _p(row_ptr), _p(col), len(items), _p(ih), _p(ib),
-                          _p(tptr), _p(tidx), _p(dk), _p(dv))
+                          _p(pl.blk_len), _p(row_ptr), _p(col), len(subs), _p(ih), _p(ib),
+                          _p(tptr), _p(tidx), _p(sdk), _p(sdv))
+    dk = np.zeros((len(items), 256, cfg.head_dim), np.float64)
+    dv = np.zeros((len(items), 256, cfg.head_dim), np.float64)
+    for s, (it, _, _, _) in enumerate(subs):
+        dk[it] += sdk[s]
+        dv[it] += sdv[s]
     return dk, dv
 
 
@@ -370,3 +458,21 @@ def attn_bwd_head(q, k, v, do, pl: Plan, h: int):
                             cfg.head_dim, _p(pl.perm), _p(pl.blk_off), _p(pl.blk_start),
                             _p(pl.blk_len), _p(row_ptr), _p(col), h, _p(dq), _p(dk), _p(dv))
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- A->V norm map
+
+def av_cross(q, ka, va, tokens, want_o: bool = False):
+    """A->V cross-attention of video queries q [heads, N, D] over audio keys
+    and values ka, va [heads, Na, D] at the listed tokens: the norm
+    ||h_hat_n||_2 over all heads and channels (fp64), and optionally h_hat
+    [len(tokens), heads, D]."""
+    heads, N, D = q.shape
+    Na = ka.shape[1]
+    tokens = np.ascontiguousarray(tokens, np.int64)
+    norm = np.zeros(len(tokens), np.float64)
+    o = np.zeros((len(tokens), heads, D), np.float64) if want_o else None
+    rc = lib().orc_av_cross(_p(q), _p(ka), _p(va), _dtype_code(q), heads, ctypes.c_int64(N),
+                            ctypes.c_int64(Na), D, len(tokens), _p(tokens), _p(norm), _p(o))
+    assert rc == 0
+    return (norm, o) if want_o else norm

@@ -339,6 +339,169 @@ int orc_nearest_shape(const float* g, int B) {
   return best;
 }
 
+/* ------------------------------------------------------------------ */
+/* Shape-mapping variants.  paper.rainbus.top "技术新颖性" (ablation of     */
+/* Table 10) names b_d ~ g_d^(-alpha) with alpha in {1/3, 1/2, 2},        */
+/* Softmax, Rank and Entropy mappings and an Isotropic baseline, without  */
+/* formulas; the readings below (listed in the design notes) give each a  */
+/* target point l in log2 space with sum_d l_d = S = log2 B, and the      */
+/* shape is the candidate of volume B nearest to l (Euclidean, ties to    */
+/* the lower id), as for alpha = 1/2 [ID] 2.                              */
+/*   power(alpha): l_d = -alpha log2 g_d + (S + alpha sum log2 g) / 3     */
+/*   isotropic:    l_d = S / 3                                            */
+/*   softmax:      l_d = S softmax(-g)_d                                  */
+/*   rank:         l_d = S / 3 + rank_d - 1, rank_d = 0 for the largest   */
+/*                 g (ties: earlier axis first)                           */
+/*   entropy:      l_d = S i_d / sum i, i_d = -ln(g_d / sum g) (the       */
+/*                 self-information of each axis' share of g)             */
+/* alpha = 1/2 keeps the exact product-form test above.  Every other      */
+/* target is evaluated in fp64 with plain operations in the written      */
+/* order, with the logarithm and exponential below, so that an           */
+/* independent implementation reproduces the decisions bit for bit.      */
+/* ------------------------------------------------------------------ */
+#define MAP_POWER 0
+#define MAP_ISOTROPIC 1
+#define MAP_SOFTMAX 2
+#define MAP_RANK 3
+#define MAP_ENTROPY 4
+
+static const double W_LN2 = 0.69314718055994530942;
+static const double W_INV_LN2 = 1.4426950408889634074;
+
+/* x = m 2^e with m in [1, 2), exactly */
+static double split_pow2(double x, int* e) {
+  double m = frexp(x, e); /* [0.5, 1) */
+  *e -= 1;
+  return m * 2.0;
+}
+
+/* ln m for m in [1, 2): z = (m - 1) / (m + 1), ln m = 2 atanh z =
+ * 2 z sum_{k=0}^{16} z^(2k) / (2k + 1), Horner in z^2. */
+static double ln_mant(double m) {
+  double z = (m - 1.0) / (m + 1.0);
+  double z2 = z * z;
+  double s = 1.0 / 33.0;
+  for (int k = 15; k >= 0; k--) s = s * z2 + 1.0 / (double)(2 * k + 1);
+  return (2.0 * z) * s;
+}
+
+double orc_wlog2(double x) {
+  int e;
+  double m = split_pow2(x, &e);
+  return (double)e + ln_mant(m) * W_INV_LN2;
+}
+
+double orc_wln(double x) {
+  int e;
+  double m = split_pow2(x, &e);
+  return (double)e * W_LN2 + ln_mant(m);
+}
+
+/* e^x: y = x log2 e, k = rint(y), f = y - k in [-1/2, 1/2],
+ * 2^f = sum_{n=0}^{14} (f ln 2)^n / n! with c_n = c_{n-1} ln2 / n, Horner. */
+double orc_wexp(double x) {
+  double y = x * W_INV_LN2;
+  double k = rint(y);
+  double f = y - k;
+  double cn[15];
+  cn[0] = 1.0;
+  for (int n = 1; n < 15; n++) cn[n] = cn[n - 1] * W_LN2 / (double)n;
+  double p = cn[14];
+  for (int n = 13; n >= 0; n--) p = p * f + cn[n];
+  return ldexp(p, (int)k);
+}
+
+/* target point l (fp64) of a mapping; 0 on success */
+int orc_map_target(const float* g, int B, int map, float alpha, double* l) {
+  double S = (double)ilog2i(B);
+  if (map == MAP_POWER) {
+    double a = (double)alpha;
+    double L[3] = {orc_wlog2((double)g[0]), orc_wlog2((double)g[1]), orc_wlog2((double)g[2])};
+    double Ls = (L[0] + L[1]) + L[2];
+    double c = (S + a * Ls) / 3.0;
+    for (int d = 0; d < 3; d++) l[d] = (-a) * L[d] + c;
+  } else if (map == MAP_ISOTROPIC) {
+    for (int d = 0; d < 3; d++) l[d] = S / 3.0;
+  } else if (map == MAP_SOFTMAX) {
+    double gm = (double)g[0];
+    for (int d = 1; d < 3; d++)
+      if ((double)g[d] < gm) gm = (double)g[d];
+    double w[3];
+    for (int d = 0; d < 3; d++) w[d] = orc_wexp(gm - (double)g[d]); /* exp(-g_d) / exp(-min g) */
+    double ws = (w[0] + w[1]) + w[2];
+    for (int d = 0; d < 3; d++) l[d] = S * (w[d] / ws);
+  } else if (map == MAP_RANK) {
+    for (int d = 0; d < 3; d++) {
+      int r = 0;
+      for (int e = 0; e < 3; e++)
+        if (g[e] > g[d] || (g[e] == g[d] && e < d)) r++;
+      l[d] = S / 3.0 + (double)(r - 1);
+    }
+  } else if (map == MAP_ENTROPY) {
+    double gs = ((double)g[0] + (double)g[1]) + (double)g[2];
+    double lgs = orc_wln(gs);
+    double inf[3];
+    for (int d = 0; d < 3; d++) inf[d] = lgs - orc_wln((double)g[d]);
+    double is = (inf[0] + inf[1]) + inf[2];
+    for (int d = 0; d < 3; d++) l[d] = S * (inf[d] / is);
+  } else {
+    return OR_EINVAL;
+  }
+  return OR_OK;
+}
+
+/* nearest candidate of volume B to the mapping's target; exact ties go to
+ * the lower id.  power with alpha = 1/2 is the exact test above. */
+int orc_nearest_shape_map(const float* g, int B, int map, float alpha) {
+  build_candidates();
+  if (map == MAP_POWER && alpha == 0.5f) return orc_nearest_shape(g, B);
+  double l[3];
+  if (orc_map_target(g, B, map, alpha, l) != OR_OK) return -1;
+  int best = -1;
+  double bestd = 0.0;
+  for (int i = 0; i < cand_n; i++) {
+    if (cand[i][3] != B) continue;
+    double d0 = l[0] - (double)ilog2i(cand[i][0]);
+    double d1 = l[1] - (double)ilog2i(cand[i][1]);
+    double d2 = l[2] - (double)ilog2i(cand[i][2]);
+    double dist = (d0 * d0 + d1 * d1) + d2 * d2;
+    if (best < 0 || dist < bestd) {
+      best = i;
+      bestd = dist;
+    }
+  }
+  return best;
+}
+
+/* nearest candidate of volume B with b_T <= cap (a zone split by a shot
+ * cut); the same comparisons as without the cap, over fewer candidates */
+static int orc_nearest_capped(const float* g, int B, int map, float alpha, int cap) {
+  build_candidates();
+  int best = -1;
+  if (map == MAP_POWER && alpha == 0.5f) {
+    for (int i = 0; i < cand_n; i++) {
+      if (cand[i][3] != B || cand[i][0] > cap) continue;
+      if (best < 0 || nearer(g, i, best)) best = i;
+    }
+    return best;
+  }
+  double l[3];
+  if (orc_map_target(g, B, map, alpha, l) != OR_OK) return -1;
+  double bestd = 0.0;
+  for (int i = 0; i < cand_n; i++) {
+    if (cand[i][3] != B || cand[i][0] > cap) continue;
+    double d0 = l[0] - (double)ilog2i(cand[i][0]);
+    double d1 = l[1] - (double)ilog2i(cand[i][1]);
+    double d2 = l[2] - (double)ilog2i(cand[i][2]);
+    double dist = (d0 * d0 + d1 * d1) + d2 * d2;
+    if (best < 0 || dist < bestd) {
+      best = i;
+      bestd = dist;
+    }
+  }
+  return best;
+}
+
 /* Volume tier from rho = rho_raw / max rho_raw [ZH]:
  * rho >= tau128 -> 64, else rho >= tau256 -> 128, else 256.
  * A head whose zones all have zero density takes 256 everywhere.
@@ -364,12 +527,18 @@ static int volume_of(float rho_raw, float rho_max, float tau128, float tau256,
 
 /* vstats [heads][Z][5] from orc_zone_stats; astats [Z][4] or NULL (first
  * layer).  Writes shape ids [heads][Z]; optional g [heads][Z][3] and
- * volume [heads][Z]. fixed_id >= 0 forces one shape everywhere. */
+ * volume [heads][Z]. fixed_id >= 0 forces one shape everywhere; otherwise
+ * map / alpha select the shape mapping (MAP_POWER with alpha = 1/2 is the
+ * pages' method). */
+static int orc_nearest_capped(const float* g, int B, int map, float alpha, int cap);
+
 int orc_shapes(const float* vstats, const float* astats, int heads, int Z, float eps,
-               float tau128, float tau256, uint32_t volume_mask, int fixed_id,
-               uint8_t* shape_id, float* g_out, int32_t* vol_out) {
+               float tau128, float tau256, uint32_t volume_mask, int fixed_id, int map,
+               float alpha, const int32_t* zt_cap, int zones_per_t, uint8_t* shape_id,
+               float* g_out, int32_t* vol_out) {
   build_candidates();
   if (fixed_id >= cand_n) return OR_EINVAL;
+  if (map < MAP_POWER || map > MAP_ENTROPY) return OR_EINVAL;
   if ((volume_mask & 7u) == 0) return OR_EINVAL;
   /* audio coupling abar = zone mean / max zone mean (0 if all zero) */
   float amax = 0.0f;
@@ -401,7 +570,14 @@ int orc_shapes(const float* vstats, const float* astats, int heads, int Z, float
         B = cand[id][3];
       } else {
         B = volume_of(s[3] + s[4], rmax, tau128, tau256, volume_mask);
-        id = orc_nearest_shape(g, B);
+        int cap = zt_cap ? zt_cap[m / zones_per_t] : 8;
+        if (cap >= 8) {
+          id = orc_nearest_shape_map(g, B, map, alpha);
+        } else {
+          /* a shot cut inside the zone: at most 128 tokens when b_T = 2 */
+          if (cap == 2 && B > 128) B = 128;
+          id = orc_nearest_capped(g, B, map, alpha, cap);
+        }
       }
       shape_id[(int64_t)h * Z + m] = (uint8_t)id;
       if (g_out)
@@ -909,6 +1085,114 @@ int orc_attn_bwd_head(const void* q, const void* k, const void* v, const void* d
     }
     free(lk);
     free(lv);
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* The A->V norm map consumed by the next layer's stage one             */
+/* (paper.rainbus.top "双分支视频-音频 DiT 与跨模态交叉注意力": the video  */
+/* hidden state takes audio information through h_hat =                  */
+/* CrossAttn(h, K_a, V_a), and the L2 norm of that output at each video  */
+/* position measures how much audio it absorbed; "核心方法": the norms    */
+/* of one layer are cached for the next).  Reading: h_hat of token n is  */
+/* the concatenation over heads of softmax(q_{h,n} K_a,h^T / sqrt D)     */
+/* V_a,h (before any output projection), and a_n = ||h_hat_n||_2.       */
+/* fp64, two-pass softmax.  For each listed token: norm_out[i] and, if   */
+/* o_out is not NULL, o_out[i][heads][D].                               */
+/* ------------------------------------------------------------------ */
+int orc_av_cross(const void* q, const void* ka, const void* va, int dtype, int heads, int64_t N,
+                 int64_t Na, int D, int ntok, const int64_t* tokens, double* norm_out,
+                 double* o_out) {
+  if (Na <= 0 || D > 128) return OR_EINVAL;
+  double scale = 1.0 / sqrt((double)D);
+#pragma omp parallel for schedule(dynamic)
+  for (int it = 0; it < ntok; it++) {
+    int64_t n = tokens[it];
+    double* s = (double*)malloc(sizeof(double) * Na);
+    double ss = 0.0;
+    for (int h = 0; h < heads; h++) {
+      double qv[128], o[128];
+      for (int c = 0; c < D; c++) {
+        qv[c] = ld(q, dtype, ((int64_t)h * N + n) * D + c);
+        o[c] = 0.0;
+      }
+      double mx = -INFINITY;
+      for (int64_t m = 0; m < Na; m++) {
+        double acc = 0.0;
+        for (int c = 0; c < D; c++) acc += qv[c] * ld(ka, dtype, ((int64_t)h * Na + m) * D + c);
+        s[m] = acc * scale;
+        if (s[m] > mx) mx = s[m];
+      }
+      double sum = 0.0;
+      for (int64_t m = 0; m < Na; m++) sum += exp(s[m] - mx);
+      for (int64_t m = 0; m < Na; m++) {
+        double p = exp(s[m] - mx) / sum;
+        for (int c = 0; c < D; c++) o[c] += p * ld(va, dtype, ((int64_t)h * Na + m) * D + c);
+      }
+      for (int c = 0; c < D; c++) {
+        ss += o[c] * o[c];
+        if (o_out) o_out[((int64_t)it * heads + h) * D + c] = o[c];
+      }
+    }
+    norm_out[it] = sqrt(ss);
+    free(s);
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Shot-cut-aware temporal zone boundaries (paper.rainbus.top            */
+/* "独立分析的弱点" (1): detect shot cuts from frame differences and force */
+/* the macro-zones to split there).  Readings:                            */
+/*  - the frame-difference energy of frame t >= 1 is                      */
+/*    e_t = mean over heads, the H x W tokens and the channels of         */
+/*    (V_t - V_{t-1})^2 (fp64); a cut starts frame t when                 */
+/*    e_t > kappa * mean_{t'} e_{t'} (kappa = the cut threshold, 0: off);  */
+/*  - a zone of frames [8 zt, 8 zt + 8) with a cut at offset c (1..7)     */
+/*    splits there: its blocks may not be longer in time than the largest */
+/*    power of two dividing c (at least 2, the shortest edge a candidate  */
+/*    has, so an odd offset leaves one 2-frame block row across the cut); */
+/*    the cap is the smallest over the zone's cuts, and the zone's volume */
+/*    drops to the largest volume that has a candidate within the cap     */
+/*    (b_T = 2 allows at most 128).                                       */
+/* cuts[t] = 1 where a cut starts (cuts[0] = 0); energy[t] = e_t (e_0 = 0) */
+/* ------------------------------------------------------------------ */
+int orc_detect_cuts(const void* v, int dtype, int T, int H, int W, int heads, int D,
+                    float kappa, uint8_t* cuts, double* energy) {
+  int64_t N = (int64_t)T * H * W, HW = (int64_t)H * W;
+  energy[0] = 0.0;
+#pragma omp parallel for schedule(static)
+  for (int t = 1; t < T; t++) {
+    double s = 0.0;
+    for (int h = 0; h < heads; h++)
+      for (int64_t p = 0; p < HW; p++)
+        for (int c = 0; c < D; c++) {
+          double a = ld(v, dtype, ((int64_t)h * N + (int64_t)t * HW + p) * D + c);
+          double b = ld(v, dtype, ((int64_t)h * N + (int64_t)(t - 1) * HW + p) * D + c);
+          s += (a - b) * (a - b);
+        }
+    energy[t] = s / ((double)heads * (double)HW * (double)D);
+  }
+  double mean = 0.0;
+  for (int t = 1; t < T; t++) mean += energy[t];
+  mean = T > 1 ? mean / (double)(T - 1) : 0.0;
+  cuts[0] = 0;
+  for (int t = 1; t < T; t++) cuts[t] = (kappa > 0.0f && energy[t] > (double)kappa * mean) ? 1 : 0;
+  return OR_OK;
+}
+
+/* largest b_T allowed in each temporal zone row zt (8 = no cut inside) */
+int orc_cut_caps(const uint8_t* cuts, int T, int32_t* cap) {
+  for (int zt = 0; zt < T / 8; zt++) {
+    int c_cap = 8;
+    for (int c = 1; c < 8; c++) {
+      if (!cuts[8 * zt + c]) continue;
+      int p = c & (-c); /* largest power of two dividing c */
+      if (p < 2) p = 2;
+      if (p < c_cap) c_cap = p;
+    }
+    cap[zt] = c_cap;
   }
   return OR_OK;
 }

@@ -91,3 +91,30 @@ def test_candidate_table_matches_oracle(nat, orc):
     for i, row in enumerate(orc.candidates()):
         assert nat.lib().prism_candidate(i, a) == 0
         assert tuple(a) == tuple(int(x) for x in row)
+
+
+def test_sparsity_schedules(nat):
+    """paper.rainbus.top "独立分析的弱点" (4): schedules of a sparsity
+    hyper-parameter over steps, against their closed forms."""
+    import math
+    from dynamic_block_sparse_zone_amd import api
+    f32 = lambda x: float(ctypes.c_float(x).value)
+    for kind in ("constant", "linear", "cosine"):
+        assert api.schedule_value(kind, 0, 10, 0.9, 0.2) == f32(0.9)
+        assert api.schedule_value(kind, 0, 1, 0.9, 0.2) == f32(0.9)
+    assert api.schedule_value("constant", 9, 10, 0.9, 0.2) == f32(0.9)
+    for kind in ("linear", "cosine"):
+        assert api.schedule_value(kind, 9, 10, 0.9, 0.2) == f32(0.2)
+        assert api.schedule_value(kind, 99, 10, 0.9, 0.2) == f32(0.2)      # clamped
+        vals = [api.schedule_value(kind, s, 21, 0.9, 0.2) for s in range(21)]
+        assert all(a >= b for a, b in zip(vals, vals[1:]))                 # monotone
+    assert api.schedule_value("linear", 5, 11, 0.0, 1.0) == f32(0.5)
+    assert abs(api.schedule_value("cosine", 5, 11, 0.0, 1.0) - 0.5) < 1e-7
+    s = 3 / 10
+    assert abs(api.schedule_value("cosine", 3, 11, 1.0, 0.0) -
+               (0.5 * (1 + math.cos(math.pi * s)))) < 1e-7
+    out = ctypes.c_float()
+    L = nat.lib()
+    assert L.prism_schedule_value(7, 0, 10, 0.1, 0.2, ctypes.byref(out)) == 1
+    assert L.prism_schedule_value(1, 0, 0, 0.1, 0.2, ctypes.byref(out)) == 1
+    assert L.prism_schedule_value(1, 0, 10, float("nan"), 0.2, ctypes.byref(out)) == 1

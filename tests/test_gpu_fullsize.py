@@ -1,21 +1,32 @@
 """Parity at the full 2K training-scale size, in the configuration bench.py
-times (72 x 120 x 120 = 1,036,800 tokens, 40 heads of 128, bf16, k = 16,
-p = 0.9, plan with the key-major transpose, forward and backward).
+times (72 x 120 x 120 = 1,036,800 tokens, 40 heads of 128, bf16, plan with
+the key-major transpose, forward and backward), at the benchmark's k = 16,
+p = 0.9 (train2k) and at the pages' operating point, Top-k of 5 % of the
+blocks with Top-p 0.2 (train2k_op; paper.rainbus.top "复现评估").
 
-The GPU runs the whole layer once.  The oracle then plans single heads on the
-CPU (a head's plan depends on that head's Q, K, V and the shared A->V map
-only), so for the sampled heads every plan array and every CSR row is
-compared bit for bit; the key-major transpose is checked to be exactly the
-transpose of the query-major lists; and sampled query blocks (O, LSE, dQ) are
-compared with the fp64 oracle within the bf16 bar.  The oracle's dK/dV of a
-key block needs the whole softmax row of every query that selected it (about
-10^14 operations per head here), so at this size dK and dV are checked by
-identities that hold at any size instead: every probability row sums to one,
-so the dV of a head summed over keys equals its dO summed over queries, and
-dK summed over keys is zero; key blocks that no query selected get exactly
-zero gradient.  (Element-wise dK/dV parity runs on the smaller grids, through
-the same kernels.)  At this size more than 2^31 pairs are selected, so 32-bit
-position arithmetic anywhere in the plan shows up here and nowhere smaller."""
+The GPU runs the whole layer of each configuration once.  The oracle then
+plans four heads alone (a head's plan depends on that head's Q, K, V and the
+shared A->V map only; the heads are stacked into one four-head problem), so
+for those heads every plan array and every CSR row is compared bit for bit,
+and the key-major transpose is checked to be exactly the transpose of the
+query-major lists.  On heads 0 and 39, sampled query blocks (two of each
+volume present) are compared with the fp64 oracle on O, LSE and dQ within the
+bf16 bar.
+
+dK/dV of a key block need the whole softmax row of every query that selected
+it.  At the operating point (density 0.15) the oracle computes them
+element-wise for the key block of each sampled head whose selecting rows cost
+it least.  At p = 0.9 that costs ~10^14 operations per key block, so there
+dK and dV are checked by identities that hold at any size instead: every
+probability row sums to one, so the dV of a head summed over keys equals its
+dO summed over queries, and dK summed over keys is zero; key blocks that no
+query selected get exactly zero gradient.  (The p = 0.9 plan takes the
+ordered persistent dK/dV launch, the operating point one work-group per
+unit; element-wise dK/dV parity of the persistent launch runs on the smaller
+grids, through the same kernel.)  At p = 0.9 more than 2^31 pairs are
+selected, so 32-bit position arithmetic anywhere in the plan shows up here
+and nowhere smaller."""
+import os
 import sys
 import time
 
@@ -28,9 +39,10 @@ from tests.helpers import compare_bf16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-HEADS = (0, 39)          # sampled heads
-Q_PER_HEAD = 6           # sampled query blocks per head (two per volume class)
-K_PER_HEAD = 3           # sampled key blocks per head (one per volume class)
+VARIANTS = ("train2k", "train2k_op")
+PLAN_HEADS = (0, 13, 26, 39)   # whole plan compared
+HEADS = (0, 39)                # sampled outputs compared
+THREADS = max(1, min(16, int(os.environ.get("OMP_NUM_THREADS", 0) or os.cpu_count() or 1)))
 
 
 def note(msg, t0=[time.time()]):
@@ -41,35 +53,43 @@ def note(msg, t0=[time.time()]):
 @pytest.fixture(scope="module")
 def run():
     import dynamic_block_sparse_zone_amd as prism
-    wl = synth.WORKLOADS["train2k"]
-    note(f"workload {wl.name}: {wl.T}x{wl.H}x{wl.W}, {wl.heads} heads")
-    x = synth.make_inputs(wl, device=DEV, with_grad=True)
+    base = synth.WORKLOADS["train2k"]
+    note(f"inputs {base.T}x{base.H}x{base.W}, {base.heads} heads")
+    x = synth.make_inputs(base, device=DEV, with_grad=True)
     q, k, v, do, av = x["q"], x["k"], x["v"], x["do"], x["av"]
-    pl = prism.plan(q, k, v, av, T=wl.T, H=wl.H, W=wl.W, top_k=wl.top_k, top_p=wl.top_p)
-    note(f"plan: nnz {pl.nnz}")
-    o, lse = prism.attn_fwd(pl, q, k, v)
-    torch.cuda.synchronize()
-    note("forward")
-    dq, dk, dv = prism.attn_bwd(pl, q, k, v, o, lse, do)
-    torch.cuda.synchronize()
-    note("backward")
-    arrays = {n: pl.export(n) for n in ("shape_id", "blk_off", "blk_start", "row_ptr", "col_idx",
-                                        "colt_ptr", "colt_idx", "perm")}
-    note("plan exported")
-    heads = {}
-    for h in HEADS:
-        heads[h] = {
-            "in": {n: synth.to_numpy_bits(x[n][h:h + 1].contiguous()) for n in ("q", "k", "v", "do")},
-            "out": {n: t[h].float().cpu().numpy() for n, t in
-                    (("o", o), ("dq", dq), ("dk", dk), ("dv", dv))},
-            "lse": lse[h].cpu().numpy(),
-        }
-    # per-head sums over all tokens (fp64) for the gradient identities
-    sums = {n: t.double().sum(1).cpu().numpy() for n, t in (("dk", dk), ("dv", dv), ("do", do))}
-    for n, t in (("dk", dk), ("dv", dv)):
-        sums[n + "2"] = t.double().square().sum(1).cpu().numpy()
-    out = dict(wl=wl, arrays=arrays, heads=heads, av=av.cpu().numpy(), nnz=pl.nnz, sums=sums)
-    del x, q, k, v, do, o, lse, dq, dk, dv, pl
+    hsel = list(PLAN_HEADS)
+    out = {"wl": base, "av": av.cpu().numpy(), "var": {},
+           "in": {n: synth.to_numpy_bits(x[n][hsel].contiguous())
+                  for n in ("q", "k", "v", "do")}}
+    sums_do = do.double().sum(1).cpu().numpy()
+    for name in VARIANTS:
+        wl = synth.WORKLOADS[name]
+        note(f"{name}: plan (k={wl.top_k}, frac={wl.top_k_frac}, p={wl.top_p})")
+        pl = prism.plan(q, k, v, av, T=wl.T, H=wl.H, W=wl.W, top_k=wl.top_k,
+                        top_k_frac=wl.top_k_frac, top_p=wl.top_p)
+        info = pl.info()
+        note(f"{name}: nnz {pl.nnz}, persistent dK/dV launch {info['kv_persistent']}")
+        o, lse = prism.attn_fwd(pl, q, k, v)
+        dq, dk, dv = prism.attn_bwd(pl, q, k, v, o, lse, do)
+        torch.cuda.synchronize()
+        note(f"{name}: forward and backward done")
+        arrays = {n: pl.export(n) for n in ("shape_id", "blk_off", "blk_start", "row_ptr",
+                                            "col_idx", "colt_ptr", "colt_idx", "perm")}
+        r = {"wl": wl, "arrays": arrays, "nnz": pl.nnz, "info": info,
+             "out": {h: {n: t[h].cpu() for n, t in (("o", o), ("dq", dq), ("dk", dk),
+                                                    ("dv", dv))} for h in HEADS},
+             "lse": {h: lse[h].cpu().numpy() for h in HEADS},
+             # per-head sums over all tokens (fp64) for the gradient identities
+             "sums": {"dk": dk.double().sum(1).cpu().numpy(),
+                      "dv": dv.double().sum(1).cpu().numpy(), "do": sums_do,
+                      "dk2": dk.double().square().sum(1).cpu().numpy(),
+                      "dv2": dv.double().square().sum(1).cpu().numpy()}}
+        out["var"][name] = r
+        note(f"{name}: exported")
+        pl.close()
+        del pl, o, lse, dq, dk, dv
+        torch.cuda.empty_cache()
+    del x, q, k, v, do, av
     torch.cuda.empty_cache()
     return out
 
@@ -77,18 +97,19 @@ def run():
 _oracle = {}
 
 
-def oracle_head(run, orc, h):
-    """Oracle plan of head h alone, with every row selected (cached)."""
-    if h not in _oracle:
-        wl = run["wl"]
-        hb = run["heads"][h]["in"]
-        cfg = orc.Config(wl.T, wl.H, wl.W, 1, wl.head_dim, top_k=wl.top_k, top_p=wl.top_p,
+def oracle_plan(run, orc, name):
+    """Oracle plan of the PLAN_HEADS alone, with every row selected (cached)."""
+    if name not in _oracle:
+        wl = run["var"][name]["wl"]
+        hb = run["in"]
+        cfg = orc.Config(wl.T, wl.H, wl.W, len(PLAN_HEADS), wl.head_dim, top_k=wl.top_k,
+                         top_k_frac=wl.top_k_frac, top_p=wl.top_p,
                          volume_mask=wl.volume_mask, fixed_shape=tuple(wl.fixed_shape))
         opl = orc.plan(hb["q"], hb["k"], hb["v"], run["av"], cfg)
-        row_ptr, col = orc.select_all(opl)
-        note(f"oracle plan and selection of head {h}")
-        _oracle[h] = (opl, row_ptr, col)
-    return _oracle[h]
+        row_ptr, col = orc.select_all(opl, threads=THREADS)
+        note(f"{name}: oracle plan and selection of heads {PLAN_HEADS}")
+        _oracle[name] = (opl, row_ptr, col)
+    return _oracle[name]
 
 
 def head_rows(a, h):
@@ -99,68 +120,126 @@ def head_rows(a, h):
 
 
 def test_more_than_2_31_pairs(run):
-    assert run["nnz"] > 2 ** 31
+    assert run["var"]["train2k"]["nnz"] > 2 ** 31
 
 
-@pytest.mark.parametrize("h", HEADS)
-def test_plan_matches_oracle(run, orc, h):
-    a = run["arrays"]
-    wl = run["wl"]
+def test_dkdv_launch_form(run):
+    """The dense selection takes the ordered persistent dK/dV launch, the
+    operating point one work-group per unit."""
+    assert run["var"]["train2k"]["info"]["kv_persistent"]
+    assert not run["var"]["train2k_op"]["info"]["kv_persistent"]
+
+
+@pytest.mark.parametrize("name", VARIANTS)
+def test_plan_matches_oracle(run, orc, name):
+    got = run["var"][name]
+    a = got["arrays"]
+    wl = got["wl"]
     sid = a["shape_id"].reshape(wl.heads, -1)
-    opl, row_ptr, col = oracle_head(run, orc, h)
-    g0, g1, rp, c, rel = head_rows(a, h)
-    assert np.array_equal(sid[h], opl.shape_id[0])
-    assert g1 - g0 == opl.nblk(0)
-    assert np.array_equal(a["blk_start"][g0:g1], opl.blk_start)
-    assert np.array_equal(a["perm"].reshape(wl.heads, -1)[h], opl.perm[0])
-    assert np.array_equal(rel, row_ptr)
-    assert np.array_equal(c, col)
+    perm = a["perm"].reshape(wl.heads, -1)
+    opl, row_ptr, col = oracle_plan(run, orc, name)
+    for hi, h in enumerate(PLAN_HEADS):
+        g0, g1, rp, c, rel = head_rows(a, h)
+        o0, o1 = int(opl.blk_off[hi]), int(opl.blk_off[hi + 1])
+        assert np.array_equal(sid[h], opl.shape_id[hi]), (name, h)
+        assert g1 - g0 == o1 - o0
+        assert np.array_equal(a["blk_start"][g0:g1], opl.blk_start[o0:o1])
+        assert np.array_equal(perm[h], opl.perm[hi])
+        orp = row_ptr[o0:o1 + 1]
+        assert np.array_equal(rel, orp - orp[0]), (name, h)
+        assert np.array_equal(c, col[orp[0]:orp[-1]]), (name, h)
 
 
-@pytest.mark.parametrize("h", HEADS)
-def test_transpose_is_exact(run, h):
-    a = run["arrays"]
-    g0, g1, rp, c, rel = head_rows(a, h)
-    n = g1 - g0
-    rows = np.repeat(np.arange(n, dtype=np.int64), np.diff(rel))
-    order = np.lexsort((rows, c))
-    cp = a["colt_ptr"][g0:g1 + 1]
-    ct = a["colt_idx"][cp[0]:cp[-1]]
-    assert np.array_equal(cp - cp[0], np.concatenate([[0], np.cumsum(np.bincount(c, minlength=n))]))
-    assert np.array_equal(ct, rows[order].astype(np.int32))
+@pytest.mark.parametrize("name", VARIANTS)
+def test_transpose_is_exact(run, name):
+    a = run["var"][name]["arrays"]
+    for h in PLAN_HEADS:
+        g0, g1, rp, c, rel = head_rows(a, h)
+        n = g1 - g0
+        rows = np.repeat(np.arange(n, dtype=np.int64), np.diff(rel))
+        order = np.lexsort((rows, c))
+        cp = a["colt_ptr"][g0:g1 + 1]
+        ct = a["colt_idx"][cp[0]:cp[-1]]
+        assert np.array_equal(cp - cp[0],
+                              np.concatenate([[0], np.cumsum(np.bincount(c, minlength=n))]))
+        assert np.array_equal(ct, rows[order].astype(np.int32)), (name, h)
 
 
-def _pick(opl, n_per, rng):
-    """Blocks of head 0 of an oracle plan, spread over the volume classes."""
-    ln = opl.blk_len[: opl.nblk(0)]
+def _pick(opl, hi, n_per, rng):
+    """Local blocks of stacked head hi, n_per of each volume present,
+    largest volumes first (they take the oracle longest)."""
+    ln = opl.blk_len[int(opl.blk_off[hi]):int(opl.blk_off[hi + 1])]
     out = []
-    for vol in (64, 128, 256):
+    for vol in (256, 128, 64):
         ids = np.nonzero(ln == vol)[0]
         if len(ids):
             out += sorted(rng.choice(ids, min(n_per, len(ids)), replace=False).tolist())
     return out
 
 
-@pytest.mark.parametrize("h", HEADS)
-def test_forward_and_dq_sampled(run, orc, h):
-    rng = np.random.default_rng(7 + h)
-    opl = oracle_head(run, orc, h)[0]
-    hb, got = run["heads"][h]["in"], run["heads"][h]
-    blocks = _pick(opl, Q_PER_HEAD // 3, rng)
-    items = [(0, b) for b in blocks]
+def _rows(t, toks):
+    return t[torch.from_numpy(np.asarray(toks, np.int64))].float().numpy()
+
+
+@pytest.mark.parametrize("name", VARIANTS)
+def test_forward_and_dq_sampled(run, orc, name):
+    got = run["var"][name]
+    hb = run["in"]
+    opl = oracle_plan(run, orc, name)[0]
+    rng = np.random.default_rng(7)
+    items = [(PLAN_HEADS.index(h), b) for h in HEADS
+             for b in _pick(opl, PLAN_HEADS.index(h), 2, rng)]
     o_ref, lse_ref = orc.attn_fwd(hb["q"], hb["k"], hb["v"], opl, items)
-    note(f"oracle forward of {len(items)} blocks of head {h}")
+    note(f"{name}: oracle forward of {len(items)} blocks")
     dq_ref = orc.attn_bwd_q(hb["q"], hb["k"], hb["v"], hb["do"], opl, items)
-    note(f"oracle dQ of {len(items)} blocks of head {h}")
-    for it, b in enumerate(blocks):
-        toks = orc.tokens_of_block(opl, 0, b)
+    note(f"{name}: oracle dQ of {len(items)} blocks")
+    for it, (hi, b) in enumerate(items):
+        h = PLAN_HEADS[hi]
+        toks = orc.tokens_of_block(opl, hi, b)
         n = len(toks)
-        compare_bf16(got["out"]["o"][toks], o_ref[it, :n], what=f"O h{h} b{b}")
-        assert np.abs(got["lse"][toks] - lse_ref[it, :n]).max() < 2e-3, (h, b)
-        compare_bf16(got["out"]["dq"][toks], dq_ref[it, :n], what=f"dQ h{h} b{b}")
+        out = got["out"][h]
+        compare_bf16(_rows(out["o"], toks), o_ref[it, :n], what=f"{name} O h{h} b{b}")
+        assert np.abs(got["lse"][h][toks] - lse_ref[it, :n]).max() < 2e-3, (name, h, b)
+        compare_bf16(_rows(out["dq"], toks), dq_ref[it, :n], what=f"{name} dQ h{h} b{b}")
 
 
-def test_gradient_identities(run):
+def test_dkdv_sampled_operating_point(run, orc):
+    """Element-wise dK, dV of one key block per sampled head at the pages'
+    operating point: the block whose selecting query rows cost the oracle
+    least (B_i times the selected tokens of S_i, summed over the query
+    blocks i that selected it), among blocks some query selected."""
+    name = "train2k_op"
+    got = run["var"][name]
+    hb = run["in"]
+    opl, row_ptr, col = oracle_plan(run, orc, name)
+    items = []
+    for h in HEADS:
+        hi = PLAN_HEADS.index(h)
+        o0, n = int(opl.blk_off[hi]), opl.nblk(hi)
+        rp = row_ptr[o0:o0 + n + 1]
+        c = col[rp[0]:rp[-1]]
+        ln = opl.blk_len[o0:o0 + n].astype(np.int64)
+        cs = np.concatenate([[0], np.cumsum(ln[c])])
+        row_tok = cs[rp[1:] - rp[0]] - cs[rp[:-1] - rp[0]]     # selected tokens of S_i
+        cost = np.bincount(c, weights=np.repeat(ln * row_tok, np.diff(rp)), minlength=n)
+        cost[cost == 0] = np.inf
+        items.append((hi, int(np.argmin(cost))))
+        note(f"{name}: head {h} key block {items[-1][1]} ({ln[items[-1][1]]} tokens, "
+             f"oracle cost {cost.min():.3g} token pairs)")
+    dk_ref, dv_ref = orc.attn_bwd_kv(hb["q"], hb["k"], hb["v"], hb["do"], opl, items,
+                                     threads=THREADS, split=THREADS)
+    note(f"{name}: oracle dK/dV of {len(items)} key blocks")
+    for it, (hi, j) in enumerate(items):
+        h = PLAN_HEADS[hi]
+        toks = orc.tokens_of_block(opl, hi, j)
+        n = len(toks)
+        out = got["out"][h]
+        compare_bf16(_rows(out["dk"], toks), dk_ref[it, :n], what=f"dK h{h} b{j}")
+        compare_bf16(_rows(out["dv"], toks), dv_ref[it, :n], what=f"dV h{h} b{j}")
+
+
+@pytest.mark.parametrize("name", VARIANTS)
+def test_gradient_identities(run, name):
     """Per head and channel: sum_keys dV = sum_queries dO, sum_keys dK = 0.
 
     The scale is the root of the sum of squares over keys: a sum of that
@@ -172,28 +251,30 @@ def test_gradient_identities(run):
     ~10^6 query rows of such residuals times q reaches several percent of
     the scale on these inputs; its bound is set well above that and well
     below 1."""
-    s = run["sums"]
+    s = run["var"][name]["sums"]
     ev, ek = [], []
     for h in range(run["wl"].heads):
         ev.append((np.abs(s["dv"][h] - s["do"][h]) / np.sqrt(s["dv2"][h])).max())
         ek.append((np.abs(s["dk"][h]) / np.sqrt(s["dk2"][h])).max())
-    note(f"identity residuals: dV max {max(ev):.4f}, dK max {max(ek):.4f}")
+    note(f"{name}: identity residuals: dV max {max(ev):.4f}, dK max {max(ek):.4f}")
     assert max(ev) < 5e-2, ev
     assert max(ek) < 0.25, ek
 
 
-@pytest.mark.parametrize("h", HEADS)
-def test_unselected_keys_get_no_gradient(run, h):
-    a = run["arrays"]
-    wl = run["wl"]
-    g0, g1, rp, c, rel = head_rows(a, h)
-    n = g1 - g0
-    chosen = np.zeros(n, bool)
-    chosen[c] = True
-    perm = a["perm"].reshape(wl.heads, -1)[h]
-    start = a["blk_start"][g0:g1]
-    nxt = np.append(start[1:], wl.N)
-    got = run["heads"][h]["out"]
-    for j in np.nonzero(~chosen)[0]:
-        toks = perm[start[j]:nxt[j]]
-        assert np.all(got["dk"][toks] == 0) and np.all(got["dv"][toks] == 0), (h, j)
+@pytest.mark.parametrize("name", VARIANTS)
+def test_unselected_keys_get_no_gradient(run, name):
+    got = run["var"][name]
+    a = got["arrays"]
+    wl = got["wl"]
+    for h in HEADS:
+        g0, g1, rp, c, rel = head_rows(a, h)
+        n = g1 - g0
+        chosen = np.zeros(n, bool)
+        chosen[c] = True
+        perm = a["perm"].reshape(wl.heads, -1)[h]
+        start = a["blk_start"][g0:g1]
+        nxt = np.append(start[1:], wl.N)
+        out = got["out"][h]
+        for j in np.nonzero(~chosen)[0]:
+            toks = torch.from_numpy(perm[start[j]:nxt[j]].astype(np.int64))
+            assert torch.all(out["dk"][toks] == 0) and torch.all(out["dv"][toks] == 0), (h, j)

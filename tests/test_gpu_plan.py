@@ -43,6 +43,10 @@ def _check_plan_arrays(pl, opl, cfg):
     start = pl.export("blk_start")
     np.testing.assert_array_equal(start[:G], opl.blk_start)
     np.testing.assert_array_equal(pl.export("perm").reshape(H, -1), opl.perm)
+    # each block's first token: where the attention kernels start the
+    # block -> token map of its rows
+    heads_of = np.repeat(np.arange(H), np.diff(opl.blk_off))
+    np.testing.assert_array_equal(pl.export("blk_org")[:G], opl.perm[heads_of, opl.blk_start])
     D = cfg.head_dim
     np.testing.assert_array_equal(pl.export("qbar").reshape(G, D), opl.qbar)
     np.testing.assert_array_equal(pl.export("kbar").reshape(G, D), opl.kbar)
@@ -130,6 +134,19 @@ def test_plan_variants(prism, orc, over):
     _check_csr(pl, opl, orc)
 
 
+@pytest.mark.parametrize("shape_map,alpha", [(0, 1 / 3), (0, 2.0), (1, 0.5), (2, 0.5),
+                                             (3, 0.5), (4, 0.5)])
+def test_shape_map_variants(prism, orc, shape_map, alpha):
+    """The shape-mapping ablations (power alpha = 1/3 and 2, isotropic,
+    softmax, rank, entropy) give the oracle's shapes, block table and lists
+    bit for bit."""
+    for name in ("check", "small"):
+        wl, pl, opl = _case(prism, orc, name, shape_map=shape_map, alpha=alpha)
+        _check_plan_arrays(pl, opl, opl.cfg)
+        _check_csr(pl, opl, orc, rows_per_head=None if name == "check" else 40)
+        pl.close()
+
+
 def test_block_scores_bit_exact(prism, orc):
     wl, pl, opl = _case(prism, orc, "small")
     rng = np.random.default_rng(3)
@@ -176,3 +193,44 @@ def test_kv_order(prism, over):
             unit_work[u] = work[first:max(last, first + 1)].max()
         want = sorted(range(upH), key=lambda u: (-min(int(unit_work[u]), 16383), u))
         np.testing.assert_array_equal(order[h], np.array(want, np.int32))
+
+
+def test_shot_cut_zones(prism, orc):
+    """Shot-cut-aware temporal zones: the GPU finds the oracle's cuts (the
+    two spliced shots of the cuts workload; the energies of every frame are
+    far from the threshold) and gives its shapes, block table and lists bit
+    for bit."""
+    wl = synth.WORKLOADS["cuts"]
+    wl_, pl, opl = _case(prism, orc, "cuts", cut_threshold=4.0)
+    got = pl.export("cuts")
+    _, energy = orc.detect_cuts(synth.to_numpy_bits(
+        synth.make_inputs(wl, device="cpu", with_grad=False)["v"]), opl.cfg)
+    thr = 4.0 * energy[1:].mean()
+    assert np.all(np.abs(energy[1:] - thr) > 1e-6 * thr)      # no decision near the threshold
+    np.testing.assert_array_equal(got, opl.cuts)
+    assert np.nonzero(got)[0].tolist() == list(wl.cut_frames)
+    _check_plan_arrays(pl, opl, opl.cfg)
+    _check_csr(pl, opl, orc)
+
+
+def test_schedule_gives_nested_selections(prism, orc):
+    """A Top-p schedule loosening from 0.2 to 0.9 over the steps: each step's
+    selection holds the previous one (both are prefixes of one order), and
+    each is the oracle's for its p."""
+    wl = synth.WORKLOADS["check"]
+    x = synth.make_inputs(wl, device="cpu", with_grad=False)
+    dx = to_dev(x, DEV)
+    hb = host_bits(x)
+    prev = None
+    for step in range(4):
+        p = prism.schedule_value("cosine", step, 4, 0.2, 0.9)
+        pl = gpu_plan(prism, wl, dx, top_p=p)
+        rp, col = pl.export("row_ptr"), pl.export("col_idx")
+        rows = [set(col[rp[g]:rp[g + 1]].tolist()) for g in range(len(rp) - 1)]
+        if prev is not None:
+            assert all(a <= b for a, b in zip(prev, rows))
+        prev = rows
+        opl = orc.plan(hb["q"], hb["k"], hb["v"], x["av"].numpy(),
+                       oracle_config(orc, wl, top_p=p))
+        _check_csr(pl, opl, orc, rows_per_head=30, seed=step)
+        pl.close()

@@ -595,3 +595,174 @@ def test_backward_head_matches_autograd_and_blockwise(orc, case):
         sparse |= bool(np.any(np.all(dv == 0, axis=1)))
     if case.get("top_p") == 0.0:
         assert sparse      # some key tokens received no gradient at all
+
+
+# ----------------------------------------------------------- shape-mapping variants
+
+def test_written_log_and_exp(orc):
+    """The fp64 logarithm and exponential the mapping variants use agree with
+    the correctly rounded functions to within 4 ulp over the ranges used."""
+    rng = np.random.default_rng(31)
+    for x in np.concatenate([np.exp(rng.uniform(-12, 2, 2000)), [1.0, 2.0, 0.5, 3.0]]):
+        x = float(np.float32(x))
+        assert abs(orc.wlog2(x) - math.log2(x)) <= 4 * np.spacing(max(1.0, abs(math.log2(x))))
+        assert abs(orc.wln(x) - math.log(x)) <= 4 * np.spacing(max(1.0, abs(math.log(x))))
+    for x in rng.uniform(-3, 0, 2000):
+        assert abs(orc.wexp(x) / math.exp(x) - 1) <= 4 * 2.0 ** -52
+
+
+def _target_decimal(g, B, shape_map, alpha):
+    """The mapping's target point in 60-digit decimal arithmetic."""
+    getcontext().prec = 60
+    ln2 = Decimal(2).ln()
+    S = Decimal(int(math.log2(B)))
+    gd = [Decimal(float(x)) for x in g]
+    if shape_map == 0:
+        a = Decimal(float(np.float32(alpha)))
+        lg = [x.ln() / ln2 for x in gd]
+        c = (S + a * sum(lg)) / 3
+        return [-a * lg[d] + c for d in range(3)]
+    if shape_map == 1:
+        return [S / 3] * 3
+    if shape_map == 2:
+        w = [(-x).exp() for x in gd]
+        return [S * x / sum(w) for x in w]
+    if shape_map == 3:
+        r = [sum(1 for e in range(3) if g[e] > g[d] or (g[e] == g[d] and e < d)) for d in range(3)]
+        return [S / 3 + r[d] - 1 for d in range(3)]
+    gs = sum(gd)
+    inf = [-(x / gs).ln() for x in gd]
+    return [S * x / sum(inf) for x in inf]
+
+
+def _nearest_target(t, B, margin):
+    """Nearest candidate to t, or None when the two nearest are within margin."""
+    from oracle import oracle as O
+    d = []
+    for i, (bt, bh, bw, BB) in enumerate(O.candidates()):
+        if BB == B:
+            e = [Decimal(int(math.log2(x))) for x in (bt, bh, bw)]
+            d.append((sum((t[k] - e[k]) ** 2 for k in range(3)), i))
+    d.sort()
+    if d[1][0] - d[0][0] < margin:
+        return None
+    return d[0][1]
+
+
+@pytest.mark.parametrize("shape_map,alpha", [(0, 1 / 3), (0, 2.0), (0, 0.5), (1, 0.5),
+                                             (2, 0.5), (3, 0.5), (4, 0.5)])
+def test_shape_mappings_brute_force(orc, shape_map, alpha):
+    """paper.rainbus.top "技术新颖性" (Table 10) names b ~ g^(-alpha) for
+    alpha in {1/3, 1/2, 2}, isotropic, softmax, rank and entropy mappings:
+    each, in the reading the design notes give, against the same target
+    point computed in 60-digit decimal arithmetic and the nearest candidate
+    by plain Euclidean distance (cases within 1e-9 of a tie are skipped)."""
+    rng = np.random.default_rng(40 + shape_map)
+    gs = [rng.uniform(1e-4, 2.0, 3) for _ in range(150)]
+    gs += [np.exp(rng.uniform(-9, 0.7, 3)) for _ in range(150)]
+    checked = 0
+    for g in gs:
+        g = np.asarray(g, np.float32)
+        for B in (64, 128, 256):
+            t = _target_decimal(g, B, shape_map, alpha)
+            got_t = orc.map_target(g, B, shape_map, alpha)
+            assert max(abs(float(t[d]) - got_t[d]) for d in range(3)) < 1e-12
+            assert abs(sum(got_t) - math.log2(B)) < 1e-12        # sum_d l_d = S
+            want = _nearest_target(t, B, Decimal("1e-9"))
+            if want is None:
+                continue
+            assert orc.nearest_shape_map(g, B, shape_map, alpha) == want, (g, B)
+            checked += 1
+    assert checked >= 250
+
+
+def test_shape_mapping_special_cases(orc):
+    cand = orc.candidates()
+    shape = lambda g, B, m, a=0.5: tuple(int(x) for x in cand[orc.nearest_shape_map(
+        np.asarray(g, np.float32), B, m, a)][:3])
+    rng = np.random.default_rng(50)
+    for _ in range(50):
+        g = rng.uniform(1e-4, 2, 3)
+        # isotropic: the most cubic candidate, ties to the lower id
+        assert [shape(g, B, 1) for B in (64, 128, 256)] == [(4, 4, 4), (4, 4, 8), (4, 8, 8)]
+        # alpha = 0 is isotropic; alpha = 1/2 is the pages' exact method
+        assert [shape(g, B, 0, 0.0) for B in (64, 128, 256)] == [(4, 4, 4), (4, 4, 8), (4, 8, 8)]
+        for B in (64, 128, 256):
+            assert orc.nearest_shape_map(np.asarray(g, np.float32), B, 0, 0.5) == \
+                orc.nearest_shape(np.asarray(g, np.float32), B)
+    # equal indicators: every mapping that sees magnitudes is isotropic; rank
+    # sees only the order, and equal values rank the earlier axis first
+    for m in (0, 2, 4):
+        assert shape([1 / 3] * 3, 64, m, 2.0 if m == 0 else 0.5) == (4, 4, 4)
+    assert shape([1 / 3] * 3, 64, 3) == (2, 4, 8)
+    # rank keeps only the order: the largest g gets the smallest edge
+    assert shape([0.9, 0.3, 0.1], 64, 3) == (2, 4, 8)
+    assert shape([0.9, 0.3, 0.1], 64, 3) == shape([1.9, 1.0, 0.001], 64, 3)
+    assert shape([0.1, 0.3, 0.9], 64, 3) == (8, 4, 2)
+    # a larger exponent exaggerates the anisotropy: b ~ g^-2 reaches the
+    # most elongated candidate where b ~ g^-1/3 stays cubic
+    g = [0.5, 0.3, 0.2]
+    assert shape(g, 64, 0, 2.0) == (2, 4, 8)
+    assert shape(g, 64, 0, 1 / 3) == (4, 4, 4)
+
+
+# ----------------------------------------------------------- A->V norm map
+
+def test_av_cross_norm_is_textbook_attention(orc):
+    """paper.rainbus.top "双分支视频-音频 DiT 与跨模态交叉注意力": the norm map is
+    ||h_hat||_2 of h_hat = CrossAttn(h, K_a, V_a) per video position: against
+    fp64 torch softmax attention and its norm over heads and channels; with
+    identical audio keys the attention is uniform and h_hat is the mean of the
+    audio values."""
+    rng = np.random.default_rng(60)
+    heads, N, Na, D = 3, 512, 128, 64
+    q = rng.normal(size=(heads, N, D)).astype(np.float32)
+    ka = rng.normal(size=(heads, Na, D)).astype(np.float32)
+    va = rng.normal(size=(heads, Na, D)).astype(np.float32)
+    toks = np.arange(0, N, 7)
+    norm, o = orc.av_cross(q, ka, va, toks, want_o=True)
+    Q, K, V = (torch.tensor(x, dtype=torch.float64) for x in (q, ka, va))
+    ref = (torch.softmax(Q @ K.transpose(1, 2) / math.sqrt(D), -1) @ V)[:, toks]
+    np.testing.assert_allclose(o, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(norm, ref.permute(1, 0, 2).reshape(len(toks), -1).norm(dim=1),
+                               rtol=1e-12)
+    ka_same = np.repeat(ka[:, :1], Na, axis=1)
+    norm_u, o_u = orc.av_cross(q, ka_same, va, toks, want_o=True)
+    mean = va.astype(np.float64).mean(axis=1)                      # [heads, D]
+    np.testing.assert_allclose(o_u, np.broadcast_to(mean, o_u.shape), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(norm_u, np.sqrt((mean ** 2).sum()), rtol=1e-12)
+
+
+# ----------------------------------------------------------- shot-cut-aware zones
+
+def test_shot_cut_detection_and_zone_caps(orc):
+    """paper.rainbus.top "独立分析的弱点" (1): shot cuts detected from frame
+    differences split the zones they fall in.  The energy against plain
+    numpy fp64; cuts at frames 12 (offset 4 of zone row 1) and 19 (offset 3
+    of row 2) cap b_T at 4 and 2, the second also the volume at 128; the
+    uncut row keeps the shapes of the plan without cut detection."""
+    T, H, W, D = 24, 16, 16, 64
+    rng = np.random.default_rng(70)
+    t = np.arange(T)[:, None, None, None]
+    ph = [rng.uniform(0, 6.3, (1, H, W, D)) for _ in range(3)]
+    seg = np.where(t < 12, 0, np.where(t < 19, 1, 2))
+    v = np.choose(seg, [np.sin(0.3 * t + ph[0]), np.sin(0.2 * t + ph[1]), np.sin(0.25 * t + ph[2])])
+    v = (v + 0.05 * rng.normal(size=v.shape)).astype(np.float32).reshape(1, -1, D)
+    cfg = _cfg(orc, T, H, W, 1, D, cut_threshold=4.0)
+    cuts, e = orc.detect_cuts(v, cfg)
+    x = v.reshape(T, H * W * D).astype(np.float64)
+    ref = np.concatenate([[0.0], ((x[1:] - x[:-1]) ** 2).mean(axis=1)])
+    np.testing.assert_allclose(e, ref, rtol=1e-12)
+    assert np.nonzero(cuts)[0].tolist() == [12, 19]
+    assert orc.cut_caps(cuts, T).tolist() == [8, 4, 2]
+    assert orc.detect_cuts(v, _cfg(orc, T, H, W, 1, D))[0].sum() == 0     # threshold 0: off
+    q = k = v
+    pl = orc.plan(q, k, v, None, cfg)
+    pl0 = orc.plan(q, k, v, None, _cfg(orc, T, H, W, 1, D))
+    cand = orc.candidates()
+    zpt = (H // 8) * (W // 8)
+    row = lambda p, zt: p.shape_id[0, zt * zpt:(zt + 1) * zpt]
+    assert np.array_equal(row(pl, 0), row(pl0, 0))
+    assert np.all(cand[row(pl, 1), 0] <= 4)
+    assert np.all(cand[row(pl, 2), 0] <= 2) and np.all(cand[row(pl, 2), 3] <= 128)
+    assert np.any(cand[row(pl0, 2), 0] > 2) or np.any(cand[row(pl0, 2), 3] > 128)
