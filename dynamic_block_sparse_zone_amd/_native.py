@@ -24,6 +24,7 @@ PRISM_BF16 = 1
 SHAPE_MAPS = {"power": 0, "isotropic": 1, "softmax": 2, "rank": 3, "entropy": 4}
 SCHEDULES = {"constant": 0, "linear": 1, "cosine": 2}
 
+NOALLOC_SCRATCH_BYTES = 128 << 20   # PRISM_NOALLOC_SCRATCH_BYTES
 
 ARRAYS = {
     "zone_stats": 0, "audio_stats": 1, "shape_id": 2, "blk_off": 3, "blk_start": 4,
@@ -35,8 +36,8 @@ ARRAYS = {
 EXPORTED = [
     "prism_config_default", "prism_config_check", "prism_plan_workspace_size",
     "prism_plan_create", "prism_plan_destroy", "prism_attn_fwd",
-    "prism_attn_bwd_workspace_size", "prism_attn_bwd", "prism_av_cross_attn",
-    "prism_block_scores",
+    "prism_attn_bwd_workspace_size", "prism_attn_bwd", "prism_attn_bwd_noalloc",
+    "prism_av_cross_attn", "prism_block_scores",
     "prism_plan_array_bytes", "prism_plan_export", "prism_plan_info", "prism_candidate",
     "prism_schedule_value",
     "prism_status_str", "prism_timing_enable", "prism_timing_read",
@@ -98,6 +99,7 @@ def lib() -> ctypes.CDLL:
         L.prism_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.prism_attn_bwd_workspace_size.argtypes = [cfgp, ctypes.POINTER(sz)]
         L.prism_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.prism_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.prism_av_cross_attn.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp]
         L.prism_block_scores.argtypes = [vp, i32, vp, vp]
         L.prism_plan_array_bytes.argtypes = [vp, i32, ctypes.POINTER(sz)]

@@ -178,6 +178,18 @@ def attn_bwd(pl: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace
     return dq, dk, dv
 
 
+def attn_bwd_noalloc(pl: Plan, q, k, v, o, lse, do, dq, dk, dv):
+    """prism_attn_bwd_noalloc: the backward with its scratch in the library's
+    static per-GPU array (no workspace, no allocation).  The caller passes
+    the output tensors; raises PrismError (workspace too small) when the
+    problem needs more scratch than the array holds."""
+    nat.check(nat.lib().prism_attn_bwd_noalloc(pl.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                               _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                               _ptr(dv), _stream(q.device)),
+              "prism_attn_bwd_noalloc")
+    return dq, dk, dv
+
+
 def av_cross_attn(q, ka, va, o=None, norm=None, want_o=False):
     """The A->V norm map: h_hat = softmax(q ka^T / sqrt(D)) va per head for
     the video queries q [heads, N, D] over the audio keys and values

@@ -392,6 +392,29 @@ prism_status bwd_run(const prism_plan_t* plan, const void* q, const void* k, con
   return ok ? PRISM_OK : PRISM_EDEVICE;
 }
 
+// Scratch of the allocation-free backward: one copy per GPU, held from the
+// library's load until the process ends.  In host code `scratch` names a
+// host-side stand-in; the device address of each GPU's copy comes from
+// hipGetSymbolAddress with that GPU current, and only that address is used.
+static __device__ __align__(256) char scratch[PRISM_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+prism_status scratch_address(void** out) {
+  int dev = -1;
+  PRISM_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return PRISM_EDEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PRISM_EDEVICE;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return PRISM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -402,6 +425,22 @@ prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void*
                             size_t workspace_bytes, void* stream) {
   return bwd_run(plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes,
                  (hipStream_t)stream, true);
+}
+
+prism_status prism_attn_bwd_noalloc(const prism_plan_t* plan, const void* q, const void* k,
+                                    const void* v, const void* o, const float* lse,
+                                    const void* d_o, void* dq, void* dk, void* dv,
+                                    void* stream) {
+  if (!plan) return PRISM_EINVAL;
+  size_t need = 0;
+  prism_status s = prism_attn_bwd_workspace_size(&plan->cfg, &need);
+  if (s != PRISM_OK) return s;
+  if (need > (size_t)PRISM_NOALLOC_SCRATCH_BYTES) return PRISM_ENOMEM_WORKSPACE;
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != PRISM_OK) return s;
+  return bwd_run(plan, q, k, v, o, lse, d_o, dq, dk, dv, ws, PRISM_NOALLOC_SCRATCH_BYTES,
+                 (hipStream_t)stream, false);
 }
 
 prism_status prism_av_cross_attn(const void* q, const void* ka, const void* va, int32_t heads,

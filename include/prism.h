@@ -184,6 +184,26 @@ prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void*
                             void* dq, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* Size of the per-GPU scratch array of prism_attn_bwd_noalloc (128 MiB). */
+#define PRISM_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* prism_attn_bwd for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and results as prism_attn_bwd
+ * without the workspace: the backward's scratch lives in a static device
+ * array of PRISM_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends.  The call allocates nothing (no hipMalloc,
+ * no hipFree, no event creation; the stage timing of prism_timing_enable
+ * skips it).  Returns PRISM_ENOMEM_WORKSPACE, before any device work, when
+ * prism_attn_bwd_workspace_size exceeds the array.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two host threads) race and must not be issued; calls ordered on
+ * one stream are safe, since each fully rewrites the scratch it reads. */
+prism_status prism_attn_bwd_noalloc(const prism_plan_t* plan, const void* q, const void* k,
+                                    const void* v, const void* o, const float* lse,
+                                    const void* d_o, void* dq, void* dk, void* dv,
+                                    void* stream);
+
 /* The A->V norm map of the next layer: the audio-to-video cross-attention
  * h_hat = CrossAttn(h, K_a, V_a) of the video tokens over the audio tokens
  * and, in its epilogue, the L2 norm of each video position's output

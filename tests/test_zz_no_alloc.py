@@ -1,0 +1,74 @@
+"""The allocation-free backward, prism_attn_bwd_noalloc (for callers that
+cannot allocate: its scratch is the library's static per-GPU array), against
+the backward with a caller workspace, prism_attn_bwd, through the C ABI.
+
+Both run the same deterministic kernels, so the gradients must agree bit for
+bit (stricter than the bf16 bar).  Two calls in a row, the second on a
+smaller problem, show that the shared array carries nothing from one call to
+the next; a problem whose scratch exceeds the array is rejected before any
+device work, leaving the outputs untouched."""
+import ctypes
+
+import pytest
+import torch
+
+from dynamic_block_sparse_zone_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def prism():
+    import dynamic_block_sparse_zone_amd as p
+    return p
+
+
+def _layer(prism, wl):
+    x = synth.make_inputs(wl, device="cpu", with_grad=True)
+    q, k, v, do, av = (x[n].to(DEV) for n in ("q", "k", "v", "do", "av"))
+    pl = prism.plan(q, k, v, av, T=wl.T, H=wl.H, W=wl.W, top_k=wl.top_k, top_p=wl.top_p)
+    o, lse = prism.attn_fwd(pl, q, k, v)
+    return pl, q, k, v, do, o, lse
+
+
+def test_noalloc_matches_workspace_backward_twice(prism):
+    for wl in (synth.WORKLOADS["check"], synth.WORKLOADS["bwdcheck"]):
+        print(f"[no-alloc] workload={wl.name} heads={wl.heads}", flush=True)
+        pl, q, k, v, do, o, lse = _layer(prism, wl)
+        ref = prism.attn_bwd(pl, q, k, v, o, lse, do)
+        got = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+        prism.attn_bwd_noalloc(pl, q, k, v, o, lse, do, *got)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), ref, got):
+            assert torch.equal(a, b), (wl.name, name)
+        pl.close()
+
+
+def test_noalloc_rejects_problems_beyond_the_array(prism):
+    from dynamic_block_sparse_zone_amd import _native as nat
+
+    def need(heads):
+        cfg = prism.make_config(64, 128, 128, heads, 128, torch.bfloat16)
+        n = ctypes.c_size_t()
+        nat.check(nat.lib().prism_attn_bwd_workspace_size(ctypes.byref(cfg), ctypes.byref(n)),
+                  "prism_attn_bwd_workspace_size")
+        return n.value
+
+    heads = nat.NOALLOC_SCRATCH_BYTES // need(1) + 1
+    assert need(heads) > nat.NOALLOC_SCRATCH_BYTES >= need(heads - 1)
+    wl = synth.Workload("noalloc_over", 64, 128, 128, heads, 128, "bf16", top_k=4, top_p=0.0,
+                        kind="iid", seed=1009)
+    print(f"[no-alloc] over-size problem: {heads} heads x {wl.N} tokens, {need(heads)} bytes",
+          flush=True)
+    x = synth.make_inputs(wl, device=DEV, with_grad=True)
+    q, k, v, do, av = (x[n] for n in ("q", "k", "v", "do", "av"))
+    pl = prism.plan(q, k, v, av, T=wl.T, H=wl.H, W=wl.W, top_k=wl.top_k, top_p=wl.top_p)
+    o, lse = prism.attn_fwd(pl, q, k, v)
+    got = tuple(torch.full_like(q, 7.0) for _ in range(3))
+    with pytest.raises(nat.PrismError) as e:
+        prism.attn_bwd_noalloc(pl, q, k, v, o, lse, do, *got)
+    assert e.value.status == nat.PRISM_ENOMEM_WORKSPACE
+    torch.cuda.synchronize()
+    assert all(bool(torch.all(t == 7.0)) for t in got)
+    pl.close()
