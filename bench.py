@@ -151,6 +151,49 @@ def summarize_mfma(csv_path, agent_csv, workload, cmds, out):
     print("\n".join(lines))
 
 
+def summarize_trace(db, workload, cmds, out):
+    """Per-kernel summary of a rocprofv3 --kernel-trace run (its rocpd
+    SQLite output): the library's kernels with dispatch count, total and
+    average duration, the longest dispatch and its launch shape."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration, grid_x, grid_y, workgroup_x, vgpr_count, "
+                       "accum_vgpr_count, lds_size from kernels").fetchall()
+    agg = {}
+    other_ns, other_n = 0, 0
+    for name, dur, gx, gy, wx, vg, ag, lds in rows:
+        if "prism::" not in name:
+            other_ns += dur
+            other_n += 1
+            continue
+        key = name.split("(")[0].replace("void ", "").replace("prism::", "")
+        a = agg.setdefault(key, {"n": 0, "tot": 0, "max": 0, "shape": None})
+        a["n"] += 1
+        a["tot"] += dur
+        if dur > a["max"]:
+            a["max"] = dur
+            a["shape"] = (gx, gy, wx, vg, ag, lds)
+    total = sum(a["tot"] for a in agg.values())
+    lines = [f"# Kernel trace, {workload}", "",
+             "rocprofv3 `--kernel-trace --stats` over one bench step (after the small-grid "
+             "warm-up); durations from the trace's rocpd database.  The longest dispatch of "
+             "each attention kernel is the full-size one.", "",
+             "Command (from /tmp, TMPDIR=/tmp):", "", *[f"    {c}" for c in cmds], "",
+             "| kernel | dispatches | total ms | average ms | longest ms | % of library time | "
+             "grid (x, y) | threads | VGPR | AGPR | LDS B |",
+             "|---|---:|---:|---:|---:|---:|---|---:|---:|---:|---:|"]
+    for k, a in sorted(agg.items(), key=lambda kv: -kv[1]["tot"]):
+        gx, gy, wx, vg, ag, lds = a["shape"]
+        lines.append(f"| `{k}` | {a['n']} | {a['tot'] / 1e6:.3f} | {a['tot'] / a['n'] / 1e6:.3f} |"
+                     f" {a['max'] / 1e6:.3f} | {100 * a['tot'] / total:.2f} | ({gx}, {gy}) | {wx} |"
+                     f" {vg} | {ag} | {lds} |")
+    lines += ["", f"Other (input generation, torch) kernels: {other_n} dispatches, "
+              f"{other_ns / 1e6:.1f} ms.", ""]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def summarize_pmc(fetch_csv, write_csv, stage, workload, cmds, out):
     """Turns two rocprofv3 counter-collection CSVs (FETCH_SIZE, WRITE_SIZE,
     in KiB per dispatch) of a profiled step that ends with the calibration
@@ -224,6 +267,9 @@ def parse():
                     help="write the traffic summary of the dominant kernel from two "
                          "rocprofv3 counter-collection CSVs, then exit")
     ap.add_argument("--stage", default="bwd.dkdv", help="kernel stage for --summarize-pmc")
+    ap.add_argument("--summarize-trace", metavar="ROCPD_DB",
+                    help="write the per-kernel summary of a rocprofv3 --kernel-trace run "
+                         "(its rocpd database) to profiles/<workload>_kernel_trace.md, then exit")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_CSV", "AGENT_CSV"),
                     help="write the attention kernels' MFMA utilisation summary from one "
                          "rocprofv3 counter pass (and its agent info), then exit")
@@ -290,6 +336,10 @@ def main():
                       traffic_file(args.stage, args.workload))
         summarize_hbm_table(*args.summarize_pmc, args.workload, args.cmd,
                             os.path.join(ROOT, "profiles", f"kernels_{args.workload}_hbm.md"))
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, args.cmd,
+                        os.path.join(ROOT, "profiles", f"{args.workload}_kernel_trace.md"))
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, args.workload, args.cmd,

@@ -25,6 +25,7 @@ _NP = {
     "qexp": np.int32, "kexp": np.int32, "row_ptr": np.int64, "col_idx": np.int32,
     "colt_ptr": np.int64, "colt_idx": np.int32, "perm": np.int32, "qgrid": np.uint16,
     "kgrid": np.uint16, "kv_order": np.int32, "blk_org": np.int32, "cuts": np.uint8,
+    "qlo": np.uint16, "klo": np.uint16,
 }
 
 

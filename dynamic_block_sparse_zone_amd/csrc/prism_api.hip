@@ -126,6 +126,8 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
   P->kbar = A.take<float>(G * D);
   P->qgrid = A.take<uint16_t>(G * D);
   P->kgrid = A.take<uint16_t>(G * D);
+  P->qlo = A.take<uint16_t>(G * D);
+  P->klo = A.take<uint16_t>(G * D);
   P->qexp = A.take<int32_t>(G);
   P->kexp = A.take<int32_t>(G);
   P->scores = A.take<float>(maxblk * maxblk);
@@ -502,6 +504,8 @@ static const void* array_ptr(const prism_plan_t* pl, int which, size_t* bytes) {
       return P.korder;
     case PRISM_ARR_BLK_ORG: *bytes = sizeof(int32_t) * G; return P.blk_org;
     case PRISM_ARR_CUTS: *bytes = c.cut_threshold > 0.0f ? (size_t)c.T : 0; return P.cuts;
+    case PRISM_ARR_QLO: *bytes = sizeof(uint16_t) * G * c.head_dim; return P.qlo;
+    case PRISM_ARR_KLO: *bytes = sizeof(uint16_t) * G * c.head_dim; return P.klo;
     default: *bytes = 0; return nullptr;
   }
 }
@@ -510,13 +514,13 @@ prism_status prism_plan_array_bytes(const prism_plan_t* plan, int32_t which, siz
   if (!plan || !bytes) return PRISM_EINVAL;
   const void* p = array_ptr(plan, which, bytes);
   if (!p && *bytes) return PRISM_EINVAL;
-  if (which < 0 || which > PRISM_ARR_CUTS) return PRISM_EINVAL;
+  if (which < 0 || which > PRISM_ARR_KLO) return PRISM_EINVAL;
   return PRISM_OK;
 }
 
 prism_status prism_plan_export(const prism_plan_t* plan, int32_t which, void* dst,
                                size_t dst_bytes, void* stream) {
-  if (!plan || !dst || which < 0 || which > PRISM_ARR_CUTS) return PRISM_EINVAL;
+  if (!plan || !dst || which < 0 || which > PRISM_ARR_KLO) return PRISM_EINVAL;
   size_t bytes = 0;
   const void* p = array_ptr(plan, which, &bytes);
   if (dst_bytes < bytes) return PRISM_EINVAL;

@@ -148,8 +148,10 @@ struct PlanDev {
   int32_t* blk_head;   // [Gmax]
   float* qbar;         // [Gmax][D]
   float* kbar;
-  uint16_t* qgrid;     // [Gmax][D] bf16 integers
+  uint16_t* qgrid;     // [Gmax][D] bf16 integers: high part of the two-level grid
   uint16_t* kgrid;
+  uint16_t* qlo;       // [Gmax][D] bf16 integers: low part (x ~ 2^E (hi + 2^-8 lo))
+  uint16_t* klo;
   int32_t* qexp;       // [Gmax]
   int32_t* kexp;
   int32_t* blk_org;    // [Gmax]  original token of the block's first row (within head)

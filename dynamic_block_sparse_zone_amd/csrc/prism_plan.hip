@@ -619,8 +619,8 @@ __global__ __launch_bounds__(512) void k_pool(
     const int64_t* __restrict__ blk_off, int32_t* __restrict__ blk_start,
     int32_t* __restrict__ blk_org, uint8_t* __restrict__ blk_shape,
     int32_t* __restrict__ blk_head, float* __restrict__ qbar, float* __restrict__ kbar,
-    uint16_t* __restrict__ qgrid, uint16_t* __restrict__ kgrid, int32_t* __restrict__ qexp,
-    int32_t* __restrict__ kexp) {
+    uint16_t* __restrict__ qgrid, uint16_t* __restrict__ kgrid, uint16_t* __restrict__ qlo,
+    uint16_t* __restrict__ klo, int32_t* __restrict__ qexp, int32_t* __restrict__ kexp) {
   constexpr int D = 64 * CPL;
   __shared__ float tsum[2][8][D];
   const int hm = blockIdx.x;
@@ -680,11 +680,17 @@ __global__ __launch_bounds__(512) void k_pool(
       }
       float* xb = which ? kbar : qbar;
       uint16_t* gr = which ? kgrid : qgrid;
+      uint16_t* grl = which ? klo : qlo;
 #pragma unroll
       for (int c = 0; c < CPL; c++) {
         xb[g * D + lane * CPL + c] = x[c];
-        float qv = mx > 0.0f ? rintf(ldexpf(x[c], -e)) : 0.0f;
-        gr[g * D + lane * CPL + c] = (uint16_t)(__float_as_uint(qv) >> 16);  // exact: |qv| <= 256
+        // two-level grid: x ~ 2^E (hi + 2^-8 lo), hi in [-256, 256],
+        // lo in [-128, 128], both exact in bf16
+        const float y = mx > 0.0f ? ldexpf(x[c], -e) : 0.0f;
+        const float hi = rintf(y);
+        const float lo = rintf(ldexpf(y - hi, 8));
+        gr[g * D + lane * CPL + c] = (uint16_t)(__float_as_uint(hi) >> 16);
+        grl[g * D + lane * CPL + c] = (uint16_t)(__float_as_uint(lo) >> 16);
       }
       if (lane == 0) (which ? kexp : qexp)[g] = e;
     }
@@ -692,63 +698,70 @@ __global__ __launch_bounds__(512) void k_pool(
 }
 
 // ============================================================ K5: block scores
-// s_ij = ldexp(I_ij, Ei + Ej) * fl(1/sqrt D), I_ij = integer dot product of the
-// grid rows, exact in fp32 on the bf16 MFMA (|I| <= 2^23).
-// Block of 256 threads covers 128 x 128 scores; each wave 64 x 64.
+// s_ij = Qbar_i . Kbar_j / sqrt(D) on the two-level grid x ~ 2^E (hi + 2^-8 lo):
+// the integer dot products I_hh = hi.hi, I_x = hi_i.lo_j + lo_i.hi_j and
+// I_ll = lo.lo are exact on the bf16 MFMA (every partial sum is an integer
+// below 2^24), J = 2^16 I_hh + 2^8 I_x + I_ll is formed exactly in int64, and
+// s = fl32(fl32(J) 2^(Ei + Ej - 16)) * fl(1/sqrt D), J rounded once (it is
+// exact in fp64).  A block of 256 threads covers 128 x 128 scores, each wave
+// 64 x 64 as two 32-row halves.
 template <int D>
-__global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict__ qgrid,
-                                                      const uint16_t* __restrict__ kgrid,
-                                                      const int32_t* __restrict__ qexp,
-                                                      const int32_t* __restrict__ kexp,
-                                                      int64_t g0, int n, float cD,
-                                                      float* __restrict__ scores) {
+__global__ __launch_bounds__(256) void k_block_scores(
+    const uint16_t* __restrict__ qgrid, const uint16_t* __restrict__ kgrid,
+    const uint16_t* __restrict__ qlo, const uint16_t* __restrict__ klo,
+    const int32_t* __restrict__ qexp, const int32_t* __restrict__ kexp, int64_t g0, int n,
+    float cD, float* __restrict__ scores) {
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i0 = blockIdx.y * 128 + (wv >> 1) * 64;
   const int j0 = blockIdx.x * 128 + (wv & 1) * 64;
   const int hl = lane >> 5, l32 = lane & 31;
-  f32x16 acc[2][2];
+  auto frag = [&](const uint16_t* base, int row, int kk) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (row < n) u = *(const uint4*)(base + (g0 + row) * D + kk * 16 + hl * 8);
+    return __builtin_bit_cast(bf16x8, u);
+  };
 #pragma unroll
-  for (int a = 0; a < 2; a++)
+  for (int a = 0; a < 2; a++) {
+    f32x16 hh[2], hx[2], ll[2];
 #pragma unroll
     for (int b = 0; b < 2; b++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) acc[a][b][r] = 0.0f;
+      for (int r = 0; r < 16; r++) {
+        hh[b][r] = 0.0f;
+        hx[b][r] = 0.0f;
+        ll[b][r] = 0.0f;
+      }
+    const int ia = i0 + a * 32 + l32;
 #pragma unroll
-  for (int kk = 0; kk < D / 16; kk++) {
-    bf16x8 af[2], bfr[2];
+    for (int kk = 0; kk < D / 16; kk++) {
+      const bf16x8 qh = frag(qgrid, ia, kk), ql = frag(qlo, ia, kk);
 #pragma unroll
-    for (int rb = 0; rb < 2; rb++) {
-      int i = i0 + rb * 32 + l32;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (i < n) u = *(const uint4*)(qgrid + (g0 + i) * D + kk * 16 + hl * 8);
-      af[rb] = __builtin_bit_cast(bf16x8, u);
-      int j = j0 + rb * 32 + l32;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (j < n) w = *(const uint4*)(kgrid + (g0 + j) * D + kk * 16 + hl * 8);
-      bfr[rb] = __builtin_bit_cast(bf16x8, w);
+      for (int b = 0; b < 2; b++) {
+        const int jb = j0 + b * 32 + l32;
+        const bf16x8 kh = frag(kgrid, jb, kk), kl = frag(klo, jb, kk);
+        hh[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kh, hh[b], 0, 0, 0);
+        hx[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kl, hx[b], 0, 0, 0);
+        hx[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kh, hx[b], 0, 0, 0);
+        ll[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kl, ll[b], 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-      for (int b = 0; b < 2; b++)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
-  }
-#pragma unroll
-  for (int a = 0; a < 2; a++)
-#pragma unroll
     for (int b = 0; b < 2; b++) {
-      int j = j0 + b * 32 + l32;
+      const int j = j0 + b * 32 + l32;
       if (j >= n) continue;
-      int ej = kexp[g0 + j];
+      const int ej = kexp[g0 + j];
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        int i = i0 + a * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+        const int i = i0 + a * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
         if (i < n) {
-          float s = ldexpf(acc[a][b][r], qexp[g0 + i] + ej) * cD;
+          const int64_t J = (int64_t)hh[b][r] * 65536 + (int64_t)hx[b][r] * 256 +
+                            (int64_t)ll[b][r];
+          const float s = ldexpf((float)(double)J, qexp[g0 + i] + ej - 16) * cD;
           scores[(int64_t)i * n + j] = (s == 0.0f) ? 0.0f : s;
         }
       }
     }
+  }
 }
 
 // ============================================================ K6: selection
@@ -1659,7 +1672,7 @@ bool launch_pool(const PlanDev& P, const void* q, const void* k, hipStream_t st)
   dim3 grid(P.heads * P.Z), block(512);
 #define PP_ARGS                                                                          \
   q, k, P.H, P.W, P.Z, P.N, P.shape_id, P.zone_base, P.blk_off, P.blk_start, P.blk_org, \
-      P.blk_shape, P.blk_head, P.qbar, P.kbar, P.qgrid, P.kgrid, P.qexp, P.kexp
+      P.blk_shape, P.blk_head, P.qbar, P.kbar, P.qgrid, P.kgrid, P.qlo, P.klo, P.qexp, P.kexp
   if (P.dtype == PRISM_BF16 && P.D == 128)
     hipLaunchKernelGGL((k_pool<1, 2>), grid, block, 0, st, PP_ARGS);
   else if (P.dtype == PRISM_BF16 && P.D == 64)
@@ -1679,11 +1692,11 @@ bool launch_block_scores(const PlanDev& P, int64_t g0, int n, float* out, hipStr
   float cD = (float)(1.0 / sqrt((double)P.D));
   dim3 grid((n + 127) / 128, (n + 127) / 128), block(256);
   if (P.D == 128)
-    hipLaunchKernelGGL((k_block_scores<128>), grid, block, 0, st, P.qgrid, P.kgrid, P.qexp,
-                       P.kexp, g0, n, cD, out);
+    hipLaunchKernelGGL((k_block_scores<128>), grid, block, 0, st, P.qgrid, P.kgrid, P.qlo,
+                       P.klo, P.qexp, P.kexp, g0, n, cD, out);
   else
-    hipLaunchKernelGGL((k_block_scores<64>), grid, block, 0, st, P.qgrid, P.kgrid, P.qexp,
-                       P.kexp, g0, n, cD, out);
+    hipLaunchKernelGGL((k_block_scores<64>), grid, block, 0, st, P.qgrid, P.kgrid, P.qlo,
+                       P.klo, P.qexp, P.kexp, g0, n, cD, out);
   return hipGetLastError() == hipSuccess;
 }
 

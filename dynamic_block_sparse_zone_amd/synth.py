@@ -77,6 +77,9 @@ WORKLOADS = {
                            kind="background", active_frac=0.2, seed=1003, top_k_frac=0.05),
     "train2k_op": Workload("train2k_op", 72, 120, 120, 40, 128, "bf16", top_k=0, top_p=0.2,
                            seed=1004, backward=True, unit_var=True, top_k_frac=0.05),
+    # the same with Top-p 0.3, the contrast of the pages' Table 7
+    "train2k_op3": Workload("train2k_op3", 72, 120, 120, 40, 128, "bf16", top_k=0, top_p=0.3,
+                            seed=1004, backward=True, unit_var=True, top_k_frac=0.05),
     # small bf16 grid for full element-by-element checks (fwd + bwd): several
     # zones of every volume, a ragged number of blocks per head
     "check": Workload("check", 16, 24, 32, 3, 128, "bf16", top_k=3, top_p=0.9, seed=1006,

@@ -248,7 +248,10 @@ prism_status prism_schedule_value(int32_t kind, int64_t step, int64_t steps, flo
 
 /* Block scores of one head (stage 3): out_scores device float32
  * [N_blk(head)][N_blk(head)], s_ij = Qbar_i . Kbar_j / sqrt(head_dim) with
- * both means on the integer grid of prism_plan_export's QGRID/KGRID. */
+ * both means on the two-level integer grid x ~ 2^E (hi + 2^-8 lo) of
+ * prism_plan_export's QGRID/QLO/QEXP and KGRID/KLO/KEXP (about 17
+ * significant bits): the dot product of the grid values is formed exactly
+ * and rounded once to float32 before the 1/sqrt(head_dim) scaling. */
 prism_status prism_block_scores(const prism_plan_t* plan, int32_t head, float* out_scores,
                                 void* stream);
 
@@ -268,7 +271,7 @@ typedef enum {
   PRISM_ARR_COLT_PTR = 11,    /* int64 [G+1]: key-major pointer (need_backward) */
   PRISM_ARR_COLT_IDX = 12,    /* int32 [nnz]: query blocks selecting each key block, ascending */
   PRISM_ARR_PERM = 13,        /* int32 [heads][N]: original token of each permuted row */
-  PRISM_ARR_QGRID = 14,       /* uint16 (bf16 bits) [G][head_dim]: integer grid of Qbar */
+  PRISM_ARR_QGRID = 14,       /* uint16 (bf16 bits) [G][head_dim]: high part of the grid of Qbar */
   PRISM_ARR_KGRID = 15,       /* uint16 (bf16 bits) [G][head_dim] */
   PRISM_ARR_KV_ORDER = 16,    /* int32 [heads][N/128] (need_backward): the dK/dV kernel's work
                                  units (128 permuted key rows) of each head, in the order it
@@ -279,7 +282,10 @@ typedef enum {
   PRISM_ARR_BLK_ORG = 17,     /* int32 [G]: original token (within its head) of each block's
                                  first row: with the block's shape this gives every row's
                                  token in closed form */
-  PRISM_ARR_CUTS = 18         /* uint8 [T] (cut_threshold > 0): 1 where a shot cut starts */
+  PRISM_ARR_CUTS = 18,        /* uint8 [T] (cut_threshold > 0): 1 where a shot cut starts */
+  PRISM_ARR_QLO = 19,         /* uint16 (bf16 bits) [G][head_dim]: low part of the grid of
+                                 Qbar, Qbar ~ 2^QEXP (QGRID + 2^-8 QLO) */
+  PRISM_ARR_KLO = 20          /* uint16 (bf16 bits) [G][head_dim] */
 } prism_array;
 
 /* Size in bytes of a plan array. Host-only. */

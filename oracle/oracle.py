@@ -68,10 +68,11 @@ def lib():
             getattr(_lib, name).restype = ctypes.c_double
             getattr(_lib, name).argtypes = [ctypes.c_double]
         _lib.orc_score_row.argtypes = [
-            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-            ctypes.c_int, ctypes.c_void_p]
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
         _lib.orc_quantize.argtypes = [
-            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p]
     return _lib
 
 
@@ -199,10 +200,12 @@ class Plan:
     perm: np.ndarray              # [heads, N] int32 permuted position -> token
     qbar: np.ndarray              # [G, D] fp32
     kbar: np.ndarray              # [G, D] fp32
-    qgrid: np.ndarray             # [G, D] fp32 (integers)
+    qgrid: np.ndarray             # [G, D] fp32 (integers): the grid's high part
     qexp: np.ndarray              # [G] int32
     kgrid: np.ndarray
     kexp: np.ndarray
+    qlo: np.ndarray               # [G, D] fp32 (integers): the grid's low part
+    klo: np.ndarray
     rows: dict = field(default_factory=dict)   # (head, local block) -> selected local key ids
     cuts: np.ndarray | None = None             # [T] uint8 shot cuts (cut_threshold > 0)
 
@@ -284,11 +287,14 @@ def pool(x: np.ndarray, shape_id, blk_off, cfg: Config) -> np.ndarray:
 
 
 def quantize(xbar: np.ndarray):
+    """Two-level integer grid of pooled rows: (hi [rows, D], E [rows],
+    lo [rows, D]) with x ~ 2^E (hi + 2^-8 lo)."""
     xbar = np.ascontiguousarray(xbar, np.float32)
     q = np.zeros_like(xbar)
+    lo = np.zeros_like(xbar)
     e = np.zeros(xbar.shape[0], np.int32)
-    lib().orc_quantize(_p(xbar), xbar.shape[0], xbar.shape[1], _p(q), _p(e))
-    return q, e
+    lib().orc_quantize(_p(xbar), xbar.shape[0], xbar.shape[1], _p(q), _p(lo), _p(e))
+    return q, e, lo
 
 
 def plan(q, k, v, av_norm, cfg: Config) -> Plan:
@@ -303,9 +309,10 @@ def plan(q, k, v, av_norm, cfg: Config) -> Plan:
     perm = perm_map(sid, cfg)
     qbar = pool(q, sid, off, cfg)
     kbar = pool(k, sid, off, cfg)
-    qg, qe = quantize(qbar)
-    kg, ke = quantize(kbar)
-    pl = Plan(cfg, vs, ast, g, vol, sid, off, start, ln, perm, qbar, kbar, qg, qe, kg, ke)
+    qg, qe, ql = quantize(qbar)
+    kg, ke, kl = quantize(kbar)
+    pl = Plan(cfg, vs, ast, g, vol, sid, off, start, ln, perm, qbar, kbar, qg, qe, kg, ke, ql,
+              kl)
     pl.cuts = cuts
     return pl
 
@@ -315,10 +322,12 @@ def score_row(pl: Plan, h: int, i: int) -> np.ndarray:
     o, n = int(pl.blk_off[h]), pl.nblk(h)
     s = np.zeros(n, np.float32)
     qrow = np.ascontiguousarray(pl.qgrid[o + i])
+    qlo = np.ascontiguousarray(pl.qlo[o + i])
     kg = np.ascontiguousarray(pl.kgrid[o:o + n])
+    kl = np.ascontiguousarray(pl.klo[o:o + n])
     ke = np.ascontiguousarray(pl.kexp[o:o + n])
-    lib().orc_score_row(_p(qrow), int(pl.qexp[o + i]), _p(kg), _p(ke), n, pl.cfg.head_dim,
-                        _p(s))
+    lib().orc_score_row(_p(qrow), _p(qlo), int(pl.qexp[o + i]), _p(kg), _p(kl), _p(ke), n,
+                        pl.cfg.head_dim, _p(s))
     return s
 
 

@@ -683,10 +683,15 @@ int orc_pool(const void* x, int dtype, int T, int H, int W, int heads, int D,
 /* stage 3b: block scores on an exact integer grid, then Top-k U Top-p   */
 /* ------------------------------------------------------------------ */
 
-/* Each pooled row x is written as 2^E * q with integer q_c = rint(x_c 2^-E),
- * E chosen so that max_c |x_c| 2^-E lies in [128, 256).  A zero row has
- * E = 0, q = 0. */
-int orc_quantize(const float* xbar, int64_t rows, int D, float* qgrid, int32_t* E) {
+/* Each pooled row x is written on a two-level integer grid,
+ *   x_c ~ 2^E (hi_c + 2^-8 lo_c),
+ * E chosen so that max_c |x_c| 2^-E lies in [128, 256):
+ *   hi_c = rint(x_c 2^-E)            in [-256, 256]
+ *   lo_c = rint((x_c 2^-E - hi_c) 2^8) in [-128, 128]
+ * (the subtraction is exact), so x is seen to about 17 significant bits and
+ * every product of grid values is an integer the matrix cores sum exactly.
+ * A zero row has E = 0, hi = lo = 0. */
+int orc_quantize(const float* xbar, int64_t rows, int D, float* qgrid, float* qlo, int32_t* E) {
   for (int64_t i = 0; i < rows; i++) {
     const float* x = xbar + i * D;
     float mx = 0.0f;
@@ -698,20 +703,36 @@ int orc_quantize(const float* xbar, int64_t rows, int D, float* qgrid, int32_t* 
       e -= 8;
     }
     E[i] = e;
-    for (int c = 0; c < D; c++) qgrid[i * D + c] = mx > 0.0f ? rintf(ldexpf(x[c], -e)) : 0.0f;
+    for (int c = 0; c < D; c++) {
+      float y = mx > 0.0f ? ldexpf(x[c], -e) : 0.0f;
+      float hi = rintf(y);
+      qgrid[i * D + c] = hi;
+      if (qlo) qlo[i * D + c] = rintf(ldexpf(y - hi, 8));
+    }
   }
   return OR_OK;
 }
 
 /* scores s_ij = Qbar_i . Kbar_j / sqrt(D) of query row i against the n key
- * rows: the integer dot product is exact; s = ldexp(I, Ei + Ej) * fl(1/sqrt D). */
-int orc_score_row(const float* qrow, int32_t Ei, const float* kgrid, const int32_t* Ek,
-                  int64_t n, int D, float* s) {
+ * rows on the two-level grid: with the integer dot products I_hh = hi.hi,
+ * I_x = hi_i.lo_j + lo_i.hi_j and I_ll = lo.lo,
+ *   J = 2^16 I_hh + 2^8 I_x + I_ll   (exact, |J| < 2^41)
+ * and s = fl32(fl32(J) 2^(Ei + Ej - 16)) * fl32(1/sqrt D), fl32(J) rounded
+ * once to nearest (J is exact in fp64). */
+int orc_score_row(const float* qrow, const float* qlo, int32_t Ei, const float* kgrid,
+                  const float* klo, const int32_t* Ek, int64_t n, int D, float* s) {
   float cD = (float)(1.0 / sqrt((double)D));
   for (int64_t j = 0; j < n; j++) {
-    int64_t I = 0;
-    for (int c = 0; c < D; c++) I += (int64_t)qrow[c] * (int64_t)kgrid[j * D + c];
-    float v = ldexpf((float)I, Ei + Ek[j]) * cD;
+    int64_t Ihh = 0, Ix = 0, Ill = 0;
+    for (int c = 0; c < D; c++) {
+      int64_t qh = (int64_t)qrow[c], ql = (int64_t)qlo[c];
+      int64_t kh = (int64_t)kgrid[j * D + c], kl = (int64_t)klo[j * D + c];
+      Ihh += qh * kh;
+      Ix += qh * kl + ql * kh;
+      Ill += ql * kl;
+    }
+    int64_t J = Ihh * 65536 + Ix * 256 + Ill;
+    float v = ldexpf((float)(double)J, Ei + Ek[j] - 16) * cD;
     s[j] = (v == 0.0f) ? 0.0f : v;
   }
   return OR_OK;

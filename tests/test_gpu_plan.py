@@ -57,6 +57,8 @@ def _check_plan_arrays(pl, opl, cfg):
     to_f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
     np.testing.assert_array_equal(to_f(qg), opl.qgrid)
     np.testing.assert_array_equal(to_f(kg), opl.kgrid)
+    np.testing.assert_array_equal(to_f(pl.export("qlo").reshape(G, D)), opl.qlo)
+    np.testing.assert_array_equal(to_f(pl.export("klo").reshape(G, D)), opl.klo)
 
 
 def _check_csr(pl, opl, orc, rows_per_head=None, seed=0):

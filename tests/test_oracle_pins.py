@@ -309,36 +309,48 @@ def test_pooling_is_block_mean(orc):
 
 
 def test_integer_grid_quantisation(orc):
+    """The two-level grid: integers hi in [-256, 256] and lo in [-128, 128]
+    with |x - 2^E (hi + 2^-8 lo)| <= 2^(E - 9), and hi alone within
+    2^(E - 1)."""
     rng = np.random.default_rng(10)
     x = (rng.normal(size=(50, 128)) * np.exp(rng.uniform(-8, 3, (50, 1)))).astype(np.float32)
     x[3] = 0
-    q, e = orc.quantize(x)
+    q, e, lo = orc.quantize(x)
     assert np.all(q == np.round(q)) and np.abs(q).max() <= 256
+    assert np.all(lo == np.round(lo)) and np.abs(lo).max() <= 128
     for i in range(50):
         if i == 3:
-            assert e[i] == 0 and np.all(q[i] == 0)
+            assert e[i] == 0 and np.all(q[i] == 0) and np.all(lo[i] == 0)
             continue
         assert 128 <= np.abs(q[i]).max() <= 256
-        err = np.abs(x[i].astype(np.float64) - q[i] * 2.0 ** e[i])
-        assert err.max() <= 2.0 ** (e[i] - 1)
+        xi = x[i].astype(np.float64)
+        assert np.abs(xi - q[i] * 2.0 ** e[i]).max() <= 2.0 ** (e[i] - 1)
+        assert np.abs(xi - (q[i] + lo[i] / 256.0) * 2.0 ** e[i]).max() <= 2.0 ** (e[i] - 9)
 
 
 def test_block_scores(orc):
     """s_ij = Qbar_i . Kbar_j / sqrt(D) (paper.rainbus.top stage three), on
-    the integer grid: within the grid's rounding of the fp64 product."""
+    the two-level grid: within the grid's rounding of the fp64 product of
+    the means, and equal (to one fp32 rounding) to the exact product of the
+    grid values, which the oracle forms as an integer."""
     rng = np.random.default_rng(11)
     D = 128
     qb = rng.normal(size=(1, D)).astype(np.float32)
-    kb = rng.normal(size=(40, D)).astype(np.float32)
-    qg, qe = orc.quantize(qb)
-    kg, ke = orc.quantize(kb)
+    kb = (rng.normal(size=(40, D)) * np.exp(rng.uniform(-4, 2, (40, 1)))).astype(np.float32)
+    qg, qe, ql = orc.quantize(qb)
+    kg, ke, kl = orc.quantize(kb)
     from oracle.oracle import _p, lib
     s = np.zeros(40, np.float32)
-    lib().orc_score_row(_p(np.ascontiguousarray(qg[0])), int(qe[0]), _p(kg), _p(ke), 40, D, _p(s))
+    lib().orc_score_row(_p(np.ascontiguousarray(qg[0])), _p(np.ascontiguousarray(ql[0])),
+                        int(qe[0]), _p(kg), _p(kl), _p(ke), 40, D, _p(s))
     ref = (kb.astype(np.float64) @ qb[0].astype(np.float64)) / math.sqrt(D)
-    bound = (np.abs(qb).max() * 2.0 ** -8 * np.abs(kb).sum(1) +
-             np.abs(kb).max(1) * 2.0 ** -8 * np.abs(qb).sum()) / math.sqrt(D)
-    assert np.all(np.abs(s - ref) <= bound * 1.01 + 1e-6)
+    bound = (np.abs(qb).max() * 2.0 ** -16 * np.abs(kb).sum(1) +
+             np.abs(kb).max(1) * 2.0 ** -16 * np.abs(qb).sum()) / math.sqrt(D)
+    assert np.all(np.abs(s - ref) <= bound * 1.01 + np.abs(ref) * 2.0 ** -22)
+    hq = qg[0].astype(np.float64) + ql[0] / 256.0
+    hk = kg.astype(np.float64) + kl / 256.0
+    exact = (hk @ hq) * 2.0 ** (qe[0] + ke.astype(np.float64)) / math.sqrt(D)
+    np.testing.assert_allclose(s, exact, rtol=2.0 ** -22)
 
 
 # ----------------------------------------------------------- selection
