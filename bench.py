@@ -204,14 +204,17 @@ def summarize_pmc(fetch_csv, write_csv, stage, workload, cmds, out):
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        kern = [float(r["Counter_Value"]) * 1024 for r in rows if sym in r["Kernel_Name"]]
+        # the launch of the workload is the kernel's longest dispatch (the
+        # run also warms every kernel up on a small grid first)
+        kern = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                 float(r["Counter_Value"]) * 1024) for r in rows if sym in r["Kernel_Name"]]
         # the calibration copy is the run's only bitwise-not kernel
         copies = [float(r["Counter_Value"]) * 1024 for r in rows
                   if "bitwise_not" in r["Kernel_Name"]]
         if not kern or len(copies) != 1:
             raise SystemExit(f"{path}: {len(kern)} {sym} and {len(copies)} copy dispatches "
                              f"with {counter}")
-        return sum(kern) / len(kern), copies[0]
+        return max(kern)[1], copies[0]
 
     fk, fc = per_kernel(fetch_csv, "FETCH_SIZE")
     wk, wc = per_kernel(write_csv, "WRITE_SIZE")
@@ -222,7 +225,9 @@ def summarize_pmc(fetch_csv, write_csv, stage, workload, cmds, out):
         "",
         "Two `rocprofv3 --pmc` passes over one profiled step that ends with a plain",
         f"copy of {CALIB_BYTES >> 20} MiB (read and write); each counter is scaled by "
-        "the factor that makes it read the copy's known size.",
+        "the factor that makes it read the copy's known size.  The figures are those of",
+        "the kernel's longest dispatch, the full-size launch (the run first warms every",
+        "kernel up on a small grid).",
         "",
         "Commands (from /tmp, TMPDIR=/tmp):",
         "",
