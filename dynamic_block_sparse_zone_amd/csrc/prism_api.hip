@@ -131,6 +131,8 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
   P->qexp = A.take<int32_t>(G);
   P->kexp = A.take<int32_t>(G);
   P->scores = A.take<float>(maxblk * maxblk);
+  P->selmask = A.take<unsigned long long>(maxblk * ((maxblk + 63) / 64));
+  P->volm = A.take<unsigned long long>(3 * ((maxblk + 63) / 64));
   P->row_cnt = A.take<int32_t>(G);
   P->row_key = A.take<uint32_t>(G);
   P->row_tie = A.take<int32_t>(G);
@@ -143,6 +145,7 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
     P->colt_ptr = A.take<int64_t>(G + 1);
     P->colt_cnt = A.take<int32_t>(G);
     P->chunk_cnt = A.take<int32_t>((maxblk / 64 + 1) * maxblk);
+    P->chunk_cost = A.take<int32_t>((maxblk / 64 + 1) * maxblk);
     P->korder = A.take<int32_t>((int64_t)c.heads * (N / 128));
     P->colt_cost = A.take<int64_t>(G);
     P->sync = A.take<int32_t>(128);
@@ -150,6 +153,7 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
     P->colt_ptr = nullptr;
     P->colt_cnt = nullptr;
     P->chunk_cnt = nullptr;
+    P->chunk_cost = nullptr;
     P->korder = nullptr;
     P->colt_cost = nullptr;
     P->sync = nullptr;
@@ -283,6 +287,13 @@ prism_status prism_plan_create(const prism_config* c, const void* q, const void*
     stage_begin("plan.select", st);
     ok = ok && launch_select(P, off[h], n, *c, h == c->heads - 1, st);
     stage_end(st);
+    // the key-major lists of the head, from its selection mask (writes past
+    // the capacity are dropped; the plan then fails below)
+    if (c->need_backward) {
+      stage_begin("plan.transpose", st);
+      ok = ok && launch_transpose(P, off[h], n, h == c->heads - 1, st);
+      stage_end(st);
+    }
   }
   if (!ok) return PRISM_EDEVICE;
   int64_t nnz = 0;
@@ -291,17 +302,8 @@ prism_status prism_plan_create(const prism_config* c, const void* q, const void*
   if (nnz_out) *nnz_out = nnz;
   if (nnz > cap) return PRISM_ENOMEM_WORKSPACE;
   if (c->need_backward) {
-    stage_begin("plan.transpose", st);
-    for (int h = 0; h < c->heads && ok; h++) {
-      int n = (int)(off[h + 1] - off[h]);
-      ok = launch_transpose(P, off[h], n, h == c->heads - 1, st);
-    }
-    stage_end(st);
-    if (!ok) return PRISM_EDEVICE;
-  }
-  if (c->need_backward) {
     stage_begin("plan.order", st);
-    ok = launch_unit_order_k(P, off, st);
+    ok = launch_unit_order_k(P, st);
     stage_end(st);
     if (!ok) return PRISM_EDEVICE;
   }

@@ -165,7 +165,10 @@ struct PlanDev {
   int64_t* colt_ptr;   // [Gmax+1]
   int32_t* colt_idx;   // [cap]
   int32_t* colt_cnt;   // [Gmax] scratch
-  int32_t* chunk_cnt;  // [(maxblk/64+1) * maxblk] scratch
+  int32_t* chunk_cnt;  // [(maxblk/64+1) * maxblk] scratch: per (row tile, column) counts
+  int32_t* chunk_cost; // [(maxblk/64+1) * maxblk] scratch: per (row tile, column) volumes
+  unsigned long long* selmask;  // [maxblk][maxblk/64] one head's selection, a bit per pair
+  unsigned long long* volm;     // [3][maxblk/64] one head's blocks by volume class
   int64_t* row_cost;   // [Gmax] B_i * sum_{j in S_i} B_j
   int64_t* counters;   // [8]: [0] nnz running total
   int64_t cap;

@@ -20,7 +20,7 @@ bool launch_transpose(const PlanDev& P, int64_t g0, int n, int last, hipStream_t
 bool launch_perm_map(const PlanDev& P, int32_t* out, hipStream_t st);
 bool launch_sum_i64(const int64_t* in, int64_t n, int64_t* out, hipStream_t st);
 // the dK/dV work-unit order (after the transpose)
-bool launch_unit_order_k(const PlanDev& P, const std::vector<int64_t>& off, hipStream_t st);
+bool launch_unit_order_k(const PlanDev& P, hipStream_t st);
 
 bool launch_attn_fwd(const PlanDev& P, const void* q, const void* k, const void* v, void* o,
                      float* lse, hipStream_t st);

@@ -793,19 +793,29 @@ __device__ inline float exp2_taylor(float x) {
   return ldexpf(p, (int)kf);
 }
 
+// The same value without a branch (the series is evaluated for every x and
+// the result replaced by 0 below the cut-off), for unrolled loops.
+__device__ inline float exp2_taylor_sel(float x) {
+  const float kf = rintf(x);
+  const float f = x - kf;
+  float p = 0.000015252733804059840280f;
+  p = __builtin_fmaf(p, f, 0.00015403530393381609954f);
+  p = __builtin_fmaf(p, f, 0.0013333558146428443423f);
+  p = __builtin_fmaf(p, f, 0.0096181291076284771620f);
+  p = __builtin_fmaf(p, f, 0.055504108664821579953f);
+  p = __builtin_fmaf(p, f, 0.24022650695910071233f);
+  p = __builtin_fmaf(p, f, 0.69314718055994530942f);
+  p = __builtin_fmaf(p, f, 1.0f);
+  const float r = ldexpf(p, x > -100.0f ? (int)kf : 0);
+  return x > -100.0f ? r : 0.0f;
+}
+
 // softmax weight of a score in 2^-32 units relative to the row maximum
 __device__ inline uint64_t weight_of(float s, float smax) {
   const float LOG2E = 1.44269504088896340736f;
   float x = (s - smax) * LOG2E;
   float y = exp2_taylor(x);
   return (uint64_t)(y * 4294967296.0f);
-}
-
-__device__ inline int bucket_of(float s, float smax) {
-  const float LOG2E = 1.44269504088896340736f;
-  float x = (s - smax) * LOG2E;  // same rounding as weight_of: monotone in s
-  float b = -x * 8.0f;
-  return b >= 255.0f ? 255 : (int)b;
 }
 
 template <typename T>
@@ -822,27 +832,9 @@ __device__ inline T block_sum(T v, T* sh) {
 }
 
 constexpr int kSelThreads = 256;
-// longest score row (key blocks of a head) the selection kernels stage in LDS
-constexpr int kSelLdsMax = 16384;
-// floats of LDS a staged row takes (rounded up to whole 64-lane pieces)
-__host__ __device__ inline int sel_row_floats(int n) { return (n + 63) / 64 * 64; }
 // block volume of a shape id (ids are ordered by volume: 0..6 are 64,
 // 7..12 are 128, 13..15 are 256)
 __device__ inline int volume_of_id(int sid) { return sid < 7 ? 64 : sid < 13 ? 128 : 256; }
-
-// One score row (n <= kSelLdsMax floats) into LDS: every wave issues its
-// 256-byte pieces as direct HBM->LDS loads, all in flight at once, then one
-// wait and a barrier.  Lanes past n read zeros (range-checked buffer) into
-// the unused tail of `dst`.
-__device__ inline void stage_row(const float* row, int n, float* dst) {
-  const __amdgpu_buffer_rsrc_t rs = buffer_of(row, (uint32_t)n * 4u);
-  const uint32_t o = lds_offset(dst);
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  for (int j0 = wv * 64; j0 < n; j0 += kSelThreads)
-    dma4(rs, (uint32_t)(j0 + lane) * 4u, o + (uint32_t)j0 * 4u);
-  __builtin_amdgcn_s_waitcnt(wait_vm(0));
-  __syncthreads();
-}
 
 // Shared state of the row selection: per-wave digit histograms (count and
 // integer weight) of one radix level, and the scan scratch.
@@ -873,30 +865,9 @@ __device__ inline unsigned long long block_incl_scan(unsigned long long v,
   return before + v;
 }
 
-// Sources of a row's scores for the selection passes: src.each(f) calls f
-// on every score of this thread's share of the row (elements tid + 256 e).
-// LdsRow reads a row staged in LDS eight elements at a time, all eight reads
-// in flight before any is used (one at a time, every element paid the LDS
-// latency); GlobalRow reads a row of any length from HBM on every pass.
-struct LdsRow {
-  const float* row;
-  int n;
-  template <class F>
-  __device__ void each(F f) const {
-    constexpr int kBatch = 8;
-    for (int j0 = threadIdx.x; j0 < n; j0 += kBatch * kSelThreads) {
-      float v[kBatch];
-#pragma unroll
-      for (int k = 0; k < kBatch; k++) {
-        const int j = j0 + k * kSelThreads;
-        v[k] = row[j < n ? j : j0];
-      }
-#pragma unroll
-      for (int k = 0; k < kBatch; k++)
-        if (j0 + k * kSelThreads < n) f(v[k]);
-    }
-  }
-};
+// The row's scores for the radix select below: src.each(f) calls f on every
+// score of this thread's share of the row (elements tid + 256 e), read from
+// HBM on every pass.
 struct GlobalRow {
   const float* row;
   int n;
@@ -913,7 +884,7 @@ struct GlobalRow {
 // down and returns the digit at which the running total (weight, else
 // count) first reaches `need`; *above_c / *above_w get the count and weight
 // of the candidates with a larger digit.  The row is visited through `src`
-// (LdsRow or GlobalRow).
+// (a GlobalRow).
 template <class Src, class Cls>
 __device__ int select_level(const Src& src, Cls cls, float smax, bool by_weight,
                             unsigned long long need, SelShared& S, uint32_t* above_c,
@@ -1060,7 +1031,6 @@ __device__ uint32_t exact_select(const Src& src, float smax, float smin, bool by
 // positions are found exactly by radix selects over the order keys (equal
 // keys carry equal weights, so a prefix of the order is "every key above K
 // and the first t copies of K").
-template <bool kLds>
 __global__ __launch_bounds__(kSelThreads) void k_select_count(
     const float* __restrict__ scores, int n, int64_t g0, int k_count, float k_frac, float p,
     int32_t* __restrict__ row_cnt, uint32_t* __restrict__ row_key,
@@ -1080,13 +1050,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_count(
     }
     return;
   }
-  // the row is read from HBM once: into LDS (n floats of dynamic shared
-  // memory) when it fits, and every later pass runs over that copy; longer
-  // rows are read from HBM on every pass
   const float* grow = scores + (int64_t)i * n;
-  extern __shared__ __attribute__((aligned(16))) float srow_dyn[];
-  if (kLds) stage_row(grow, n, srow_dyn);
-  const LdsRow rr{srow_dyn, n};
   const GlobalRow gr{grow, n};
   // the row's maximum and minimum
   float mx = -INFINITY, mn = INFINITY;
@@ -1094,10 +1058,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_count(
     mx = fmaxf(mx, s);
     mn = fminf(mn, s);
   };
-  if (kLds)
-    rr.each(minmax);
-  else
-    gr.each(minmax);
+  gr.each(minmax);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     mx = fmaxf(mx, __shfl_xor(mx, off, 64));
@@ -1117,8 +1078,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_count(
   auto select = [&](bool by_weight, unsigned long long need, uint32_t* ac,
                     unsigned long long* aw, unsigned long long p32,
                     unsigned long long* need_out) {
-    return kLds ? exact_select(rr, smax, smin, by_weight, need, S, ac, aw, p32, need_out)
-                : exact_select(gr, smax, smin, by_weight, need, S, ac, aw, p32, need_out);
+    return exact_select(gr, smax, smin, by_weight, need, S, ac, aw, p32, need_out);
   };
 
   int64_t L = 0;
@@ -1205,202 +1165,519 @@ __device__ inline int block_excl_scan_i32(int v, int* sh, int* total) {
   return before + x - v;
 }
 
-// Writes the selected key blocks of each row in ascending order, given the
-// threshold key K and the number of K-ties to take.  Thread t takes the
-// contiguous segment [tC, tC + C) of the row (C <= 64, in registers): one
-// prefix over the ties and one over the selected counts place every thread's
-// output.  With the row staged in LDS, the output is compacted into that
-// same buffer and stored contiguously.
-template <bool kLds>
+// Writes the selected key blocks of each row (rows longer than the register
+// path holds) in ascending order, given the threshold key K and the number
+// of K-ties to take, with the row's attention cost B_i * sum_j B_j.  Thread
+// t takes the contiguous segment [tC, tC + C) of the row: one prefix over
+// the ties and one over the selected counts place every thread's output.
 __global__ __launch_bounds__(kSelThreads) void k_select_fill(
     const float* __restrict__ scores, int n, int64_t g0, const int32_t* __restrict__ row_cnt,
     const uint32_t* __restrict__ row_key, const int32_t* __restrict__ row_tie,
     const int64_t* __restrict__ row_ptr, int64_t cap, const uint8_t* __restrict__ blk_shape,
     int32_t* __restrict__ col_idx, int64_t* __restrict__ row_cost) {
-  extern __shared__ __attribute__((aligned(16))) float srow_dyn[];
   __shared__ int sh[kSelThreads / 64];
   __shared__ int64_t sh_cost[kSelThreads / 64];
   const int i = blockIdx.x;
   const int64_t g = g0 + i;
-  const float* grow = scores + (int64_t)i * n;
-  // the head's shape ids (key blocks g0 .. g0 + n - 1) follow the row in
-  // LDS: the aligned words that cover them, moved in the same wait
-  const uint8_t* sshape = nullptr;
-  if (kLds) {
-    const int64_t w0 = g0 >> 2;
-    const int nw = (int)(((g0 + n + 3) >> 2) - w0);
-    uint32_t* dst = (uint32_t*)(srow_dyn + sel_row_floats(n));
-    const __amdgpu_buffer_rsrc_t rs = buffer_of(blk_shape + w0 * 4, (uint32_t)nw * 4u);
-    const uint32_t o = lds_offset(dst);
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    for (int j0 = wv * 64; j0 < nw; j0 += kSelThreads)
-      dma4(rs, (uint32_t)(j0 + lane) * 4u, o + (uint32_t)j0 * 4u);
-    sshape = (const uint8_t*)dst + (g0 & 3);
-    stage_row(grow, n, srow_dyn);
-  }
-  const float* row = kLds ? (const float*)srow_dyn : grow;
+  const float* row = scores + (int64_t)i * n;
   const uint32_t K = row_key[g];
   const int tie = row_tie[g];
   const int64_t base = row_ptr[g];
   const bool fits = base + row_cnt[g] <= cap;
-  const int C = (n + kSelThreads - 1) / kSelThreads;  // <= 64 on the LDS path
+  const int C = (n + kSelThreads - 1) / kSelThreads;
   const int j0 = min(n, (int)threadIdx.x * C), j1 = min(n, j0 + C);
   int total = 0;
   int64_t cost = 0;
-  if (kLds) {
-    uint32_t key[kSelLdsMax / kSelThreads];
-    int ties = 0;
-#pragma unroll
-    for (int e = 0; e < kSelLdsMax / kSelThreads; e++) {
-      key[e] = j0 + e < j1 ? f2key(row[j0 + e]) : 0u;
-      ties += (j0 + e < j1 && key[e] == K) ? 1 : 0;
+  int ties = 0;
+  for (int j = j0; j < j1; j++) ties += f2key(row[j]) == K;
+  int unused;
+  const int tie0 = block_excl_scan_i32(ties, sh, &unused);
+  int nsel = 0;
+  for (int j = j0, t = tie0; j < j1; j++) {
+    const uint32_t key = f2key(row[j]);
+    const bool sel = key > K || (key == K && t < tie);
+    t += key == K;
+    if (sel) {
+      nsel++;
+      cost += volume_of_id(block_shape_at(blk_shape, g0 + j));
     }
-    int unused;
-    const int tie0 = block_excl_scan_i32(ties, sh, &unused);
-    int nsel = 0;
-    uint64_t selm = 0;  // bit e: element j0 + e selected
-#pragma unroll
-    for (int e = 0, t = tie0; e < kSelLdsMax / kSelThreads; e++) {
-      const bool in = j0 + e < j1;
-      const bool sel = in && (key[e] > K || (key[e] == K && t < tie));
-      t += (in && key[e] == K) ? 1 : 0;
-      if (sel) {
-        nsel++;
-        selm |= 1ull << e;
-        cost += volume_of_id(sshape[j0 + e]);
-      }
-    }
-    int pos = block_excl_scan_i32(nsel, sh, &total);
-    // every thread holds its keys in registers: the row buffer takes the output
-    int32_t* sout = (int32_t*)srow_dyn;
-    while (selm) {
-      const int e = __builtin_ctzll(selm);
-      selm &= selm - 1;
-      sout[pos++] = j0 + e;
-    }
-    __syncthreads();
-    if (fits)
-      for (int e = threadIdx.x; e < total; e += blockDim.x) col_idx[base + e] = sout[e];
-  } else {
-    int ties = 0;
-    for (int j = j0; j < j1; j++) ties += f2key(row[j]) == K;
-    int unused;
-    const int tie0 = block_excl_scan_i32(ties, sh, &unused);
-    int nsel = 0;
-    for (int j = j0, t = tie0; j < j1; j++) {
-      const uint32_t key = f2key(row[j]);
-      const bool sel = key > K || (key == K && t < tie);
-      t += key == K;
-      if (sel) {
-        nsel++;
-        cost += volume_of_id(block_shape_at(blk_shape, g0 + j));
-      }
-    }
-    int pos = block_excl_scan_i32(nsel, sh, &total);
-    for (int j = j0, t = tie0; j < j1; j++) {
-      const uint32_t key = f2key(row[j]);
-      const bool sel = key > K || (key == K && t < tie);
-      t += key == K;
-      if (sel && fits) col_idx[base + pos] = j;
-      pos += sel;
-    }
+  }
+  int pos = block_excl_scan_i32(nsel, sh, &total);
+  for (int j = j0, t = tie0; j < j1; j++) {
+    const uint32_t key = f2key(row[j]);
+    const bool sel = key > K || (key == K && t < tie);
+    t += key == K;
+    if (sel && fits) col_idx[base + pos] = j;
+    pos += sel;
   }
   const int64_t c = block_sum<int64_t>(cost, sh_cost);
   if (threadIdx.x == 0) row_cost[g] = c * (int64_t)d_shapes[block_shape_at(blk_shape, g)].volume;
 }
 
-// Key-major transpose of one head's lists, by tiles of 64 query rows x 256
-// key columns.  A work-group takes 64 rows and a part of kTrPart columns:
-// each row's start in that part is found by one binary search, then every
-// 256-column tile is built as one 64-bit row mask per column (one wave per
-// row walks the row's sorted list with coalesced reads; LDS atomic ORs set
-// the bits).  The counting pass stores popcounts per (row tile, column); the
-// fill pass rebuilds the masks and writes each column's rows in ascending
-// order at its offset, one column per store instruction of a wave.  No global atomics, and the result does not depend on
-// the order of the ORs.
-constexpr int kTrRows = 64;
-constexpr int kTrCols = 256;
-constexpr int kTrPart = 2048;
+// ---- rows of up to kSelRegMax blocks: the selection from registers
+// A work-group of kSelMT threads takes one row; thread t holds the elements
+// t + kSelMT e (e < kSelPer) as order keys relative to the row's smallest
+// key (a score is recovered exactly from its key, so the integer softmax
+// weight is formed from it where needed, as weight_of forms it).  Slots past the
+// row's end hold copies of its last element (so no per-element test is
+// needed): they leave the row's extremes alone, every histogram takes their
+// count and weight off the digit of that element, and the mask drops their
+// bits; in index order they come after every real element.  The selects take 11-bit digits from the top of the row's key range; a level's
+// histogram packs count << 47 | integer weight per digit into one u64 (a row
+// of at most 16384 blocks has fewer than 2^15 elements and a weight total
+// below 2^47, so both fields stay exact): one LDS atomic per candidate.  The
+// threshold key and tie count are those of the radix select over the row
+// above; the row's selection leaves as a bit mask (word w: blocks
+// 64 w .. 64 w + 63, bit b: block 64 w + b).
+constexpr int kSelRegMax = 16384;
+constexpr int kSelMT = 512;                      // threads per row
+constexpr int kSelMW = kSelMT / 64;              // waves per row
+constexpr int kSelPer = kSelRegMax / kSelMT;     // elements per thread
+constexpr int kSelBits = 11;
+constexpr int kSelBins = 1 << kSelBits;
+constexpr int kSelQ = kSelBins / kSelMT;         // digits per thread in the scan
+constexpr int kCntShift = 47;
+constexpr unsigned long long kWtMask = (1ull << kCntShift) - 1ull;
 
-template <bool kFill>
-__global__ __launch_bounds__(kTrCols) void k_colt_tiles(
-    const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int n, int64_t g0,
-    const int64_t* __restrict__ colt_ptr, int32_t* __restrict__ tile_cnt,
-    int32_t* __restrict__ colt_idx) {
-  __shared__ int64_t cur[kTrRows], fin[kTrRows];
-  __shared__ unsigned long long mask[kTrCols];
-  __shared__ int64_t cpos[kTrCols];
-  const int rt = blockIdx.x;
-  const int i0 = rt * kTrRows, nrows = min(kTrRows, n - i0);
-  const int c0 = blockIdx.y * kTrPart, c1 = min(n, c0 + kTrPart);
+struct SelSharedR {
+  unsigned long long hist[kSelBins];
+  unsigned long long wsum[kSelMW];
+  unsigned long long above, wstar;
+  int pick;
+  uint32_t kmin[kSelMW], kmax[kSelMW];
+  int isum[kSelMW];
+  int trank[kSelPer * kSelMW];
+};
+
+// exclusive scan over a kSelMT-thread block of one value per thread, and the
+// block total
+template <typename T>
+__device__ inline T row_excl_scan(T v, T* sh, T* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  if (threadIdx.x < kTrRows && (int)threadIdx.x < nrows) {
-    // first entry of the row at or after column c0
-    const int r = threadIdx.x;
-    int64_t lo = row_ptr[g0 + i0 + r], hi = row_ptr[g0 + i0 + r + 1];
-    fin[r] = hi;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (col_idx[mid] < c0)
-        lo = mid + 1;
-      else
-        hi = mid;
-    }
-    cur[r] = lo;
+  T x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T u = __shfl_up(x, off, 64);
+    if (lane >= off) x += u;
+  }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  T before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelMW; w++) {
+    before += w < wv ? sh[w] : (T)0;
+    tot += sh[w];
   }
   __syncthreads();
-  for (int t0 = c0; t0 < c1; t0 += kTrCols) {
-    const int t1 = min(c1, t0 + kTrCols);
-    mask[threadIdx.x] = 0ull;
+  *total = tot;
+  return before + x - v;
+}
+
+// Per query block row (n <= kSelRegMax): the same count, threshold key and
+// tie count as k_select_count, and the row's selection mask (wd words).
+__global__ __launch_bounds__(kSelMT) void k_select_mask(
+    const float* __restrict__ scores, int n, int64_t g0, int k_count, float k_frac, float p,
+    int32_t* __restrict__ row_cnt, uint32_t* __restrict__ row_key,
+    int32_t* __restrict__ row_tie, unsigned long long* __restrict__ mask, int wd) {
+  __shared__ SelSharedR S;
+  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t g = g0 + i;
+  int64_t kk = k_count;
+  if (k_frac > 0.0f) kk = (int64_t)ceil((double)k_frac * (double)n);
+  if (kk > n) kk = n;
+  if (kk < 0) kk = 0;
+  // the row, 2 KB per slab (coalesced), as order keys; slots past its end
+  // copy element n - 1
+  const float* grow = scores + (int64_t)i * n;
+  const int npad = kSelRegMax - n;  // copies of the last element
+  uint32_t rel[kSelPer];
+#pragma unroll
+  for (int e = 0; e < kSelPer; e++) rel[e] = f2key(grow[min(tid + e * kSelMT, n - 1)]);
+  // the row's smallest and largest order keys
+  uint32_t kmn = rel[0], kmx = rel[0];
+#pragma unroll
+  for (int e = 1; e < kSelPer; e++) {
+    kmn = min(kmn, rel[e]);
+    kmx = max(kmx, rel[e]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, off, 64));
+    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, off, 64));
+  }
+  if (lane == 0) {
+    S.kmin[wv] = kmn;
+    S.kmax[wv] = kmx;
+  }
+  __syncthreads();
+  uint32_t kmin = S.kmin[0], kmax = S.kmax[0];
+#pragma unroll
+  for (int w = 1; w < kSelMW; w++) {
+    kmin = min(kmin, S.kmin[w]);
+    kmax = max(kmax, S.kmax[w]);
+  }
+  const float smax = key2f(kmax);
+  const uint32_t span = kmax - kmin;
+#pragma unroll
+  for (int e = 0; e < kSelPer; e++) rel[e] -= kmin;
+  const uint32_t rlast = f2key(grow[n - 1]) - kmin;
+  // integer softmax weight of the element of relative key r (its score is
+  // recovered exactly from the key): weight_of's value.  (kbase is kmin
+  // through an opaque copy, so that the absolute keys are re-formed here
+  // rather than kept alive beside the relative ones.)
+  uint32_t kbase = __builtin_amdgcn_readfirstlane(kmin);
+  asm volatile("" : "+s"(kbase));
+  auto wt = [&](uint32_t r) -> unsigned long long {
+    const float s = key2f(r + kbase);
+    return (unsigned long long)(exp2_taylor_sel((s - smax) * 1.44269504088896340736f) *
+                                4294967296.0f);
+  };
+
+  // one level: histogram of the digits (rel >> lo) & dmask of the
+  // candidates (the bits of rel from hi up equal those of `pre`), then the digit, from the top, at which
+  // the running total (weight, else count) first reaches `need` (digit 0
+  // if none does), with the packed totals of the larger digits.  With p32
+  // the target is the Top-p weight W*, formed from the level's total.
+  auto level = [&](int hi, int lo, uint32_t pre, bool by_weight,
+                   unsigned long long need, unsigned long long p32,
+                   unsigned long long* above) -> int {
+#pragma unroll
+    for (int q = 0; q < kSelQ; q++) S.hist[tid + q * kSelMT] = 0ull;
+    if (tid == 0) S.pick = -1;
     __syncthreads();
-    for (int r = wv; r < nrows; r += kTrCols / 64) {
-      int64_t c = cur[r];
-      const int64_t e = fin[r];
-      while (true) {
-        const int64_t idx = c + lane;
-        const int col = idx < e ? col_idx[idx] : 0x7fffffff;
-        const bool in = col < t1;  // a prefix of the lanes: the list is sorted
-        if (in) atomicOr(&mask[col - t0], 1ull << r);
-        const int m = __popcll(__ballot(in));
-        c += m;
-        if (m < 64) break;
+    const uint32_t dmask = (1u << (hi - lo)) - 1u;
+    const uint32_t hmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+    pre &= hmask;
+#pragma unroll
+    for (int e = 0; e < kSelPer; e++) {
+      if ((rel[e] & hmask) == pre) {
+        unsigned long long inc = 1ull << kCntShift;
+        if (by_weight) inc += wt(rel[e]);
+        atomicAdd(&S.hist[(rel[e] >> lo) & dmask], inc);
       }
-      if (lane == 0) cur[r] = c;
+    }
+    // the padding copies of the last element back out
+    if (tid == 0 && npad > 0 && (rlast & hmask) == pre) {
+      unsigned long long inc = 1ull << kCntShift;
+      if (by_weight) inc += wt(rlast);
+      atomicAdd(&S.hist[(rlast >> lo) & dmask], 0ull - (unsigned long long)npad * inc);
     }
     __syncthreads();
-    const int col = t0 + threadIdx.x;
-    if (!kFill) {
-      if (col < t1) tile_cnt[(int64_t)rt * n + col] = __popcll(mask[threadIdx.x]);
+    // thread t owns the digits kSelBins - 1 - kSelQ t - q, in selection order
+    unsigned long long v[kSelQ], sum = 0;
+#pragma unroll
+    for (int q = 0; q < kSelQ; q++) {
+      v[q] = S.hist[kSelBins - 1 - kSelQ * tid - q];
+      sum += v[q];
+    }
+    unsigned long long total;
+    unsigned long long run = row_excl_scan<unsigned long long>(sum, S.wsum, &total);
+    if (p32) {
+      const unsigned long long Z = total & kWtMask;
+      const unsigned long long zh = Z >> 32, zl = Z & 0xffffffffull;
+      need = p32 * zh + ((p32 * zl + 0xffffffffull) >> 32);
+      if (tid == 0) S.wstar = need;
+    }
+#pragma unroll
+    for (int q = 0; q < kSelQ; q++) {
+      const unsigned long long before = by_weight ? (run & kWtMask) : (run >> kCntShift);
+      const unsigned long long m = by_weight ? (v[q] & kWtMask) : (v[q] >> kCntShift);
+      if (before < need && before + m >= need) {
+        S.pick = kSelBins - 1 - kSelQ * tid - q;
+        S.above = run;
+      }
+      run += v[q];
+    }
+    __syncthreads();
+    int d = S.pick;
+    if (d < 0) {
+      d = 0;
+      *above = total - S.hist[0];
     } else {
-      // each column's rows go out as one store of a wave: lane r writes row
-      // i0 + r at its rank among the column's rows, so a column's run is
-      // written by consecutive lanes to consecutive addresses
-      if (col < t1) cpos[threadIdx.x] = colt_ptr[g0 + col] + tile_cnt[(int64_t)rt * n + col];
-      __syncthreads();
-      for (int cc = wv; cc < t1 - t0; cc += kTrCols / 64) {
-        const unsigned long long m = mask[cc];
-        if ((m >> lane) & 1ull)
-          colt_idx[cpos[cc] + __popcll(m & ((1ull << lane) - 1ull))] = i0 + lane;
-      }
+      *above = S.above;
     }
     __syncthreads();
+    return d;
+  };
+  // exact select: the order key at which the running total in selection
+  // order first reaches `need`, with the count and weight of larger keys
+  auto select = [&](bool by_weight, unsigned long long need, unsigned long long p32,
+                    uint32_t* ac, unsigned long long* aw,
+                    unsigned long long* need_out) -> uint32_t {
+    uint32_t prefix = 0;
+    unsigned long long ab = 0;
+    bool first = true;
+    for (int hi = span ? 32 - __builtin_clz(span) : 1; hi > 0;) {
+      const int lo = hi > kSelBits ? hi - kSelBits : 0;
+      const unsigned long long done = by_weight ? (ab & kWtMask) : (ab >> kCntShift);
+      unsigned long long a;
+      const int d = level(hi, lo, prefix, by_weight, need - done,
+                          first ? p32 : 0ull, &a);
+      if (first && p32) need = S.wstar;
+      first = false;
+      prefix |= (uint32_t)d << lo;
+      ab += a;
+      hi = lo;
+    }
+    if (need_out) *need_out = need;
+    *ac = (uint32_t)(ab >> kCntShift);
+    *aw = ab & kWtMask;
+    return kmin + prefix;
+  };
+
+  int64_t nsel = n;
+  uint32_t keyL = 0u;
+  int64_t tieL = 0;
+  if (p < 1.0f) {
+    int64_t L = 0;
+    uint32_t keyP = 0, caP = 0;
+    if (p > 0.0f) {
+      const unsigned long long P32 = (unsigned long long)ceil((double)p * 4294967296.0);
+      unsigned long long wa, Wstar;
+      keyP = select(true, 0ull, P32, &caP, &wa, &Wstar);
+      const unsigned long long wk = weight_of(key2f(keyP), smax);
+      L = (int64_t)caP + (int64_t)((Wstar - wa + wk - 1) / wk);
+    }
+    nsel = kk > L ? kk : L;
+    if (nsel > n) nsel = n;
+    keyL = 0xffffffffu;
+    tieL = 0;
+    if (nsel > 0 && nsel == L) {
+      keyL = keyP;
+      tieL = L - (int64_t)caP;
+    } else if (nsel > 0) {
+      uint32_t ca;
+      unsigned long long wa;
+      keyL = select(false, (unsigned long long)nsel, 0ull, &ca, &wa, nullptr);
+      tieL = nsel - (int64_t)ca;
+    }
+  }
+  if (tid == 0) {
+    row_cnt[g] = (int32_t)nsel;
+    row_key[g] = keyL;
+    row_tie[g] = (int32_t)tieL;
+  }
+
+  // the mask: every key above keyL and the first tieL copies of keyL in
+  // index order (index j = kSelMT e + 64 wave + lane); all of the row when
+  // p >= 1, none when nothing is selected.  Padding copies of keyL rank
+  // after every real one, so the first tieL copies are real.
+  const int mode = p >= 1.0f ? 2 : nsel == 0 ? 0 : 1;
+  const uint32_t Kr = keyL - kmin;  // keyL relative to the row's smallest key (mode 1)
+  int teq = 0;
+  if (mode == 1) {
+#pragma unroll
+    for (int e = 0; e < kSelPer; e++) teq += rel[e] == Kr ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) teq += __shfl_xor(teq, off, 64);
+  if (lane == 0) S.isum[wv] = teq;
+  __syncthreads();
+  int tall = 0;
+#pragma unroll
+  for (int w = 0; w < kSelMW; w++) tall += S.isum[w];
+  // only some copies of keyL are taken: their ranks in index order
+  const bool split = mode == 1 && tieL < tall;
+  if (split) {
+#pragma unroll
+    for (int e = 0; e < kSelPer; e++) {
+      const unsigned long long b = __ballot(rel[e] == Kr);
+      if (lane == 0) S.trank[e * kSelMW + wv] = __popcll(b);
+    }
+    __syncthreads();
+    int unused;
+    const int x = tid < kSelPer * kSelMW ? S.trank[tid] : 0;
+    const int ex = row_excl_scan<int>(x, S.isum, &unused);
+    if (tid < kSelPer * kSelMW) S.trank[tid] = ex;
+    __syncthreads();
+  }
+  unsigned long long word = 0;
+#pragma unroll
+  for (int e = 0; e < kSelPer; e++) {
+    bool sel = false;
+    if (mode == 2) {
+      sel = true;
+    } else if (mode == 1) {
+      const bool eq = rel[e] == Kr;
+      sel = rel[e] > Kr;
+      if (split) {
+        const unsigned long long b = __ballot(eq);
+        const int rank = S.trank[e * kSelMW + wv] +
+                         (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        sel = sel || (eq && rank < tieL);
+      } else {
+        sel = sel || eq;
+      }
+    }
+    const unsigned long long b = __ballot(sel);
+    if (lane == e) word = b;
+  }
+  // lane e (< kSelPer) holds the word of slab e and this wave: blocks
+  // j0 .. j0 + 63, j0 = kSelMT e + 64 wave; the bits of j >= n are dropped
+  const int w = kSelMW * lane + wv;
+  const int lim = n - (kSelMT * lane + 64 * wv);
+  if (lim < 64) word &= lim <= 0 ? 0ull : (1ull << lim) - 1ull;
+  if (lane < kSelPer && w < wd) mask[(int64_t)i * wd + w] = word;
+}
+
+// Per head: masks of the blocks of each volume class (64, 128, 256 rows),
+// word w covering blocks 64 w .. 64 w + 63 (one wave per word).
+__global__ __launch_bounds__(256) void k_vol_masks(const uint8_t* __restrict__ blk_shape,
+                                                   int64_t g0, int n, int wd,
+                                                   unsigned long long* __restrict__ volm) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= wd) return;
+  const int j = 64 * w + lane;
+  const int vol = j < n ? volume_of_id(block_shape_at(blk_shape, g0 + j)) : 0;
+  const unsigned long long m64 = __ballot(vol == 64), m128 = __ballot(vol == 128),
+                           m256 = __ballot(vol == 256);
+  if (lane == 0) {
+    volm[w] = m64;
+    volm[wd + w] = m128;
+    volm[2 * wd + w] = m256;
+  }
+}
+
+// sum of the volumes of the blocks set in word m of mask word index w
+__device__ inline int64_t masked_volume(unsigned long long m, const unsigned long long* volm,
+                                        int wd, int w) {
+  return 64 * (int64_t)__popcll(m & volm[w]) + 128 * (int64_t)__popcll(m & volm[wd + w]) +
+         256 * (int64_t)__popcll(m & volm[2 * wd + w]);
+}
+
+// Each row's selected key blocks in ascending order from its mask, and the
+// row's attention cost B_i * sum_{j in S_i} B_j.  Thread t takes word t
+// (wd <= 256): one prefix over the words' popcounts places every thread's
+// output in LDS, which is then stored contiguously.
+__global__ __launch_bounds__(kSelThreads) void k_select_emit(
+    const unsigned long long* __restrict__ mask, int wd, int64_t g0,
+    const int64_t* __restrict__ row_ptr, int64_t cap, const unsigned long long* __restrict__ volm,
+    const uint8_t* __restrict__ blk_shape, int32_t* __restrict__ col_idx,
+    int64_t* __restrict__ row_cost) {
+  __shared__ int32_t sout[kSelRegMax];
+  __shared__ int sh[kSelThreads / 64];
+  __shared__ int64_t sh_cost[kSelThreads / 64];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int64_t g = g0 + i;
+  unsigned long long m = tid < wd ? mask[(int64_t)i * wd + tid] : 0ull;
+  const int64_t cost = tid < wd ? masked_volume(m, volm, wd, tid) : 0;
+  int total;
+  int pos = block_excl_scan_i32(__popcll(m), sh, &total);
+  while (m) {
+    sout[pos++] = 64 * tid + __builtin_ctzll(m);
+    m &= m - 1;
+  }
+  __syncthreads();
+  const int64_t base = row_ptr[g];
+  if (base + total <= cap)
+    for (int e = tid; e < total; e += kSelThreads) col_idx[base + e] = sout[e];
+  const int64_t c = block_sum<int64_t>(cost, sh_cost);
+  if (tid == 0) row_cost[g] = c * (int64_t)volume_of_id(block_shape_at(blk_shape, g));
+}
+
+// The mask of a row from its ascending list (rows longer than the register
+// path holds): thread t builds the words t, t + 256, ..; a word's entries
+// are found by a binary search for its first block.  A row whose list did
+// not fit the workspace gets an empty mask.
+__global__ __launch_bounds__(kSelThreads) void k_list_mask(
+    const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t g0,
+    int wd, int64_t cap, unsigned long long* __restrict__ mask) {
+  const int i = blockIdx.x;
+  const int64_t a = row_ptr[g0 + i], e = row_ptr[g0 + i + 1];
+  const bool ok = e <= cap;
+  for (int w = threadIdx.x; w < wd; w += kSelThreads) {
+    unsigned long long word = 0;
+    if (ok) {
+      int64_t lo = a, hi = e;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (col_idx[mid] < 64 * w)
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      for (int64_t q = lo; q < e && col_idx[q] < 64 * w + 64; q++)
+        word |= 1ull << (col_idx[q] - 64 * w);
+    }
+    mask[(int64_t)i * wd + w] = word;
+  }
+}
+
+// Key-major transpose of one head's selection masks, by tiles of 64 query
+// rows x 64 key columns: lane r holds row i0 + r's mask word of the tile,
+// and one ballot per column gives that column's rows.  The counting pass
+// stores per (row tile, column) the column's row count and the sum of those
+// rows' volumes; the fill pass writes each column's rows of the tile in
+// ascending order at the column's offset, one store instruction per column.
+// No atomics: the result does not depend on the schedule.  Positions past
+// the workspace's capacity are not written (the plan then reports it).
+constexpr int kMtWords = 4;  // column words per wave
+template <bool kFill>
+__global__ __launch_bounds__(256) void k_mask_tr(
+    const unsigned long long* __restrict__ mask, int wd, int n, int64_t g0,
+    const unsigned long long* __restrict__ volm, const int64_t* __restrict__ colt_ptr,
+    int32_t* __restrict__ tile_cnt, int32_t* __restrict__ tile_cost, int64_t cap,
+    int32_t* __restrict__ colt_idx) {
+  const int rt = blockIdx.x, i0 = rt * 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = i0 + lane;
+  const int cw0 = (blockIdx.y * 4 + wv) * kMtWords;
+  for (int k = 0; k < kMtWords; k++) {
+    const int c = cw0 + k;
+    if (c >= wd) break;
+    const unsigned long long m = row < n ? mask[(int64_t)row * wd + c] : 0ull;
+    const int col = 64 * c + lane;
+    if (!kFill) {
+      unsigned long long cm = 0;
+#pragma unroll
+      for (int b = 0; b < 64; b++) {
+        const unsigned long long bal = __ballot((m >> b) & 1ull);
+        if (lane == b) cm = bal;
+      }
+      if (col < n) {
+        tile_cnt[(int64_t)rt * n + col] = __popcll(cm);
+        tile_cost[(int64_t)rt * n + col] = (int32_t)masked_volume(cm, volm, wd, rt);
+      }
+    } else {
+      const int64_t cpos = col < n ? colt_ptr[g0 + col] + tile_cnt[(int64_t)rt * n + col] : 0;
+      const uint32_t plo = (uint32_t)cpos, phi = (uint32_t)(cpos >> 32);
+#pragma unroll
+      for (int b = 0; b < 64; b++) {
+        const bool bit = (m >> b) & 1ull;
+        const unsigned long long bal = __ballot(bit);
+        if (bal == 0ull) continue;
+        const int64_t base = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(phi, b) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readlane(plo, b));
+        const int64_t pos = base + __builtin_amdgcn_mbcnt_hi(
+                                       (uint32_t)(bal >> 32),
+                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (bit && pos < cap) colt_idx[pos] = row;
+      }
+    }
   }
 }
 
 // per column: turn the row-tile counts into output positions relative to the
-// column's start (at most n, so they fit in 32 bits at any nnz), and the
-// column's total
-__global__ void k_colt_offsets(int n, int nch, int32_t* __restrict__ chunk_cnt,
-                               int32_t* __restrict__ colt_cnt) {
+// column's start (at most n, so they fit in 32 bits at any nnz), the
+// column's total, and its cost B_j * sum_{i: j in S_i} B_i
+__global__ void k_colt_offsets(int n, int nch, int64_t g0, int32_t* __restrict__ chunk_cnt,
+                               const int32_t* __restrict__ chunk_cost,
+                               const uint8_t* __restrict__ blk_shape,
+                               int32_t* __restrict__ colt_cnt, int64_t* __restrict__ colt_cost) {
   int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
   int32_t run = 0;
+  int64_t cost = 0;
   for (int c = 0; c < nch; c++) {
     int32_t t = chunk_cnt[(int64_t)c * n + j];
     chunk_cnt[(int64_t)c * n + j] = run;
     run += t;
+    cost += chunk_cost[(int64_t)c * n + j];
   }
-  colt_cnt[j] = run;
+  colt_cnt[g0 + j] = run;
+  colt_cost[g0 + j] = cost * (int64_t)volume_of_id(block_shape_at(blk_shape, g0 + j));
 }
 
 // key-major scan: counts per column -> pointers (reuses k_scan_rows on colt_cnt)
@@ -1443,25 +1720,6 @@ __global__ __launch_bounds__(256) void k_sum_i64(const int64_t* __restrict__ in,
 // unit index).  Units that run side by side then walk lists of nearly equal
 // length, which over a dense-ish selection name mostly the same tiles, and
 // start and end together.
-
-// Cost of each key block's key-major list in token pairs, B_j * sum_i B_i
-// (the transpose of the rows' cost); one wave per block.
-__global__ __launch_bounds__(256) void k_colt_cost(const int64_t* __restrict__ colt_ptr,
-                                                   const int32_t* __restrict__ colt_idx,
-                                                   int64_t g0, int n,
-                                                   const uint8_t* __restrict__ blk_shape,
-                                                   int64_t* __restrict__ colt_cost) {
-  const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (j >= n) return;
-  const int64_t g = g0 + j;
-  int64_t c = 0;
-  for (int64_t e = colt_ptr[g] + lane; e < colt_ptr[g + 1]; e += 64)
-    c += volume_of_id(block_shape_at(blk_shape, g0 + colt_idx[e]));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
-  if (lane == 0) colt_cost[g] = c * (int64_t)volume_of_id(block_shape_at(blk_shape, g));
-}
 
 // One work-group per head: the walk length of every unit of U rows (the
 // longest list among the unit's blocks, in 64-row tiles: cost / B / 64),
@@ -1520,13 +1778,7 @@ __global__ __launch_bounds__(1024) void k_unit_order(const uint8_t* __restrict__
 }
 
 // ============================================================ launchers
-bool launch_unit_order_k(const PlanDev& P, const std::vector<int64_t>& off, hipStream_t st) {
-  for (int h = 0; h < P.heads; h++) {
-    const int n = (int)(off[h + 1] - off[h]);
-    if (n > 0)
-      hipLaunchKernelGGL(k_colt_cost, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st,
-                         P.colt_ptr, P.colt_idx, off[h], n, P.blk_shape, P.colt_cost);
-  }
+bool launch_unit_order_k(const PlanDev& P, hipStream_t st) {
   hipLaunchKernelGGL(k_unit_order<128>, dim3(P.heads), dim3(1024), 0, st, P.shape_id,
                      P.zone_base, P.blk_off, P.colt_cost, P.Z, P.N, P.korder);
   return hipGetLastError() == hipSuccess;
@@ -1700,54 +1952,53 @@ bool launch_block_scores(const PlanDev& P, int64_t g0, int n, float* out, hipStr
   return hipGetLastError() == hipSuccess;
 }
 
-// dynamic LDS of the staged row: n floats, rounded up to whole 64-float
-// pieces of the staging loads
-static unsigned sel_lds_bytes(int n) { return (unsigned)(sel_row_floats(n) * 4); }
-// the fill kernel also stages the words that cover the head's n shape ids
-static unsigned sel_fill_lds_bytes(int n) {
-  return sel_lds_bytes(n) + (unsigned)(((n + 3) / 4 + 1 + 63) / 64 * 64 * 4);
-}
+// mask words per row of a head of n blocks
+static int mask_words(int n) { return (n + 63) / 64; }
 
 bool launch_select(const PlanDev& P, int64_t g0, int n, const prism_config& c, int last,
                    hipStream_t st) {
-  const bool lds = n <= kSelLdsMax;
-  if (n > 0) {
-    if (lds)
-      hipLaunchKernelGGL(k_select_count<true>, dim3(n), dim3(kSelThreads), sel_lds_bytes(n), st,
-                         P.scores, n, g0, c.top_k, c.top_k_frac, c.top_p, P.row_cnt, P.row_key,
-                         P.row_tie);
-    else
-      hipLaunchKernelGGL(k_select_count<false>, dim3(n), dim3(kSelThreads), 0, st, P.scores, n,
-                         g0, c.top_k, c.top_k_frac, c.top_p, P.row_cnt, P.row_key, P.row_tie);
-  }
-  hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, st, P.row_cnt, n, g0, P.row_ptr,
-                     P.counters, last);
-  if (n > 0) {
-    if (lds)
-      hipLaunchKernelGGL(k_select_fill<true>, dim3(n), dim3(kSelThreads), sel_fill_lds_bytes(n),
-                         st,
-                         P.scores, n, g0, P.row_cnt, P.row_key, P.row_tie, P.row_ptr, P.cap,
-                         P.blk_shape, P.col_idx, P.row_cost);
-    else
-      hipLaunchKernelGGL(k_select_fill<false>, dim3(n), dim3(kSelThreads), 0, st, P.scores, n,
-                         g0, P.row_cnt, P.row_key, P.row_tie, P.row_ptr, P.cap, P.blk_shape,
+  const int wd = mask_words(n);
+  if (n > 0)
+    hipLaunchKernelGGL(k_vol_masks, dim3((unsigned)((wd + 3) / 4)), dim3(256), 0, st,
+                       P.blk_shape, g0, n, wd, P.volm);
+  if (n > 0 && n <= kSelRegMax) {
+    hipLaunchKernelGGL(k_select_mask, dim3(n), dim3(kSelMT), 0, st, P.scores, n, g0,
+                       c.top_k, c.top_k_frac, c.top_p, P.row_cnt, P.row_key, P.row_tie,
+                       P.selmask, wd);
+    hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, st, P.row_cnt, n, g0, P.row_ptr,
+                       P.counters, last);
+    hipLaunchKernelGGL(k_select_emit, dim3(n), dim3(kSelThreads), 0, st, P.selmask, wd, g0,
+                       P.row_ptr, P.cap, P.volm, P.blk_shape, P.col_idx, P.row_cost);
+  } else {
+    if (n > 0)
+      hipLaunchKernelGGL(k_select_count, dim3(n), dim3(kSelThreads), 0, st, P.scores, n, g0,
+                         c.top_k, c.top_k_frac, c.top_p, P.row_cnt, P.row_key, P.row_tie);
+    hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, st, P.row_cnt, n, g0, P.row_ptr,
+                       P.counters, last);
+    if (n > 0) {
+      hipLaunchKernelGGL(k_select_fill, dim3(n), dim3(kSelThreads), 0, st, P.scores, n, g0,
+                         P.row_cnt, P.row_key, P.row_tie, P.row_ptr, P.cap, P.blk_shape,
                          P.col_idx, P.row_cost);
+      if (c.need_backward)
+        hipLaunchKernelGGL(k_list_mask, dim3(n), dim3(kSelThreads), 0, st, P.row_ptr,
+                           P.col_idx, g0, wd, P.cap, P.selmask);
+    }
   }
   return hipGetLastError() == hipSuccess;
 }
 
 bool launch_transpose(const PlanDev& P, int64_t g0, int n, int last, hipStream_t st) {
   if (n <= 0) return true;
-  const int nrt = (n + kTrRows - 1) / kTrRows;
-  const dim3 grid((unsigned)nrt, (unsigned)((n + kTrPart - 1) / kTrPart));
-  hipLaunchKernelGGL(k_colt_tiles<false>, grid, dim3(kTrCols), 0, st, P.row_ptr, P.col_idx, n,
-                     g0, P.colt_ptr, P.chunk_cnt, P.colt_idx);
-  hipLaunchKernelGGL(k_colt_offsets, dim3((n + 255) / 256), dim3(256), 0, st, n, nrt,
-                     P.chunk_cnt, P.colt_cnt + g0);
+  const int wd = mask_words(n);
+  const dim3 grid((unsigned)wd, (unsigned)((wd + 4 * kMtWords - 1) / (4 * kMtWords)));
+  hipLaunchKernelGGL(k_mask_tr<false>, grid, dim3(256), 0, st, P.selmask, wd, n, g0, P.volm,
+                     P.colt_ptr, P.chunk_cnt, P.chunk_cost, P.cap, P.colt_idx);
+  hipLaunchKernelGGL(k_colt_offsets, dim3((n + 255) / 256), dim3(256), 0, st, n, wd, g0,
+                     P.chunk_cnt, P.chunk_cost, P.blk_shape, P.colt_cnt, P.colt_cost);
   hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, st, P.colt_cnt, n, g0, P.colt_ptr,
                      P.counters + 1, last);
-  hipLaunchKernelGGL(k_colt_tiles<true>, grid, dim3(kTrCols), 0, st, P.row_ptr, P.col_idx, n,
-                     g0, P.colt_ptr, P.chunk_cnt, P.colt_idx);
+  hipLaunchKernelGGL(k_mask_tr<true>, grid, dim3(256), 0, st, P.selmask, wd, n, g0, P.volm,
+                     P.colt_ptr, P.chunk_cnt, P.chunk_cost, P.cap, P.colt_idx);
   return hipGetLastError() == hipSuccess;
 }
 

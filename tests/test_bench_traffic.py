@@ -15,21 +15,28 @@ FIELDS = ["Kernel_Name", "Counter_Name", "Counter_Value"]
 
 
 def write_csv(path, counter, rows):
+    """rows: (kernel name, KiB[, duration ns]); dispatches run back to back"""
     with open(path, "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w = csv.DictWriter(f, fieldnames=FIELDS + ["Start_Timestamp", "End_Timestamp"])
         w.writeheader()
-        for name, kib in rows:
-            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": kib})
+        t = 0
+        for name, kib, *dur in rows:
+            d = dur[0] if dur else 1000
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": kib,
+                        "Start_Timestamp": t, "End_Timestamp": t + d})
+            t += d
 
 
 def test_summary_scales_by_the_copy_and_tracks_the_sources(tmp_path, monkeypatch):
     gib_kib = (1 << 30) / 1024
-    # the counters read half the copy's fetched bytes and all of its writes
+    # the counters read half the copy's fetched bytes and all of its writes;
+    # the kernel's short first dispatch (a small warm-up grid) is not the launch
     write_csv(tmp_path / "f.csv", "FETCH_SIZE",
-              [("prism::k_bwd_dkdv(...)", 1000.0), ("other_kernel", 5.0),
+              [("prism::k_bwd_dkdv(...)", 7.0, 50), ("prism::k_bwd_dkdv(...)", 1000.0, 9000),
+               ("other_kernel", 5.0),
                ("void at::native::bitwise_not_kernel(...)", gib_kib / 2)])
     write_csv(tmp_path / "w.csv", "WRITE_SIZE",
-              [("prism::k_bwd_dkdv(...)", 30.0),
+              [("prism::k_bwd_dkdv(...)", 3.0, 50), ("prism::k_bwd_dkdv(...)", 30.0, 9000),
                ("void at::native::bitwise_not_kernel(...)", gib_kib)])
     out = tmp_path / "summary.md"
     bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "bwd.dkdv", "wl",
