@@ -266,6 +266,9 @@ def parse():
     ap.add_argument("--cpu-blocks", type=int, default=0,
                     help="query blocks in the CPU-oracle sample (0 = host cores)")
     ap.add_argument("--fwd-only", action="store_true")
+    ap.add_argument("--gather", action="store_true",
+                    help="no re-laid copies: attention gathers every tile through the "
+                         "block -> token map")
     ap.add_argument("--calib-copy", action="store_true",
                     help="end with a plain copy of known size (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -369,7 +372,7 @@ def main():
     q, k, v, do, av = x["q"], x["k"], x["v"], x["do"], x["av"]
     kw = dict(T=wl.T, H=wl.H, W=wl.W, top_k=wl.top_k, top_p=wl.top_p, top_k_frac=wl.top_k_frac,
               volume_mask=wl.volume_mask, fixed_shape=tuple(wl.fixed_shape),
-              need_backward=not args.fwd_only)
+              need_backward=not args.fwd_only, relayout=not args.gather)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     grads = None if args.fwd_only else (torch.empty_like(q), torch.empty_like(k),
@@ -515,7 +518,9 @@ def main():
                                f"{'fwd' if args.fwd_only else 'fwd+bwd'}",
                    "tokens": wl.N, "heads": wl.heads, "head_dim": D, "top_k": wl.top_k,
                    "top_k_frac": wl.top_k_frac,
-                   "top_p": wl.top_p, "parallelism": "single GPU"},
+                   "top_p": wl.top_p,
+                   "layout": "gathered" if args.gather else "re-laid copies",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -53,6 +53,7 @@ class PrismConfig(ctypes.Structure):
         ("eps", ctypes.c_float), ("tau128", ctypes.c_float), ("tau256", ctypes.c_float),
         ("need_backward", ctypes.c_int32), ("shape_map", ctypes.c_int32),
         ("alpha", ctypes.c_float), ("cut_threshold", ctypes.c_float),
+        ("relayout", ctypes.c_int32),
     ]
 
 

@@ -40,7 +40,7 @@ def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
 def make_config(T, H, W, heads, head_dim, dtype, *, top_k=16, top_k_frac=0.0, top_p=0.9,
                 volume_mask=7, fixed_shape=(0, 0, 0), eps=1e-4, tau128=0.5, tau256=0.25,
                 need_backward=True, shape_map="power", alpha=0.5,
-                cut_threshold=0.0) -> nat.PrismConfig:
+                cut_threshold=0.0, relayout=True) -> nat.PrismConfig:
     c = nat.PrismConfig()
     nat.lib().prism_config_default(ctypes.byref(c))
     c.T, c.H, c.W, c.heads, c.head_dim = T, H, W, heads, head_dim
@@ -54,6 +54,7 @@ def make_config(T, H, W, heads, head_dim, dtype, *, top_k=16, top_k_frac=0.0, to
     c.shape_map = nat.SHAPE_MAPS[shape_map] if isinstance(shape_map, str) else int(shape_map)
     c.alpha = float(alpha)
     c.cut_threshold = float(cut_threshold)
+    c.relayout = 1 if relayout else 0
     return c
 
 
@@ -109,11 +110,13 @@ class Plan:
 def plan(q, k, v, av_norm=None, *, T, H, W, top_k=16, top_k_frac=0.0, top_p=0.9,
          volume_mask=7, fixed_shape=(0, 0, 0), eps=1e-4, tau128=0.5, tau256=0.25,
          need_backward=True, shape_map="power", alpha=0.5, cut_threshold=0.0,
-         nnz_capacity=None, workspace=None) -> Plan:
+         relayout=True, nnz_capacity=None, workspace=None) -> Plan:
     """Stages one to three (shapes, block table, pooling, selection).
     shape_map: "power" (b_d ~ g_d^-alpha; alpha = 1/2 is the pages' method),
     "isotropic", "softmax", "rank" or "entropy" (the pages' ablations).
-    cut_threshold > 0: shot-cut-aware temporal zones."""
+    cut_threshold > 0: shot-cut-aware temporal zones.
+    relayout: keep block-contiguous copies of K and V (and let the backward
+    copy Q and dO); False gathers every tile from the caller's tensors."""
     heads, N, D = q.shape
     assert N == T * H * W and k.shape == q.shape and v.shape == q.shape
     assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
@@ -123,7 +126,8 @@ def plan(q, k, v, av_norm=None, *, T, H, W, top_k=16, top_k_frac=0.0, top_p=0.9,
     cfg = make_config(T, H, W, heads, D, q.dtype, top_k=top_k, top_k_frac=top_k_frac,
                       top_p=top_p, volume_mask=volume_mask, fixed_shape=fixed_shape, eps=eps,
                       tau128=tau128, tau256=tau256, need_backward=need_backward,
-                      shape_map=shape_map, alpha=alpha, cut_threshold=cut_threshold)
+                      shape_map=shape_map, alpha=alpha, cut_threshold=cut_threshold,
+                      relayout=relayout)
     nat.check(nat.lib().prism_config_check(ctypes.byref(cfg)), "prism_config_check")
     Z = (T // 8) * (H // 8) * (W // 8)
     worst = heads * (8 * Z) ** 2
@@ -166,13 +170,16 @@ def attn_bwd_workspace_bytes(pl: Plan) -> int:
 
 
 def attn_bwd(pl: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None):
-    """Backward with the plan held constant; returns (dq, dk, dv)."""
+    """Backward with the plan held constant; returns (dq, dk, dv).  Without a
+    workspace one of attn_bwd_workspace_bytes(pl) is allocated; a given one
+    is used as it is (one holding only the Delta / LSE columns, 8 bytes per
+    token and head, runs the backward without the copies of Q and dO)."""
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = attn_bwd_workspace_bytes(pl)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(attn_bwd_workspace_bytes(pl), dtype=torch.uint8,
+                                device=q.device)
     nat.check(nat.lib().prism_attn_bwd(pl.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                        _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                        workspace.numel(), _stream(q.device)), "prism_attn_bwd")

@@ -130,6 +130,10 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
   P->klo = A.take<uint16_t>(G * D);
   P->qexp = A.take<int32_t>(G);
   P->kexp = A.take<int32_t>(G);
+  // stage two's copies of K and V (bf16, head_dim 128)
+  P->relayout = c.relayout && c.dtype == PRISM_BF16 && c.head_dim == 128;
+  P->kp = P->relayout ? A.take<uint16_t>((int64_t)c.heads * N * 128) : nullptr;
+  P->vp = P->relayout ? A.take<uint16_t>((int64_t)c.heads * N * 128) : nullptr;
   P->scores = A.take<float>(maxblk * maxblk);
   P->selmask = A.take<unsigned long long>(maxblk * ((maxblk + 63) / 64));
   P->volm = A.take<unsigned long long>(3 * ((maxblk + 63) / 64));
@@ -171,6 +175,37 @@ size_t carve(const prism_config& c, int64_t cap, char* base, PlanDev* P, int32_t
 
 size_t per_pair_bytes(const prism_config& c) { return c.need_backward ? 8 : 4; }
 
+// the configuration asks for stage two's copies and the kernels take them
+bool relaid_config(const prism_config& c) {
+  return c.relayout && c.dtype == PRISM_BF16 && c.head_dim == 128;
+}
+
+// The backward's workspace: Delta and log2(e) * LSE per token (token
+// order), and with the copies Q, dO and both columns in block-contiguous
+// order.  The same carving serves sizing (base null) and use.
+struct BwdCarve {
+  float *delta, *lse2, *delta_p, *lse2_p;
+  uint16_t *qp, *dop;
+};
+size_t bwd_carve(const prism_config& c, bool relaid, char* base, BwdCarve* out) {
+  const int64_t rows = (int64_t)c.heads * c.T * c.H * c.W;
+  Arena A{base};
+  BwdCarve b{};
+  b.delta = A.take<float>(rows);
+  b.lse2 = A.take<float>(rows);
+  if (relaid) {
+    b.qp = A.take<uint16_t>(rows * 128);
+    b.dop = A.take<uint16_t>(rows * 128);
+    b.delta_p = A.take<float>(rows);
+    b.lse2_p = A.take<float>(rows);
+  }
+  if (out) *out = b;
+  return A.off + 256;
+}
+size_t bwd_workspace_bytes(const prism_config& c, bool relaid) {
+  return bwd_carve(c, relaid, nullptr, nullptr);
+}
+
 }  // namespace
 
 extern "C" {
@@ -193,6 +228,7 @@ void prism_config_default(prism_config* c) {
   c->shape_map = PRISM_MAP_POWER;
   c->alpha = 0.5f;
   c->cut_threshold = 0.0f;
+  c->relayout = 1;
 }
 
 prism_status prism_config_check(const prism_config* c) {
@@ -278,6 +314,11 @@ prism_status prism_plan_create(const prism_config* c, const void* q, const void*
   stage_begin("plan.pool", st);
   ok = launch_pool(P, q, k, st);
   stage_end(st);
+  if (ok && P.relayout) {
+    stage_begin("plan.relayout", st);
+    ok = launch_relayout(P, k, v, nullptr, nullptr, P.kp, P.vp, nullptr, nullptr, st);
+    stage_end(st);
+  }
   PRISM_HIP(hipMemsetAsync(P.counters, 0, sizeof(int64_t) * 8, st));
   for (int h = 0; h < c->heads && ok; h++) {
     int n = (int)(off[h + 1] - off[h]);
@@ -346,11 +387,7 @@ prism_status prism_attn_bwd_workspace_size(const prism_config* c, size_t* bytes)
   prism_status s = prism_config_check(c);
   if (s != PRISM_OK) return s;
   if (!bytes) return PRISM_EINVAL;
-  const int64_t N = (int64_t)c->T * c->H * c->W;
-  Arena A{nullptr};
-  A.take<float>((int64_t)c->heads * N);
-  A.take<float>((int64_t)c->heads * N);
-  *bytes = A.off + 256;
+  *bytes = bwd_workspace_bytes(*c, relaid_config(*c));
   return PRISM_OK;
 }
 
@@ -358,31 +395,38 @@ prism_status prism_attn_bwd_workspace_size(const prism_config* c, size_t* bytes)
 
 namespace {
 
-// The backward with its scratch (Delta and log2(e) * LSE per token) carved
-// from `workspace`.  `timed`: record the stage events of the
+// The backward with its scratch (Delta and log2(e) * LSE per token, and
+// with `copies` and room for them the block-contiguous copies of Q and dO)
+// carved from `workspace`.  `timed`: record the stage events of the
 // measurement support (which may create HIP events).
 prism_status bwd_run(const prism_plan_t* plan, const void* q, const void* k, const void* v,
                      const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                      void* dv, void* workspace, size_t workspace_bytes, hipStream_t st,
-                     bool timed) {
+                     bool timed, bool copies) {
   if (!plan || !q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv || !workspace)
     return PRISM_EINVAL;
   if (k != plan->k || v != plan->v) return PRISM_ESTATE;
   const prism_config& c = plan->cfg;
   if (!c.need_backward) return PRISM_ESTATE;
   if (!(c.dtype == PRISM_BF16 && c.head_dim == 128)) return PRISM_EUNSUPPORTED;
-  size_t need = 0;
-  prism_attn_bwd_workspace_size(&c, &need);
-  if (workspace_bytes < need) return PRISM_ENOMEM_WORKSPACE;
-  const int64_t N = plan->P.N;
-  Arena A{(char*)workspace};
+  // the copies of Q and dO when the configuration asks for them and the
+  // workspace holds them; else the query tiles are gathered
+  const bool relaid =
+      copies && relaid_config(c) && workspace_bytes >= bwd_workspace_bytes(c, true);
+  if (workspace_bytes < bwd_workspace_bytes(c, relaid)) return PRISM_ENOMEM_WORKSPACE;
+  BwdCarve W;
+  bwd_carve(c, relaid, (char*)workspace, &W);
   BwdDev B;
   B.q = q;
   B.k = k;
   B.v = v;
   B.d_o = d_o;
-  B.delta = A.take<float>((int64_t)c.heads * N);
-  B.lse2 = A.take<float>((int64_t)c.heads * N);
+  B.delta = W.delta;
+  B.lse2 = W.lse2;
+  B.qp = W.qp;
+  B.dop = W.dop;
+  B.delta_p = W.delta_p;
+  B.lse2_p = W.lse2_p;
   PRISM_HIP(hipGetLastError());
   if (timed) stage_begin("bwd.prep", st);
   bool ok = launch_bwd_prep(plan->P, B, o, lse, st);
@@ -428,7 +472,7 @@ prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void*
                             void* dq, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, void* stream) {
   return bwd_run(plan, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes,
-                 (hipStream_t)stream, true);
+                 (hipStream_t)stream, true, true);
 }
 
 prism_status prism_attn_bwd_noalloc(const prism_plan_t* plan, const void* q, const void* k,
@@ -436,15 +480,16 @@ prism_status prism_attn_bwd_noalloc(const prism_plan_t* plan, const void* q, con
                                     const void* d_o, void* dq, void* dk, void* dv,
                                     void* stream) {
   if (!plan) return PRISM_EINVAL;
-  size_t need = 0;
-  prism_status s = prism_attn_bwd_workspace_size(&plan->cfg, &need);
+  prism_status s = prism_config_check(&plan->cfg);
   if (s != PRISM_OK) return s;
-  if (need > (size_t)PRISM_NOALLOC_SCRATCH_BYTES) return PRISM_ENOMEM_WORKSPACE;
+  // (no copies of Q and dO: the columns alone must fit the array)
+  if (bwd_workspace_bytes(plan->cfg, false) > (size_t)PRISM_NOALLOC_SCRATCH_BYTES)
+    return PRISM_ENOMEM_WORKSPACE;
   void* ws = nullptr;
   s = scratch_address(&ws);
   if (s != PRISM_OK) return s;
   return bwd_run(plan, q, k, v, o, lse, d_o, dq, dk, dv, ws, PRISM_NOALLOC_SCRATCH_BYTES,
-                 (hipStream_t)stream, false);
+                 (hipStream_t)stream, false, false);
 }
 
 prism_status prism_av_cross_attn(const void* q, const void* ka, const void* va, int32_t heads,

@@ -5,9 +5,11 @@
 //   dV = P^T dO,  dK = dS^T Q / sqrt(D),  dQ = dS K / sqrt(D).
 //
 // gfx950 design (bf16, head_dim 128), deterministic (no atomics):
-//  * prep: Delta and log2(e) * LSE per token (original order); every tile of
-//    Q, dO, K, V and every LSE / Delta column is gathered straight from the
-//    caller's tensors through the block -> token map;
+//  * prep: Delta and log2(e) * LSE per token (original order) and, with the
+//    re-layout, copies of Q, dO and both columns in block-contiguous order;
+//    every tile of Q, dO (and the LSE / Delta columns) comes from those
+//    copies and every K, V tile from the plan's (or, without copies, each is
+//    gathered from the caller's tensors through the block -> token map);
 //  * dK/dV: a work-group owns 128 permuted key rows (4 waves x 32 keys, K and
 //    V of its keys in registers, dK/dV accumulators pinned to AGPRs) and
 //    walks the query blocks whose S_i holds its key blocks (key-major lists);
@@ -70,12 +72,16 @@ __global__ __launch_bounds__(512) void k_bwd_prep(const uint16_t* __restrict__ o
 }
 
 // ---------------------------------------------------------------- dK, dV
+// kRelaid: q, d_o, lse2 and delta are the block-contiguous copies and
+// blk_base holds each block's first permuted row; else they are in token
+// order and blk_base holds each block's first token
+template <bool kRelaid>
 __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse2, const float* __restrict__ delta,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint8_t* __restrict__ shape_id, const int32_t* __restrict__ zone_base,
-    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_org,
+    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_base,
     const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ colt_ptr,
     const int32_t* __restrict__ colt_idx, int H, int W, int Z, int64_t N, float c_log2,
     float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t nunits,
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
   tr_offsets(lane, to);
 
   TileIter it;
-  it.init(colt_ptr, colt_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_org,
+  it.init(colt_ptr, colt_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_base,
           blk_shape, hoff);
   const __amdgpu_buffer_rsrc_t rsQ = buffer_of(q + hrow * 128, (uint32_t)(N * 256));
   const __amdgpu_buffer_rsrc_t rsD = buffer_of(d_o + hrow * 128, (uint32_t)(N * 256));
@@ -146,18 +152,18 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
       buffer_of((wvu & 1) ? delta + hrow : lse2 + hrow, (uint32_t)(N * 4));
   const uint32_t lring = lds_offset(ring);
   const uint32_t lcol = lds_offset(ringc) + (wvu & 1) * 256;
-  // tile t of the query block (first token org, shape sid) from Q and dO,
-  // with its LSE or Delta column, into slot b
+  // tile t of the query block (base org, shape sid) from Q and dO, with its
+  // LSE or Delta column, into slot b
   auto stage = [&](int b, uint32_t org, int sid, int t) {
     const uint32_t o = lring + b * 2 * kTile;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const uint32_t piece = i * 256 + wvu * 64;
-      const uint32_t src = tile_src16(org, sid, t, piece + lane, H, W);
+      const uint32_t src = tile_src<kRelaid>(org, sid, t, piece + lane, H, W);
       dma16(rsQ, src, o + piece * 16);
       dma16(rsD, src, o + kTile + piece * 16);
     }
-    dma4(rsC, tile_src4(org, sid, t, lane, H, W), lcol + b * 512);
+    dma4(rsC, col_src<kRelaid>(org, sid, t, lane, H, W), lcol + b * 512);
   };
 
   uint32_t ring_f = 0;  // list masks of the tiles in the ring, a byte per slot
@@ -322,12 +328,16 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_dkdv(
 }
 
 // ---------------------------------------------------------------- dQ
+// kRelaid: k and v are the plan's block-contiguous copies and blk_base holds
+// each block's first permuted row; else the caller's tensors and first tokens
+// (this work-group's own Q, dO, LSE and Delta rows are read in token order)
+template <bool kRelaid>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse2, const float* __restrict__ delta,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint8_t* __restrict__ shape_id, const int32_t* __restrict__ zone_base,
-    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_org,
+    const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_base,
     const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, int H, int W, int Z, int64_t N, float c_log2,
     float scale, uint16_t* __restrict__ dq) {
@@ -348,7 +358,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
   const int mylist = (32 * wvu) / B < nlists ? (32 * wvu) / B : 0;
 
   TileIterS it;
-  it.init(row_ptr, col_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_org,
+  it.init(row_ptr, col_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_base,
           blk_shape, hoff);
 
   // this wave's 32 query rows: Q and dO as MFMA B operands, LSE and Delta of
@@ -385,7 +395,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void k_bwd_dq(
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const uint32_t piece = i * 512 + wvu * 64;
-      const uint32_t src = tile_src16(org, sid, t, piece + lane, H, W);
+      const uint32_t src = tile_src<kRelaid>(org, sid, t, piece + lane, H, W);
       dma16(rsK, src, lK + b * kTile + piece * 16);
       dma16(rsV, src, lV + b * kTile + piece * 16);
     }
@@ -528,7 +538,10 @@ bool launch_bwd_prep(const PlanDev& P, const BwdDev& Bd, const void* o, const fl
   const int64_t rows = P.heads * P.N;
   hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)((rows + 7) / 8)), dim3(512), 0, st,
                      (const uint16_t*)o, (const uint16_t*)Bd.d_o, lse, rows, Bd.delta, Bd.lse2);
-  return hipGetLastError() == hipSuccess;
+  if (hipGetLastError() != hipSuccess) return false;
+  // the copies dK/dV streams its query tiles from
+  return !Bd.qp || launch_relayout(P, Bd.q, Bd.d_o, Bd.lse2, Bd.delta, Bd.qp, Bd.dop, Bd.lse2_p,
+                                   Bd.delta_p, st);
 }
 
 bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& Bd, void* dk, void* dv, hipStream_t st) {
@@ -538,23 +551,36 @@ bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& Bd, void* dk, void* dv, hip
   const int64_t nunits = P.heads * (P.N / kKvRows);
   if (P.kv_persist) hipLaunchKernelGGL(k_clear_sync, dim3(1), dim3(128), 0, st, P.sync);
   dim3 grid((unsigned)(P.kv_persist ? persistent_grid() : nunits)), block(kKvWaves * 64);
-  hipLaunchKernelGGL(k_bwd_dkdv, grid, block, 0, st, (const uint16_t*)Bd.q,
-                     (const uint16_t*)Bd.d_o, Bd.lse2, Bd.delta, (const uint16_t*)Bd.k,
-                     (const uint16_t*)Bd.v, P.shape_id, P.zone_base, P.blk_off, P.blk_org,
-                     P.blk_shape, P.colt_ptr, P.colt_idx, P.H, P.W, P.Z, P.N, kCLog2, kScale,
-                     (uint16_t*)dk, (uint16_t*)dv, nunits, P.korder,
-                     P.kv_persist ? P.sync : nullptr);
+  if (Bd.qp)
+    hipLaunchKernelGGL(k_bwd_dkdv<true>, grid, block, 0, st, Bd.qp, Bd.dop, Bd.lse2_p,
+                       Bd.delta_p, (const uint16_t*)Bd.k, (const uint16_t*)Bd.v, P.shape_id,
+                       P.zone_base, P.blk_off, P.blk_start, P.blk_shape, P.colt_ptr,
+                       P.colt_idx, P.H, P.W, P.Z, P.N, kCLog2, kScale, (uint16_t*)dk,
+                       (uint16_t*)dv, nunits, P.korder, P.kv_persist ? P.sync : nullptr);
+  else
+    hipLaunchKernelGGL(k_bwd_dkdv<false>, grid, block, 0, st, (const uint16_t*)Bd.q,
+                       (const uint16_t*)Bd.d_o, Bd.lse2, Bd.delta, (const uint16_t*)Bd.k,
+                       (const uint16_t*)Bd.v, P.shape_id, P.zone_base, P.blk_off, P.blk_org,
+                       P.blk_shape, P.colt_ptr, P.colt_idx, P.H, P.W, P.Z, P.N, kCLog2,
+                       kScale, (uint16_t*)dk, (uint16_t*)dv, nunits, P.korder,
+                       P.kv_persist ? P.sync : nullptr);
   return hipGetLastError() == hipSuccess;
 }
 
 bool launch_bwd_dq(const PlanDev& P, const BwdDev& Bd, void* dq, hipStream_t st) {
   if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
   dim3 grid((unsigned)(P.heads * (P.N / kDqRows))), block(kDqWaves * 64);
-  hipLaunchKernelGGL(k_bwd_dq, grid, block, 0, st, (const uint16_t*)Bd.q,
-                     (const uint16_t*)Bd.d_o, Bd.lse2, Bd.delta, (const uint16_t*)Bd.k,
-                     (const uint16_t*)Bd.v, P.shape_id, P.zone_base, P.blk_off, P.blk_org,
-                     P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W, P.Z, P.N, kCLog2, kScale,
-                     (uint16_t*)dq);
+  if (P.relayout)
+    hipLaunchKernelGGL(k_bwd_dq<true>, grid, block, 0, st, (const uint16_t*)Bd.q,
+                       (const uint16_t*)Bd.d_o, Bd.lse2, Bd.delta, P.kp, P.vp, P.shape_id,
+                       P.zone_base, P.blk_off, P.blk_start, P.blk_shape, P.row_ptr, P.col_idx,
+                       P.H, P.W, P.Z, P.N, kCLog2, kScale, (uint16_t*)dq);
+  else
+    hipLaunchKernelGGL(k_bwd_dq<false>, grid, block, 0, st, (const uint16_t*)Bd.q,
+                       (const uint16_t*)Bd.d_o, Bd.lse2, Bd.delta, (const uint16_t*)Bd.k,
+                       (const uint16_t*)Bd.v, P.shape_id, P.zone_base, P.blk_off, P.blk_org,
+                       P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W, P.Z, P.N, kCLog2, kScale,
+                       (uint16_t*)dq);
   return hipGetLastError() == hipSuccess;
 }
 

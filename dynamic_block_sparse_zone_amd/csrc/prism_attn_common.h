@@ -3,13 +3,15 @@
 //
 // Tiles.  A 64-row tile is 64 consecutive rows of one block in the
 // block-contiguous order of the plan, and every block is a whole number of
-// tiles.  Its rows are gathered straight from the caller's [heads][N][128]
-// bf16 tensors (K, V, and in the backward Q, dO) through the closed-form
-// block -> token map (block_row_offset from the block's first token), so no
-// re-laid copy of any tensor exists.  Each lane moves one 16-byte chunk per
-// load and picks the chunk so that LDS row rho holds logical chunk c at
-// c ^ chunk_swizzle(rho); a row is 256 contiguous bytes in HBM, and a wave's
-// load covers four whole rows.
+// tiles.  Either its rows are gathered straight from the caller's
+// [heads][N][128] bf16 tensors (K, V, and in the backward Q, dO) through the
+// closed-form block -> token map (block_row_offset from the block's first
+// token), or they come from re-laid copies in block-contiguous order (stage
+// two's re-layout), where a tile is one contiguous 16 KB run.  Each lane
+// moves one 16-byte chunk per load and picks the chunk so that LDS row rho
+// holds logical chunk c at c ^ chunk_swizzle(rho) (the copies store their
+// rows that way already); a row is 256 contiguous bytes in HBM, and a
+// wave's load covers four whole rows.
 //
 // Ring.  A work-group keeps kRing tile slots in LDS with kRing - 1 tiles in
 // flight.  Every step issues exactly one tile (past the end of the lists it
@@ -80,6 +82,26 @@ __device__ inline uint32_t tile_src16(uint32_t org, int sid, int t, uint32_t slo
 // Byte offset of row rho (0..63) of that tile in a per-token [N] float array.
 __device__ inline uint32_t tile_src4(uint32_t org, int sid, int t, uint32_t rho, int H, int W) {
   return (org + block_row_offset(sid, 64u * t + rho, H, W)) * 4u;
+}
+
+// Tile sources of the two layouts.  Gathered (kRelaid false): base is the
+// block's first token and rows come through the block -> token map.
+// Re-laid: base is the block's first permuted row in a copy whose rows are
+// in block-contiguous order with their chunks already swizzled, so LDS slot
+// `slot` takes byte slot * 16 of the tile's contiguous 16 KB run.
+template <bool kRelaid>
+__device__ inline uint32_t tile_src(uint32_t base, int sid, int t, uint32_t slot, int H, int W) {
+  if constexpr (kRelaid)
+    return (base + 64u * t) * 256u + slot * 16u;
+  else
+    return tile_src16(base, sid, t, slot, H, W);
+}
+template <bool kRelaid>
+__device__ inline uint32_t col_src(uint32_t base, int sid, int t, uint32_t rho, int H, int W) {
+  if constexpr (kRelaid)
+    return (base + 64u * t + rho) * 4u;
+  else
+    return tile_src4(base, sid, t, rho, H, W);
 }
 
 // Per-lane byte offsets inside a swizzled 64-row tile (row stride 256 B).

@@ -13,8 +13,9 @@
 //    holds one query row's scores and the softmax needs one cross-lane step;
 //  * O^T += V^T P^T takes the bf16 probabilities as the B operand directly;
 //    the V^T fragments come from the row-major V tile by ds_read_b64_tr_b16;
-//  * K/V tiles of 64 keys are gathered from the caller's K and V through the
-//    block -> token map and stream through a 4-slot LDS ring: the barrier of
+//  * K/V tiles of 64 keys come from the plan's re-laid copies (or are
+//    gathered from the caller's K and V through the block -> token map) and
+//    stream through a 4-slot LDS ring: the barrier of
 //    step j publishes tile j + 1 and frees the slot of tile j - 1 for tile
 //    j + 3, so while tile j is computed the next one is already readable;
 //  * the fragment reads that open each matrix stretch are issued one stretch
@@ -36,11 +37,15 @@ constexpr int kFwdWaves = kFwdRows / 32;  // one wave per 32 rows
 // loads per wave per K/V tile pair: 2 x 16 KB over 8 waves in 1 KB pieces
 constexpr int kFwdLoads = 2 * kTile / (kFwdWaves * 1024);
 
+// kRelaid: k and v are the plan's block-contiguous copies and blk_base holds
+// each block's first permuted row; else k and v are the caller's tensors and
+// blk_base each block's first token
+template <bool kRelaid>
 __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint8_t* __restrict__ shape_id,
     const int32_t* __restrict__ zone_base, const int64_t* __restrict__ blk_off,
-    const int32_t* __restrict__ blk_org, const uint8_t* __restrict__ blk_shape,
+    const int32_t* __restrict__ blk_base, const uint8_t* __restrict__ blk_shape,
     const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int H, int W,
     int Z, int64_t N, float c_log2, uint16_t* __restrict__ o, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char ringK[kRing * kTile];
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
   const int mylist = (32 * wvu) / B < nlists ? (32 * wvu) / B : 0;
 
   TileIter it;
-  it.init(row_ptr, col_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_org,
+  it.init(row_ptr, col_idx, hoff + zone_base[(int64_t)h * Z + m] + rz / B, nlists, blk_base,
           blk_shape, hoff);
 
   // query fragments: row p of this wave, 8 chunks of 16 channels
@@ -86,18 +91,18 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
     for (int r = 0; r < 16; r++) acc[db][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // this head's K and V (N original rows of 256 B) as buffers
+  // this head's K and V (N rows of 256 B) as buffers
   const __amdgpu_buffer_rsrc_t rsK = buffer_of(k + (int64_t)h * N * 128, (uint32_t)(N * 256));
   const __amdgpu_buffer_rsrc_t rsV = buffer_of(v + (int64_t)h * N * 128, (uint32_t)(N * 256));
   const uint32_t lK = lds_offset(ringK), lV = lds_offset(ringV);
-  // tile t of the block (first token org, shape sid) from K and from V into
-  // slot b: wave w fills the 1 KB pieces w, w + 8 of each (the same chunks of
-  // the same rows of both)
+  // tile t of the block (base org, shape sid) from K and from V into slot
+  // b: wave w fills the 1 KB pieces w, w + 8 of each (the same chunks of the
+  // same rows of both)
   auto stage = [&](int b, uint32_t org, int sid, int t) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const uint32_t piece = i * 512 + wvu * 64;
-      const uint32_t src = tile_src16(org, sid, t, piece + lane, H, W);
+      const uint32_t src = tile_src<kRelaid>(org, sid, t, piece + lane, H, W);
       dma16(rsK, src, lK + b * kTile + piece * 16);
       dma16(rsV, src, lV + b * kTile + piece * 16);
     }
@@ -313,10 +318,15 @@ bool launch_attn_fwd(const PlanDev& P, const void* q, const void* k, const void*
   if (P.dtype == PRISM_BF16 && P.D == 128) {
     dim3 grid((unsigned)(P.heads * (P.N / kFwdRows))), block(kFwdWaves * 64);
     float c_log2 = (float)(1.4426950408889634 / sqrt(128.0));
-    hipLaunchKernelGGL(k_attn_fwd_bf16, grid, block, 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, P.shape_id, P.zone_base,
-                       P.blk_off, P.blk_org, P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W, P.Z,
-                       P.N, c_log2, (uint16_t*)o, lse);
+    if (P.relayout)
+      hipLaunchKernelGGL(k_attn_fwd_bf16<true>, grid, block, 0, st, (const uint16_t*)q, P.kp,
+                         P.vp, P.shape_id, P.zone_base, P.blk_off, P.blk_start, P.blk_shape,
+                         P.row_ptr, P.col_idx, P.H, P.W, P.Z, P.N, c_log2, (uint16_t*)o, lse);
+    else
+      hipLaunchKernelGGL(k_attn_fwd_bf16<false>, grid, block, 0, st, (const uint16_t*)q,
+                         (const uint16_t*)k, (const uint16_t*)v, P.shape_id, P.zone_base,
+                         P.blk_off, P.blk_org, P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W,
+                         P.Z, P.N, c_log2, (uint16_t*)o, lse);
   } else if (P.dtype == PRISM_F32 && (P.D == 64 || P.D == 128)) {
     dim3 grid((unsigned)(P.heads * (P.N >> 6))), block(64);
     float scale = (float)(1.0 / sqrt((double)P.D));

@@ -155,6 +155,11 @@ struct PlanDev {
   int32_t* qexp;       // [Gmax]
   int32_t* kexp;
   int32_t* blk_org;    // [Gmax]  original token of the block's first row (within head)
+  // stage two's re-layout (relayout): K and V in block-contiguous order, each
+  // row's 16-byte chunks swizzled (chunk c of row p at c ^ chunk_swizzle(p & 63))
+  int relayout;
+  uint16_t* kp;        // [heads][N][128] or null
+  uint16_t* vp;
   // selection
   float* scores;       // [maxblk][maxblk] scratch for one head
   int32_t* row_cnt;    // [Gmax]

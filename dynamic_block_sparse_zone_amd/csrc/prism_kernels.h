@@ -34,7 +34,18 @@ struct BwdDev {
   const void* d_o;
   float* delta;    // [heads][N] rowsum(dO * O)
   float* lse2;     // [heads][N] log2(e) * LSE
+  // with the re-layout: Q, dO, Delta and log2(e) * LSE in block-contiguous
+  // order (rows swizzled as the plan's K and V copies), else null
+  uint16_t* qp;
+  uint16_t* dop;
+  float* delta_p;
+  float* lse2_p;
 };
+// Rows of two [heads][N][128] bf16 tensors (and, when fa is given, of two
+// [heads][N] float columns) into block-contiguous order with swizzled chunks.
+bool launch_relayout(const PlanDev& P, const void* a, const void* b, const float* fa,
+                     const float* fb, uint16_t* ap, uint16_t* bp, float* fap, float* fbp,
+                     hipStream_t st);
 bool launch_bwd_prep(const PlanDev& P, const BwdDev& B, const void* o, const float* lse,
                      hipStream_t st);
 bool launch_bwd_dkdv(const PlanDev& P, const BwdDev& B, void* dk, void* dv, hipStream_t st);

@@ -697,6 +697,37 @@ __global__ __launch_bounds__(512) void k_pool(
   }
 }
 
+// ============================================================ K4b: re-layout
+// Stage two's re-layout (paper.rainbus.top "方法步骤详情", stage two): rows
+// of two [heads][N][128] bf16 tensors copied into block-contiguous order
+// (permuted row p of a head takes its token token_of(p)), each row's 16-byte
+// chunks stored swizzled (chunk c of row p at c ^ chunk_swizzle(p & 63)), so
+// that an attention tile is one contiguous 16 KB run that lands in LDS as
+// it is.  With fa given, two [heads][N] float columns follow the same order.
+// 16 lanes per row (one chunk each), 32 rows per work-group of 512 threads.
+__global__ __launch_bounds__(512) void k_relayout(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+    const float* __restrict__ fa, const float* __restrict__ fb,
+    const uint8_t* __restrict__ shape_id, int H, int W, int Z, int64_t N, int64_t rows,
+    uint16_t* __restrict__ ap, uint16_t* __restrict__ bp, float* __restrict__ fap,
+    float* __restrict__ fbp) {
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 4);
+  if (row >= rows) return;
+  const int c = threadIdx.x & 15;
+  const int h = (int)(row / N);
+  const int64_t p = row - (int64_t)h * N;
+  const int m = (int)(p >> 9);
+  const int64_t src = (int64_t)h * N + token_of(d_shapes[shape_id[(int64_t)h * Z + m]], m,
+                                                (int)(p & 511), H, W);
+  const int dc = c ^ chunk_swizzle((int)(p & 63));
+  *(uint4*)(ap + row * 128 + dc * 8) = *(const uint4*)(a + src * 128 + c * 8);
+  *(uint4*)(bp + row * 128 + dc * 8) = *(const uint4*)(b + src * 128 + c * 8);
+  if (fa && c == 0) {
+    fap[row] = fa[src];
+    fbp[row] = fb[src];
+  }
+}
+
 // ============================================================ K5: block scores
 // s_ij = Qbar_i . Kbar_j / sqrt(D) on the two-level grid x ~ 2^E (hi + 2^-8 lo):
 // the integer dot products I_hh = hi.hi, I_x = hi_i.lo_j + lo_i.hi_j and
@@ -808,6 +839,14 @@ __device__ inline float exp2_taylor_sel(float x) {
   p = __builtin_fmaf(p, f, 1.0f);
   const float r = ldexpf(p, x > -100.0f ? (int)kf : 0);
   return x > -100.0f ? r : 0.0f;
+}
+
+// (u64)(y 2^32) for 0 <= y <= 1 (the exp2 of a non-positive argument): the
+// product is exact and below 2^32 unless y = 1, so a truncating 32-bit
+// conversion gives the same integer
+__device__ inline unsigned long long weight_bits(float y) {
+  const float t = y * 4294967296.0f;
+  return t >= 4294967296.0f ? (1ull << 32) : (unsigned long long)(uint32_t)t;
 }
 
 // softmax weight of a score in 2^-32 units relative to the row maximum
@@ -1275,7 +1314,7 @@ __device__ inline T row_excl_scan(T v, T* sh, T* total) {
 
 // Per query block row (n <= kSelRegMax): the same count, threshold key and
 // tie count as k_select_count, and the row's selection mask (wd words).
-__global__ __launch_bounds__(kSelMT) void k_select_mask(
+__global__ __launch_bounds__(kSelMT) __attribute__((amdgpu_waves_per_eu(4))) void k_select_mask(
     const float* __restrict__ scores, int n, int64_t g0, int k_count, float k_frac, float p,
     int32_t* __restrict__ row_cnt, uint32_t* __restrict__ row_key,
     int32_t* __restrict__ row_tie, unsigned long long* __restrict__ mask, int wd) {
@@ -1322,15 +1361,11 @@ __global__ __launch_bounds__(kSelMT) void k_select_mask(
   for (int e = 0; e < kSelPer; e++) rel[e] -= kmin;
   const uint32_t rlast = f2key(grow[n - 1]) - kmin;
   // integer softmax weight of the element of relative key r (its score is
-  // recovered exactly from the key): weight_of's value.  (kbase is kmin
-  // through an opaque copy, so that the absolute keys are re-formed here
-  // rather than kept alive beside the relative ones.)
-  uint32_t kbase = __builtin_amdgcn_readfirstlane(kmin);
-  asm volatile("" : "+s"(kbase));
-  auto wt = [&](uint32_t r) -> unsigned long long {
-    const float s = key2f(r + kbase);
-    return (unsigned long long)(exp2_taylor_sel((s - smax) * 1.44269504088896340736f) *
-                                4294967296.0f);
+  // recovered exactly from the key, kb = kmin): weight_of's value
+  const uint32_t kbase = __builtin_amdgcn_readfirstlane(kmin);
+  auto wt = [&](uint32_t r, uint32_t kb) -> unsigned long long {
+    const float s = key2f(r + kb);
+    return weight_bits(exp2_taylor_sel((s - smax) * 1.44269504088896340736f));
   };
 
   // one level: histogram of the digits (rel >> lo) & dmask of the
@@ -1348,18 +1383,26 @@ __global__ __launch_bounds__(kSelMT) void k_select_mask(
     const uint32_t dmask = (1u << (hi - lo)) - 1u;
     const uint32_t hmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
     pre &= hmask;
+    // an opaque copy per level: the weights are formed inside the level
+    // rather than hoisted out of the level loop (32 more u64 live)
+    uint32_t kb = kbase;
+    asm volatile("" : "+s"(kb));
 #pragma unroll
     for (int e = 0; e < kSelPer; e++) {
       if ((rel[e] & hmask) == pre) {
+        // (the weight is formed from a copy made here, so that it is not
+        // computed ahead of the test for every element)
+        uint32_t r = rel[e];
+        asm volatile("" : "+v"(r));
         unsigned long long inc = 1ull << kCntShift;
-        if (by_weight) inc += wt(rel[e]);
+        if (by_weight) inc += wt(r, kb);
         atomicAdd(&S.hist[(rel[e] >> lo) & dmask], inc);
       }
     }
     // the padding copies of the last element back out
     if (tid == 0 && npad > 0 && (rlast & hmask) == pre) {
       unsigned long long inc = 1ull << kCntShift;
-      if (by_weight) inc += wt(rlast);
+      if (by_weight) inc += wt(rlast, kb);
       atomicAdd(&S.hist[(rlast >> lo) & dmask], 0ull - (unsigned long long)npad * inc);
     }
     __syncthreads();
@@ -1936,6 +1979,17 @@ bool launch_pool(const PlanDev& P, const void* q, const void* k, hipStream_t st)
   else
     return false;
 #undef PP_ARGS
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_relayout(const PlanDev& P, const void* a, const void* b, const float* fa,
+                     const float* fb, uint16_t* ap, uint16_t* bp, float* fap, float* fbp,
+                     hipStream_t st) {
+  if (!(P.dtype == PRISM_BF16 && P.D == 128)) return false;
+  const int64_t rows = P.heads * P.N;
+  hipLaunchKernelGGL(k_relayout, dim3((unsigned)((rows + 31) / 32)), dim3(512), 0, st,
+                     (const uint16_t*)a, (const uint16_t*)b, fa, fb, P.shape_id, P.H, P.W, P.Z,
+                     P.N, rows, ap, bp, fap, fbp);
   return hipGetLastError() == hipSuccess;
 }
 

@@ -107,6 +107,18 @@ typedef struct {
                              of its 8 frames takes only blocks with b_T <= the largest
                              power of two dividing c (at least 2), and at most 128 tokens
                              when that is 2.  0 (default): fixed 8-frame zones. */
+  int32_t relayout;       /* stage two's re-layout (paper.rainbus.top "方法步骤详情", stage
+                             two), bf16 with head_dim 128: nonzero (default) = the plan
+                             keeps copies of K and V in block-contiguous order, and
+                             prism_attn_bwd copies Q and dO the same way when its
+                             workspace holds them, so that every attention tile is one
+                             contiguous run; 0 = no copies: every tile is gathered from
+                             the caller's tensors through the block -> token map.  The
+                             results are identical; the copies take 2 x heads x N x 256
+                             bytes in the plan's workspace (and the same again, plus 8
+                             bytes per token and head, in the backward's) and make the
+                             attention kernels 2-7 % faster.  With copies the plan holds
+                             K and V as they were at its creation. */
 } prism_config;
 
 /* Opaque plan: block shapes, block table and selected key-block lists of
@@ -167,8 +179,11 @@ void prism_plan_destroy(prism_plan_t* plan);
 prism_status prism_attn_fwd(const prism_plan_t* plan, const void* q, const void* k,
                             const void* v, void* o, float* lse, void* stream);
 
-/* Bytes of device workspace prism_attn_bwd needs (8 per token and head:
- * Delta = rowsum(dO * O) and log2(e) * LSE).  Host-only. */
+/* Bytes of device workspace prism_attn_bwd needs: 8 per token and head
+ * (Delta = rowsum(dO * O) and log2(e) * LSE), and with cfg->relayout (bf16,
+ * head_dim 128) 520 per token and head (also Q, dO and those two columns in
+ * block-contiguous order).  prism_attn_bwd given only the first amount runs
+ * without the copies.  Host-only. */
 prism_status prism_attn_bwd_workspace_size(const prism_config* cfg, size_t* bytes);
 
 /* Backward with the plan held constant: given dO = dL/dO, writes
@@ -194,8 +209,9 @@ prism_status prism_attn_bwd(const prism_plan_t* plan, const void* q, const void*
  * array of PRISM_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
  * runs on until the process ends.  The call allocates nothing (no hipMalloc,
  * no hipFree, no event creation; the stage timing of prism_timing_enable
- * skips it).  Returns PRISM_ENOMEM_WORKSPACE, before any device work, when
- * prism_attn_bwd_workspace_size exceeds the array.  Every call on one GPU
+ * skips it).  It makes no copies of Q and dO (the 8 bytes per token and head
+ * of the columns are all it keeps) and returns PRISM_ENOMEM_WORKSPACE, before
+ * any device work, when those exceed the array.  Every call on one GPU
  * shares that GPU's array: calls that overlap in time on one GPU (two
  * streams, two host threads) race and must not be issued; calls ordered on
  * one stream are safe, since each fully rewrites the scratch it reads. */

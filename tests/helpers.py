@@ -11,6 +11,7 @@ def oracle_config(O, wl, **over):
     kw = dict(top_k=wl.top_k, top_p=wl.top_p, volume_mask=wl.volume_mask,
               fixed_shape=tuple(wl.fixed_shape))
     kw.update(over)
+    kw.pop("relayout", None)  # a memory layout of the kernels, not of the method
     return O.Config(wl.T, wl.H, wl.W, wl.heads, wl.head_dim, **kw)
 
 

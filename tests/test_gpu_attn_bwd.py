@@ -58,6 +58,7 @@ def test_bwd_full(prism, orc):
     {"fixed_shape": (4, 4, 8)},
     {"top_p": 0.0, "top_k": 2},
     {"top_p": 1.0},
+    {"relayout": False},           # every tile gathered through the block -> token map
 ])
 def test_bwd_variants(prism, orc, over):
     wl, x, pl, grads = run_bwd(prism, "bwdcheck", **over)

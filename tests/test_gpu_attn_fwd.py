@@ -71,6 +71,7 @@ def test_fwd_small_bf16_sampled(prism, orc):
     {"fixed_shape": (4, 4, 8)},
     {"volume_mask": 1},              # all blocks of 64 (pairs of query blocks per unit)
     {"top_k_frac": 0.05, "top_p": 0.2},
+    {"relayout": False},             # every tile gathered through the block -> token map
 ])
 def test_fwd_variants(prism, orc, over):
     wl, pl, g, r, gl, rl = run_fwd(prism, orc, "check", **over)

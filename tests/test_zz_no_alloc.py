@@ -3,7 +3,9 @@ cannot allocate: its scratch is the library's static per-GPU array), against
 the backward with a caller workspace, prism_attn_bwd, through the C ABI.
 
 Both run the same deterministic kernels, so the gradients must agree bit for
-bit (stricter than the bf16 bar).  Two calls in a row, the second on a
+bit (stricter than the bf16 bar); the workspace backward streams re-laid
+copies of Q and dO while the allocation-free one gathers them, so this also
+holds the two layouts to the same bits.  Two calls in a row, the second on a
 smaller problem, show that the shared array carries nothing from one call to
 the next; a problem whose scratch exceeds the array is rejected before any
 device work, leaving the outputs untouched."""
@@ -49,7 +51,9 @@ def test_noalloc_rejects_problems_beyond_the_array(prism):
     from dynamic_block_sparse_zone_amd import _native as nat
 
     def need(heads):
-        cfg = prism.make_config(64, 128, 128, heads, 128, torch.bfloat16)
+        # the no-allocation backward keeps only the Delta / LSE columns: the
+        # workspace of a configuration without the re-laid copies
+        cfg = prism.make_config(64, 128, 128, heads, 128, torch.bfloat16, relayout=False)
         n = ctypes.c_size_t()
         nat.check(nat.lib().prism_attn_bwd_workspace_size(ctypes.byref(cfg), ctypes.byref(n)),
                   "prism_attn_bwd_workspace_size")
