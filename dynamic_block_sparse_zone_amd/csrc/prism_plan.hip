@@ -732,9 +732,8 @@ __global__ __launch_bounds__(512) void k_relayout(
 // s_ij = Qbar_i . Kbar_j / sqrt(D) on the two-level grid x ~ 2^E (hi + 2^-8 lo):
 // the integer dot products I_hh = hi.hi, I_x = hi_i.lo_j + lo_i.hi_j and
 // I_ll = lo.lo are exact on the bf16 MFMA (every partial sum is an integer
-// below 2^24), J = 2^16 I_hh + 2^8 I_x + I_ll is formed exactly in int64, and
-// s = fl32(fl32(J) 2^(Ei + Ej - 16)) * fl(1/sqrt D), J rounded once (it is
-// exact in fp64).  A block of 256 threads covers 128 x 128 scores, each wave
+// below 2^24), J = 2^16 I_hh + 2^8 I_x + I_ll is formed exactly (in fp64),
+// and s = fl32(fl32(J) 2^(Ei + Ej - 16)) * fl(1/sqrt D), J rounded once.  A block of 256 threads covers 128 x 128 scores, each wave
 // 64 x 64 as two 32-row halves.
 template <int D>
 __global__ __launch_bounds__(256) void k_block_scores(
@@ -785,9 +784,13 @@ __global__ __launch_bounds__(256) void k_block_scores(
       for (int r = 0; r < 16; r++) {
         const int i = i0 + a * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
         if (i < n) {
-          const int64_t J = (int64_t)hh[b][r] * 65536 + (int64_t)hx[b][r] * 256 +
-                            (int64_t)ll[b][r];
-          const float s = ldexpf((float)(double)J, qexp[g0 + i] + ej - 16) * cD;
+          // J = 2^16 I_hh + 2^8 I_x + I_ll: each product is an integer below
+          // 2^25 held exactly in fp32, and |J| < 2^42, so the fp64 sum is J
+          // exactly and is rounded once to fp32
+          const double J = __builtin_fma((double)hh[b][r], 65536.0,
+                                         __builtin_fma((double)hx[b][r], 256.0,
+                                                       (double)ll[b][r]));
+          const float s = ldexpf((float)J, qexp[g0 + i] + ej - 16) * cD;
           scores[(int64_t)i * n + j] = (s == 0.0f) ? 0.0f : s;
         }
       }
@@ -1258,9 +1261,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select_fill(
 // t + kSelMT e (e < kSelPer) as order keys relative to the row's smallest
 // key (a score is recovered exactly from its key, so the integer softmax
 // weight is formed from it where needed, as weight_of forms it).  Slots past the
-// row's end hold copies of its last element (so no per-element test is
-// needed): they leave the row's extremes alone, every histogram takes their
-// count and weight off the digit of that element, and the mask drops their
+// row's end hold copies of its last element: they leave the row's extremes
+// alone, the histogram passes skip them (they fill the slabs past
+// n / kSelMT, a uniform test, and part of one slab), and the mask drops their
 // bits; in index order they come after every real element.  The selects take 11-bit digits from the top of the row's key range; a level's
 // histogram packs count << 47 | integer weight per digit into one u64 (a row
 // of at most 16384 blocks has fewer than 2^15 elements and a weight total
@@ -1278,19 +1281,23 @@ constexpr int kSelQ = kSelBins / kSelMT;         // digits per thread in the sca
 constexpr int kCntShift = 47;
 constexpr unsigned long long kWtMask = (1ull << kCntShift) - 1ull;
 
+// The levels alternate between two histograms (and scan / result slots):
+// a level clears the other one while it fills its own, so a level takes
+// three barriers.
 struct SelSharedR {
-  unsigned long long hist[kSelBins];
-  unsigned long long wsum[kSelMW];
-  unsigned long long above, wstar;
-  int pick;
+  unsigned long long hist[2][kSelBins];
+  unsigned long long wsum[2][kSelMW];
+  unsigned long long above[2], fallback[2], wstar;
+  int pick[2];
   uint32_t kmin[kSelMW], kmax[kSelMW];
   int isum[kSelMW];
   int trank[kSelPer * kSelMW];
 };
 
 // exclusive scan over a kSelMT-thread block of one value per thread, and the
-// block total
-template <typename T>
+// block total; without `reuse` the trailing barrier is left out (the caller
+// does not write `sh` again before a later barrier)
+template <typename T, bool reuse = true>
 __device__ inline T row_excl_scan(T v, T* sh, T* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   T x = v;
@@ -1307,7 +1314,7 @@ __device__ inline T row_excl_scan(T v, T* sh, T* total) {
     before += w < wv ? sh[w] : (T)0;
     tot += sh[w];
   }
-  __syncthreads();
+  if (reuse) __syncthreads();
   *total = tot;
   return before + x - v;
 }
@@ -1328,7 +1335,9 @@ __global__ __launch_bounds__(kSelMT) __attribute__((amdgpu_waves_per_eu(4))) voi
   // the row, 2 KB per slab (coalesced), as order keys; slots past its end
   // copy element n - 1
   const float* grow = scores + (int64_t)i * n;
-  const int npad = kSelRegMax - n;  // copies of the last element
+  // slabs 0 .. nfull - 1 are whole; slab nfull holds the lanes tid < n % kSelMT
+  const int nfull = __builtin_amdgcn_readfirstlane(n / kSelMT);
+  const bool tail = tid < n % kSelMT;
   uint32_t rel[kSelPer];
 #pragma unroll
   for (int e = 0; e < kSelPer; e++) rel[e] = f2key(grow[min(tid + e * kSelMT, n - 1)]);
@@ -1348,6 +1357,10 @@ __global__ __launch_bounds__(kSelMT) __attribute__((amdgpu_waves_per_eu(4))) voi
     S.kmin[wv] = kmn;
     S.kmax[wv] = kmx;
   }
+  // the first level's histogram and result slot start clear
+#pragma unroll
+  for (int q = 0; q < kSelQ; q++) S.hist[0][tid + q * kSelMT] = 0ull;
+  if (tid == 0) S.pick[0] = -1;
   __syncthreads();
   uint32_t kmin = S.kmin[0], kmax = S.kmax[0];
 #pragma unroll
@@ -1359,7 +1372,6 @@ __global__ __launch_bounds__(kSelMT) __attribute__((amdgpu_waves_per_eu(4))) voi
   const uint32_t span = kmax - kmin;
 #pragma unroll
   for (int e = 0; e < kSelPer; e++) rel[e] -= kmin;
-  const uint32_t rlast = f2key(grow[n - 1]) - kmin;
   // integer softmax weight of the element of relative key r (its score is
   // recovered exactly from the key, kb = kmin): weight_of's value
   const uint32_t kbase = __builtin_amdgcn_readfirstlane(kmin);
@@ -1369,17 +1381,19 @@ __global__ __launch_bounds__(kSelMT) __attribute__((amdgpu_waves_per_eu(4))) voi
   };
 
   // one level: histogram of the digits (rel >> lo) & dmask of the
-  // candidates (the bits of rel from hi up equal those of `pre`), then the digit, from the top, at which
-  // the running total (weight, else count) first reaches `need` (digit 0
-  // if none does), with the packed totals of the larger digits.  With p32
-  // the target is the Top-p weight W*, formed from the level's total.
-  auto level = [&](int hi, int lo, uint32_t pre, bool by_weight,
+  // candidates (the bits of rel from hi up equal those of `pre`; every
+  // element when `all`), then the digit, from the top, at which the running
+  // total (weight, else count) first reaches `need` (digit 0 if none does),
+  // with the packed totals of the larger digits.  With p32 the target is the
+  // Top-p weight W*, formed from the level's total.  hist[cur] is clear on
+  // entry; hist[cur ^ 1] is cleared for the next level.
+  int cur = 0;
+  auto level = [&](int hi, int lo, uint32_t pre, bool all, bool by_weight,
                    unsigned long long need, unsigned long long p32,
                    unsigned long long* above) -> int {
+    unsigned long long* H = S.hist[cur];
 #pragma unroll
-    for (int q = 0; q < kSelQ; q++) S.hist[tid + q * kSelMT] = 0ull;
-    if (tid == 0) S.pick = -1;
-    __syncthreads();
+    for (int q = 0; q < kSelQ; q++) S.hist[cur ^ 1][tid + q * kSelMT] = 0ull;
     const uint32_t dmask = (1u << (hi - lo)) - 1u;
     const uint32_t hmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
     pre &= hmask;
@@ -1387,34 +1401,36 @@ __global__ __launch_bounds__(kSelMT) __attribute__((amdgpu_waves_per_eu(4))) voi
     // rather than hoisted out of the level loop (32 more u64 live)
     uint32_t kb = kbase;
     asm volatile("" : "+s"(kb));
+    // (each weight is formed from a copy made at its use, so that it is not
+    // computed ahead for every element)
+    auto add = [&](uint32_t r) {
+      asm volatile("" : "+v"(r));
+      unsigned long long inc = 1ull << kCntShift;
+      if (by_weight) inc += wt(r, kb);
+      atomicAdd(&H[(r >> lo) & dmask], inc);
+    };
+    // slabs past the row's end (whole slabs of padding copies: a uniform
+    // branch) are skipped, and in the one partial slab only the lanes before
+    // the end take part
 #pragma unroll
     for (int e = 0; e < kSelPer; e++) {
-      if ((rel[e] & hmask) == pre) {
-        // (the weight is formed from a copy made here, so that it is not
-        // computed ahead of the test for every element)
-        uint32_t r = rel[e];
-        asm volatile("" : "+v"(r));
-        unsigned long long inc = 1ull << kCntShift;
-        if (by_weight) inc += wt(r, kb);
-        atomicAdd(&S.hist[(rel[e] >> lo) & dmask], inc);
-      }
-    }
-    // the padding copies of the last element back out
-    if (tid == 0 && npad > 0 && (rlast & hmask) == pre) {
-      unsigned long long inc = 1ull << kCntShift;
-      if (by_weight) inc += wt(rlast, kb);
-      atomicAdd(&S.hist[(rlast >> lo) & dmask], 0ull - (unsigned long long)npad * inc);
+      if (e > nfull) break;
+      if (e == nfull && !tail) continue;
+      if (all || (rel[e] & hmask) == pre) add(rel[e]);
     }
     __syncthreads();
+    // every thread has read the previous level's result slot
+    if (tid == 0) S.pick[cur ^ 1] = -1;
     // thread t owns the digits kSelBins - 1 - kSelQ t - q, in selection order
     unsigned long long v[kSelQ], sum = 0;
 #pragma unroll
     for (int q = 0; q < kSelQ; q++) {
-      v[q] = S.hist[kSelBins - 1 - kSelQ * tid - q];
+      v[q] = H[kSelBins - 1 - kSelQ * tid - q];
       sum += v[q];
     }
     unsigned long long total;
-    unsigned long long run = row_excl_scan<unsigned long long>(sum, S.wsum, &total);
+    unsigned long long run =
+        row_excl_scan<unsigned long long, false>(sum, S.wsum[cur], &total);
     if (p32) {
       const unsigned long long Z = total & kWtMask;
       const unsigned long long zh = Z >> 32, zl = Z & 0xffffffffull;
@@ -1426,20 +1442,22 @@ __global__ __launch_bounds__(kSelMT) __attribute__((amdgpu_waves_per_eu(4))) voi
       const unsigned long long before = by_weight ? (run & kWtMask) : (run >> kCntShift);
       const unsigned long long m = by_weight ? (v[q] & kWtMask) : (v[q] >> kCntShift);
       if (before < need && before + m >= need) {
-        S.pick = kSelBins - 1 - kSelQ * tid - q;
-        S.above = run;
+        S.pick[cur] = kSelBins - 1 - kSelQ * tid - q;
+        S.above[cur] = run;
       }
+      // (the totals above digit 0, the answer when no digit reaches need)
+      if (kSelBins - 1 - kSelQ * tid - q == 0) S.fallback[cur] = run;
       run += v[q];
     }
     __syncthreads();
-    int d = S.pick;
+    int d = S.pick[cur];
     if (d < 0) {
       d = 0;
-      *above = total - S.hist[0];
+      *above = S.fallback[cur];
     } else {
-      *above = S.above;
+      *above = S.above[cur];
     }
-    __syncthreads();
+    cur ^= 1;
     return d;
   };
   // exact select: the order key at which the running total in selection
@@ -1454,7 +1472,7 @@ __global__ __launch_bounds__(kSelMT) __attribute__((amdgpu_waves_per_eu(4))) voi
       const int lo = hi > kSelBits ? hi - kSelBits : 0;
       const unsigned long long done = by_weight ? (ab & kWtMask) : (ab >> kCntShift);
       unsigned long long a;
-      const int d = level(hi, lo, prefix, by_weight, need - done,
+      const int d = level(hi, lo, prefix, first, by_weight, need - done,
                           first ? p32 : 0ull, &a);
       if (first && p32) need = S.wstar;
       first = false;
