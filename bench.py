@@ -286,6 +286,28 @@ def parse():
     return ap.parse_args()
 
 
+def dense_mfma_probe(dev, n=8192, reps=20):
+    """A dense reference for the attention rates: a plain bf16 n x n x n
+    matrix product through torch (the ROCm GEMM library) on the same GPU,
+    timed with events after a warm-up; TFLOP/s."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    for _ in range(5):
+        torch.mm(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
 def cpu_baseline(wl, x, nblocks, threads, step_flops):
     """The oracle as it is, timed on a bounded sample of the same workload:
     the plan of head 0 up to the pooled block means (zone statistics, shapes,
@@ -485,12 +507,20 @@ def main():
     es = 2 if wl.dtype == "bf16" else 4
     tensor_bytes = wl.heads * wl.N * D * es
     plan_ms = sum(v for s, v in ms.items() if s.startswith("plan."))
+    import numpy as np
     nblk2 = None
+    si_mean = si_max = None
     try:
         off = last.export("blk_off")
         nblk2 = float(sum((off[h + 1] - off[h]) ** 2 for h in range(wl.heads)))
+        rows = np.diff(last.export("row_ptr")[: int(off[wl.heads]) + 1])
+        si_mean, si_max = float(rows.mean()), int(rows.max())
     except Exception:
         pass
+    # the dense reference (outside the timed steps)
+    dense_tf = dense_mfma_probe(dev)
+    print(f"[bench] dense bf16 GEMM reference: {dense_tf:.1f} TFLOP/s", file=sys.stderr,
+          flush=True)
     out = {
         "metric": "selected-block attn TFLOP/s (% bf16 MFMA peak) + ms/layer fwd+bwd, N≈1M tok",
         "value": round(value, 2),
@@ -538,6 +568,12 @@ def main():
         "density": round(info["nnz"] / nblk2, 4) if nblk2 else None,
         "total_blocks": info["total_blocks"],
         "shape_hist": info["shape_hist"],
+        "selected_blocks_per_row": {"mean": round(si_mean, 1) if si_mean else None,
+                                    "max": si_max},
+        "dense_mfma_ref": {"what": "torch.mm bf16 8192x8192x8192 on the same GPU",
+                           "tflops": round(dense_tf, 1),
+                           "attn_frac_of_it": round(value / dense_tf, 4),
+                           "dominant_kernel_frac_of_it": round(achieved / dense_tf, 4)},
         "wall_s": round(wall, 2),
     }
     if args.calib_copy:
