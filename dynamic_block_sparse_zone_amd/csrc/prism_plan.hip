@@ -736,7 +736,7 @@ __global__ __launch_bounds__(512) void k_relayout(
 // and s = fl32(fl32(J) 2^(Ei + Ej - 16)) * fl(1/sqrt D), J rounded once.  A block of 256 threads covers 128 x 128 scores, each wave
 // 64 x 64 as two 32-row halves.
 template <int D>
-__global__ __launch_bounds__(256) void k_block_scores(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_block_scores(
     const uint16_t* __restrict__ qgrid, const uint16_t* __restrict__ kgrid,
     const uint16_t* __restrict__ qlo, const uint16_t* __restrict__ klo,
     const int32_t* __restrict__ qexp, const int32_t* __restrict__ kexp, int64_t g0, int n,
@@ -750,35 +750,31 @@ __global__ __launch_bounds__(256) void k_block_scores(
     if (row < n) u = *(const uint4*)(base + (g0 + row) * D + kk * 16 + hl * 8);
     return __builtin_bit_cast(bf16x8, u);
   };
+  // one 32 x 32 tile at a time (48 accumulator registers, so that four waves
+  // fit a SIMD; the tile's Q and K fragments come from L2)
 #pragma unroll
-  for (int a = 0; a < 2; a++) {
-    f32x16 hh[2], hx[2], ll[2];
-#pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        hh[b][r] = 0.0f;
-        hx[b][r] = 0.0f;
-        ll[b][r] = 0.0f;
-      }
-    const int ia = i0 + a * 32 + l32;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; kk++) {
-      const bf16x8 qh = frag(qgrid, ia, kk), ql = frag(qlo, ia, kk);
-#pragma unroll
-      for (int b = 0; b < 2; b++) {
-        const int jb = j0 + b * 32 + l32;
-        const bf16x8 kh = frag(kgrid, jb, kk), kl = frag(klo, jb, kk);
-        hh[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kh, hh[b], 0, 0, 0);
-        hx[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kl, hx[b], 0, 0, 0);
-        hx[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kh, hx[b], 0, 0, 0);
-        ll[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kl, ll[b], 0, 0, 0);
-      }
-    }
+  for (int a = 0; a < 2; a++)
 #pragma unroll
     for (int b = 0; b < 2; b++) {
-      const int j = j0 + b * 32 + l32;
-      if (j >= n) continue;
+      f32x16 hh, hx, ll;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        hh[r] = 0.0f;
+        hx[r] = 0.0f;
+        ll[r] = 0.0f;
+      }
+      const int ia = i0 + a * 32 + l32, jb = j0 + b * 32 + l32;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; kk++) {
+        const bf16x8 qh = frag(qgrid, ia, kk), ql = frag(qlo, ia, kk);
+        const bf16x8 kh = frag(kgrid, jb, kk), kl = frag(klo, jb, kk);
+        hh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kh, hh, 0, 0, 0);
+        hx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kl, hx, 0, 0, 0);
+        hx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kh, hx, 0, 0, 0);
+        ll = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kl, ll, 0, 0, 0);
+      }
+      if (jb >= n) continue;
+      const int j = jb;
       const int ej = kexp[g0 + j];
 #pragma unroll
       for (int r = 0; r < 16; r++) {
@@ -787,15 +783,13 @@ __global__ __launch_bounds__(256) void k_block_scores(
           // J = 2^16 I_hh + 2^8 I_x + I_ll: each product is an integer below
           // 2^25 held exactly in fp32, and |J| < 2^42, so the fp64 sum is J
           // exactly and is rounded once to fp32
-          const double J = __builtin_fma((double)hh[b][r], 65536.0,
-                                         __builtin_fma((double)hx[b][r], 256.0,
-                                                       (double)ll[b][r]));
+          const double J = __builtin_fma((double)hh[r], 65536.0,
+                                         __builtin_fma((double)hx[r], 256.0, (double)ll[r]));
           const float s = ldexpf((float)J, qexp[g0 + i] + ej - 16) * cD;
           scores[(int64_t)i * n + j] = (s == 0.0f) ? 0.0f : s;
         }
       }
     }
-  }
 }
 
 // ============================================================ K6: selection
