@@ -1,10 +1,11 @@
 """Selection over block-score rows longer than the 16,384 entries the
-selection kernels stage in LDS: one head of 64 x 128 x 136 tokens with
-64-token blocks only, 17,408 key blocks per row, where the rows are selected
-from global memory by the same exact radix select (xyznot.com/id "Metode" 3:
-S_i = TopK(P_i, k) U TopP(P_i, p)).  Every CSR row is compared bit for bit
-with the oracle, the key-major transpose is checked to be exactly its
-transpose, and two sampled query blocks go through the forward."""
+register selection holds: one head of 64 x 128 x 136 tokens with 64-token
+blocks only, 17,408 key blocks per row, where the rows are selected from
+global memory by the exact radix select (xyznot.com/id "Metode" 3:
+S_i = TopK(P_i, k) U TopP(P_i, p)) and their masks are built from the lists.
+Every CSR row is compared bit for bit with the oracle, the key-major
+transpose (built from those masks) is checked to be exactly its transpose,
+and two sampled query blocks go through the forward."""
 import os
 
 import numpy as np
