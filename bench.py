@@ -115,6 +115,71 @@ def summarize_hbm_table(fetch_csv, write_csv, workload, cmds, out):
     print("\n".join(lines))
 
 
+STALL_COUNTERS_A = ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+                    "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                    "SQ_VALU_MFMA_COEXEC_CYCLES"]
+STALL_COUNTERS_B = ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                    "SQ_INSTS_LDS", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_BUSY_CYCLES",
+                    "SQ_LDS_DATA_FIFO_FULL"]
+
+
+def _longest_dispatch_counters(path, names):
+    """{kernel: {counter: value}} of each attention kernel's longest dispatch
+    (the full-size launch) in a counter-collection CSV."""
+    import csv
+    vals, dur = {}, {}
+    for r in csv.DictReader(open(path)):
+        k = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("prism::", "")
+        if not any(k.startswith(s) for s, _ in KERNELS.values()):
+            continue
+        key = (k, r["Dispatch_Id"])
+        if r["Counter_Name"] in names:
+            d = vals.setdefault(key, {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        dur[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    best = {}
+    for key in vals:
+        if key[0] not in best or dur[key] > dur[best[key[0]]]:
+            best[key[0]] = key
+    return {k: vals[v] for k, v in best.items()}
+
+
+def summarize_stalls(csv_a, csv_b, workload, cmds, out):
+    """Where the attention kernels' wave time goes, from two SQ counter
+    passes: waiting at waitcnt / barriers, waiting to issue, issuing (VALU,
+    LDS, with MFMA co-execution), and LDS bank conflicts."""
+    a = _longest_dispatch_counters(csv_a, STALL_COUNTERS_A)
+    b = _longest_dispatch_counters(csv_b, STALL_COUNTERS_B)
+    lines = [f"# Where the attention kernels' wave time goes, {workload}", "",
+             "Two SQ counter passes over one profiled step, the full-size dispatch of each "
+             "kernel.  Fractions are of SQ_WAVE_CYCLES (wave-cycles resident): waiting at a "
+             "waitcnt or barrier (SQ_WAIT_ANY), waiting to issue (SQ_WAIT_INST_ANY: "
+             "dependencies, a busy matrix core), issuing (SQ_ACTIVE_INST_ANY; of which VALU "
+             "and LDS), and cycles where VALU and MFMA execute together "
+             "(SQ_VALU_MFMA_COEXEC_CYCLES).  Bank conflicts are cycles over LDS-active cycles.",
+             "", "Commands (from /tmp, TMPDIR=/tmp):", "", *[f"    {c}" for c in cmds], "",
+             "| kernel | waiting (waitcnt, barrier) | waiting to issue | issuing | VALU issuing "
+             "| LDS issuing | VALU with MFMA | LDS bank conflict | VALU instr / MFMA "
+             "| LDS instr / MFMA |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for k in sorted(a):
+        A, B = a[k], b.get(k, {})
+        wc = A["SQ_WAVE_CYCLES"]
+        fr = [A[n] / wc for n in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                                  "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                                  "SQ_VALU_MFMA_COEXEC_CYCLES")]
+        bank = B["SQ_LDS_BANK_CONFLICT"] / max(B["SQ_LDS_IDX_ACTIVE"], 1.0) if B else float("nan")
+        mf = B.get("SQ_INSTS_MFMA", 0.0)
+        vpm = (B["SQ_INSTS_VALU"] - mf) / mf if mf else float("nan")
+        lpm = B["SQ_INSTS_LDS"] / mf if mf else float("nan")
+        lines.append(f"| `{k}` | " + " | ".join(f"{100 * x:.1f} %" for x in fr) +
+                     f" | {100 * bank:.2f} % | {vpm:.2f} | {lpm:.2f} |")
+    lines.append("")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def summarize_mfma(csv_path, agent_csv, workload, cmds, out):
     """MFMA utilisation of the attention kernels from one counter pass of
     SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16."""
@@ -281,6 +346,9 @@ def parse():
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_CSV", "AGENT_CSV"),
                     help="write the attention kernels' MFMA utilisation summary from one "
                          "rocprofv3 counter pass (and its agent info), then exit")
+    ap.add_argument("--summarize-stalls", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"),
+                    help="write where the attention kernels' wave time goes from two SQ "
+                         "counter passes, then exit")
     ap.add_argument("--cmd", action="append", default=[],
                     help="profiling command lines to record in the summary")
     return ap.parse_args()
@@ -370,6 +438,10 @@ def main():
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.workload, args.cmd,
                         os.path.join(ROOT, "profiles", f"{args.workload}_kernel_trace.md"))
+        return
+    if args.summarize_stalls:
+        summarize_stalls(*args.summarize_stalls, args.workload, args.cmd,
+                         os.path.join(ROOT, "profiles", f"attention_{args.workload}_stalls.md"))
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, args.workload, args.cmd,

@@ -106,3 +106,30 @@ def test_mfma_summary_uses_the_xcd_count(tmp_path):
     row = [l for l in out.read_text().splitlines() if "k_attn_fwd_bf16" in l][0]
     cells = [c.strip() for c in row.strip("|").split("|")]
     assert cells[2] == "2.00" and cells[3] == "50.0" and cells[4] == "500.0"
+
+
+def test_stall_summary_takes_each_kernels_longest_dispatch(tmp_path):
+    """The stall table reads the full-size dispatch (the longest) of each
+    attention kernel and gives fractions of the resident wave-cycles."""
+    rows_a, rows_b = [], []
+    for dur, scale in ((100, 1.0), (10**6, 10.0)):   # a warm-up dispatch, then the launch
+        for n, v in zip(bench.STALL_COUNTERS_A, (1000, 300, 200, 10, 500, 250, 40, 100)):
+            rows_a.append(("prism::k_bwd_dkdv<true>(int)", n, v * scale, 0, dur))
+        for n, v in zip(bench.STALL_COUNTERS_B, (5, 0, 500, 150, 500, 100, 1000, 0)):
+            rows_b.append(("prism::k_bwd_dkdv<true>(int)", n, v * scale, 0, dur))
+    for path, rows in (("a.csv", rows_a), ("b.csv", rows_b)):
+        with open(tmp_path / path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value",
+                                              "Start_Timestamp", "End_Timestamp", "Dispatch_Id"])
+            w.writeheader()
+            for i, r in enumerate(rows):
+                w.writerow({"Kernel_Name": r[0], "Counter_Name": r[1], "Counter_Value": r[2],
+                            "Start_Timestamp": r[3], "End_Timestamp": r[4],
+                            "Dispatch_Id": 1 if r[4] == 100 else 2})
+    out = tmp_path / "s.md"
+    bench.summarize_stalls(str(tmp_path / "a.csv"), str(tmp_path / "b.csv"), "wl", [], str(out))
+    row = [l for l in out.read_text().splitlines() if l.startswith("| `k_bwd_dkdv")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[1:4] == ["30.0 %", "20.0 %", "50.0 %"]
+    assert cells[7] == "1.00 %"          # 5 of 500 LDS-active cycles
+    assert cells[8] == "4.00"            # (500 - 100) VALU per 100 MFMA
