@@ -346,6 +346,8 @@ def parse():
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_CSV", "AGENT_CSV"),
                     help="write the attention kernels' MFMA utilisation summary from one "
                          "rocprofv3 counter pass (and its agent info), then exit")
+    ap.add_argument("--utilisation", action="store_true",
+                    help="also report the forward's wave utilisation on two heads of the plan")
     ap.add_argument("--summarize-stalls", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"),
                     help="write where the attention kernels' wave time goes from two SQ "
                          "counter passes, then exit")
@@ -374,6 +376,34 @@ def dense_mfma_probe(dev, n=8192, reps=20):
     ms = e0.elapsed_time(e1) / reps
     del a, b
     return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
+def wave_utilisation(pl, wl, heads):
+    """The share of ring steps in which a forward (or dQ) wave computes, from
+    the plan itself: a work-group of 256 query rows walks the union of its
+    query blocks' key lists, 64 rows a step, and each of its 8 waves (32 rows
+    of one block) computes only the tiles of its own block's list.  Per head
+    listed: sum over waves of their tiles / (8 x the tiles of the union)."""
+    import numpy as np
+    vol_of = np.array([64] * 7 + [128] * 6 + [256] * 3)
+    off, rp, col = pl.export("blk_off"), pl.export("row_ptr"), pl.export("col_idx")
+    start, sid = pl.export("blk_start"), pl.export("shape_id")
+    z = wl.N // 512
+    out = {}
+    for h in heads:
+        o0, o1 = int(off[h]), int(off[h + 1])
+        st = start[o0:o1].astype(np.int64)
+        vol = vol_of[sid[h * z + (st >> 9)]]
+        tiles = vol // 64
+        units = st // 256
+        work = union = 0
+        for u in np.unique(units):
+            blocks = np.nonzero(units == u)[0]
+            lists = [col[rp[o0 + b]:rp[o0 + b + 1]] for b in blocks]
+            union += 8 * int(tiles[np.unique(np.concatenate(lists))].sum())
+            work += sum((int(vol[b]) // 32) * int(tiles[l].sum()) for b, l in zip(blocks, lists))
+        out[h] = round(work / union, 4) if union else None
+    return out
 
 
 def cpu_baseline(wl, x, nblocks, threads, step_flops):
@@ -589,6 +619,10 @@ def main():
         si_mean, si_max = float(rows.mean()), int(rows.max())
     except Exception:
         pass
+    util = None
+    if args.utilisation:
+        util = wave_utilisation(last, wl, (0, wl.heads // 2))
+        print(f"[bench] forward wave utilisation {util}", file=sys.stderr, flush=True)
     # the dense reference (outside the timed steps)
     dense_tf = dense_mfma_probe(dev)
     print(f"[bench] dense bf16 GEMM reference: {dense_tf:.1f} TFLOP/s", file=sys.stderr,
@@ -640,6 +674,7 @@ def main():
         "density": round(info["nnz"] / nblk2, 4) if nblk2 else None,
         "total_blocks": info["total_blocks"],
         "shape_hist": info["shape_hist"],
+        "fwd_wave_utilisation": util,
         "selected_blocks_per_row": {"mean": round(si_mean, 1) if si_mean else None,
                                     "max": si_max},
         "dense_mfma_ref": {"what": "torch.mm bf16 8192x8192x8192 on the same GPU",

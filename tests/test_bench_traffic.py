@@ -133,3 +133,24 @@ def test_stall_summary_takes_each_kernels_longest_dispatch(tmp_path):
     assert cells[1:4] == ["30.0 %", "20.0 %", "50.0 %"]
     assert cells[7] == "1.00 %"          # 5 of 500 LDS-active cycles
     assert cells[8] == "4.00"            # (500 - 100) VALU per 100 MFMA
+
+
+def test_wave_utilisation_counts_idle_waves():
+    """One 256-row unit of four 64-token query blocks whose lists are {0, 1},
+    {0}, {} and {1} (64-token key blocks): the unit steps through 2 tiles with
+    8 waves (16 wave-steps) and its waves compute 4 + 2 + 0 + 2 of them."""
+    import numpy as np
+
+    class FakePlan:
+        arrays = {"blk_off": np.array([0, 4]), "row_ptr": np.array([0, 2, 3, 3, 4]),
+                  "col_idx": np.array([0, 1, 0, 1]), "blk_start": np.array([0, 64, 128, 192]),
+                  "shape_id": np.array([0], dtype=np.uint8)}
+
+        def export(self, name):
+            return self.arrays[name]
+
+    class Wl:
+        N = 512
+        heads = 1
+
+    assert bench.wave_utilisation(FakePlan(), Wl(), (0,)) == {0: 0.5}
