@@ -88,6 +88,8 @@ def test_hbm_table_rates(tmp_path):
     # time 1000 ms, fetch and write 1.00 GB each, 0.002 TB/s
     assert float(cells[2]) == pytest.approx(1000.0)
     assert cells[3] == "1.00" and cells[4] == "1.00" and cells[5] == "0.00"
+    # the copy moves 2 GiB in 1 ms: 2.15 TB/s, of which 0.002 TB/s is 0.1 %
+    assert "2.15 TB/s" in out.read_text() and cells[7] == "0.1"
 
 
 def test_mfma_summary_uses_the_xcd_count(tmp_path):
