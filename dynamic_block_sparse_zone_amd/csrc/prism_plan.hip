@@ -1149,31 +1149,42 @@ __global__ __launch_bounds__(kSelThreads) void k_select_count(
 }
 
 // Exclusive scan of a head's row counts into row_ptr (base = running total in
-// counters[0]); one block of 1024 threads.
+// counters[0]); one block of 1024 threads, each taking a contiguous segment:
+// its sum, one block scan of the sums, then the segment's pointers.
 __global__ __launch_bounds__(1024) void k_scan_rows(const int32_t* __restrict__ cnt, int n,
                                                     int64_t g0, int64_t* __restrict__ ptr,
                                                     int64_t* __restrict__ counters,
                                                     int last) {
-  __shared__ int64_t sh[1024];
-  int64_t carry = counters[0];
-  for (int i0 = 0; i0 < n; i0 += 1024) {
-    int i = i0 + threadIdx.x;
-    int64_t v = i < n ? cnt[g0 + i] : 0;
-    sh[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      int64_t a = threadIdx.x >= off ? sh[threadIdx.x - off] : 0;
-      __syncthreads();
-      sh[threadIdx.x] += a;
-      __syncthreads();
-    }
-    if (i < n) ptr[g0 + i] = carry + sh[threadIdx.x] - v;
-    carry += sh[1023];
-    __syncthreads();
+  __shared__ int64_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (n + 1023) / 1024;
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  int64_t s = 0;
+  for (int i = i0; i < i1; i++) s += cnt[g0 + i];
+  int64_t x = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t u = __shfl_up(x, off, 64);
+    if (lane >= off) x += u;
   }
-  if (threadIdx.x == 0) {
-    counters[0] = carry;
-    if (last) ptr[g0 + n] = carry;
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  int64_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; w++) {
+    before += w < wv ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  const int64_t base = counters[0];
+  int64_t run = base + before + x - s;
+  for (int i = i0; i < i1; i++) {
+    ptr[g0 + i] = run;
+    run += cnt[g0 + i];
+  }
+  __syncthreads();  // every thread has read counters[0]
+  if (tid == 0) {
+    counters[0] = base + total;
+    if (last) ptr[g0 + n] = base + total;
   }
 }
 
@@ -1716,23 +1727,42 @@ __global__ __launch_bounds__(256) void k_mask_tr(
 
 // per column: turn the row-tile counts into output positions relative to the
 // column's start (at most n, so they fit in 32 bits at any nnz), the
-// column's total, and its cost B_j * sum_{i: j in S_i} B_i
-__global__ void k_colt_offsets(int n, int nch, int64_t g0, int32_t* __restrict__ chunk_cnt,
-                               const int32_t* __restrict__ chunk_cost,
-                               const uint8_t* __restrict__ blk_shape,
-                               int32_t* __restrict__ colt_cnt, int64_t* __restrict__ colt_cost) {
-  int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n) return;
-  int32_t run = 0;
+// column's total, and its cost B_j * sum_{i: j in S_i} B_i.  64 columns per
+// work-group, four threads per column, each over a quarter of the row tiles.
+__global__ __launch_bounds__(256) void k_colt_offsets(int n, int nch, int64_t g0,
+                                                      int32_t* __restrict__ chunk_cnt,
+                                                      const int32_t* __restrict__ chunk_cost,
+                                                      const uint8_t* __restrict__ blk_shape,
+                                                      int32_t* __restrict__ colt_cnt,
+                                                      int64_t* __restrict__ colt_cost) {
+  __shared__ int32_t part[4][64];
+  __shared__ int64_t pcost[4][64];
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + c;
+  const int r0 = q * nch / 4, r1 = (q + 1) * nch / 4;
+  int32_t s = 0;
   int64_t cost = 0;
-  for (int c = 0; c < nch; c++) {
-    int32_t t = chunk_cnt[(int64_t)c * n + j];
-    chunk_cnt[(int64_t)c * n + j] = run;
+  if (j < n)
+    for (int r = r0; r < r1; r++) {
+      s += chunk_cnt[(int64_t)r * n + j];
+      cost += chunk_cost[(int64_t)r * n + j];
+    }
+  part[q][c] = s;
+  pcost[q][c] = cost;
+  __syncthreads();
+  int32_t run = 0;
+  for (int k = 0; k < q; k++) run += part[k][c];
+  if (j >= n) return;
+  for (int r = r0; r < r1; r++) {
+    const int32_t t = chunk_cnt[(int64_t)r * n + j];
+    chunk_cnt[(int64_t)r * n + j] = run;
     run += t;
-    cost += chunk_cost[(int64_t)c * n + j];
   }
-  colt_cnt[g0 + j] = run;
-  colt_cost[g0 + j] = cost * (int64_t)volume_of_id(block_shape_at(blk_shape, g0 + j));
+  if (q == 3) {
+    colt_cnt[g0 + j] = run;
+    const int64_t tc = pcost[0][c] + pcost[1][c] + pcost[2][c] + pcost[3][c];
+    colt_cost[g0 + j] = tc * (int64_t)volume_of_id(block_shape_at(blk_shape, g0 + j));
+  }
 }
 
 // key-major scan: counts per column -> pointers (reuses k_scan_rows on colt_cnt)
@@ -2059,7 +2089,7 @@ bool launch_transpose(const PlanDev& P, int64_t g0, int n, int last, hipStream_t
   const dim3 grid((unsigned)wd, (unsigned)((wd + 4 * kMtWords - 1) / (4 * kMtWords)));
   hipLaunchKernelGGL(k_mask_tr<false>, grid, dim3(256), 0, st, P.selmask, wd, n, g0, P.volm,
                      P.colt_ptr, P.chunk_cnt, P.chunk_cost, P.cap, P.colt_idx);
-  hipLaunchKernelGGL(k_colt_offsets, dim3((n + 255) / 256), dim3(256), 0, st, n, wd, g0,
+  hipLaunchKernelGGL(k_colt_offsets, dim3((n + 63) / 64), dim3(256), 0, st, n, wd, g0,
                      P.chunk_cnt, P.chunk_cost, P.blk_shape, P.colt_cnt, P.colt_cost);
   hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(1024), 0, st, P.colt_cnt, n, g0, P.colt_ptr,
                      P.counters + 1, last);
