@@ -484,7 +484,7 @@ def main():
                        os.path.join(ROOT, "profiles", f"attention_{args.workload}_mfma.md"))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     import torch
