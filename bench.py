@@ -357,6 +357,12 @@ def parse():
     ap.add_argument("--summarize-stalls", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"),
                     help="write where the attention kernels' wave time goes from two SQ "
                          "counter passes, then exit")
+    ap.add_argument("--upstream", action="store_true",
+                    help="measure the two steps upstream of the plan at the workload's grid "
+                         "instead (the A->V norm producer and the shot-cut detection), print "
+                         "their JSON line and exit")
+    ap.add_argument("--trace-name", default=None,
+                    help="summary name for --summarize-trace (default <workload>_kernel_trace)")
     ap.add_argument("--cmd", action="append", default=[],
                     help="profiling command lines to record in the summary")
     return ap.parse_args()
@@ -463,6 +469,72 @@ def cpu_baseline(wl, x, nblocks, threads, step_flops):
                                        "forward rate (an extrapolation, not a measurement)"}
 
 
+def upstream(wl, dev, n_audio=512, reps=3):
+    """The two steps upstream of the plan, on the workload's grid:
+    * the A->V norm producer (prism_av_cross_attn): dense cross-attention of
+      the video queries over n_audio audio keys and values per head, with the
+      per-token norm over heads and channels in the epilogue; 4 D N N_a flop
+      per head against the bf16 MFMA peak, and its algorithmic bytes (Q read,
+      norm written, K_a and V_a read once) against the HBM peak;
+    * shot-cut detection (frame differences of V, per-zone caps): the plan's
+      statistics stage with and without it, so the difference is the
+      detection's own time; algorithmic bytes 2 reads of V.
+    Median of `reps` runs each, HIP events on the stream the library
+    launches on (torch's current stream)."""
+    import statistics
+
+    import torch
+
+    import dynamic_block_sparse_zone_amd as prism
+    from dynamic_block_sparse_zone_amd import synth
+
+    x = synth.make_inputs(wl, device=dev, with_grad=False)
+    a = synth.make_audio(wl, n_audio, device=dev)
+    H_, N, D = x["q"].shape
+    norm = torch.empty(N, dtype=torch.float32, device=dev)
+    prism.av_cross_attn(x["q"], a["ka"], a["va"], norm=norm)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        prism.av_cross_attn(x["q"], a["ka"], a["va"], norm=norm)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    t_av = statistics.median(ms)
+    flops = 4.0 * D * N * n_audio * H_
+    av_bytes = H_ * N * D * 2 + N * 4 + 2 * H_ * n_audio * D * 2
+    kw = dict(T=wl.T, H=wl.H, W=wl.W, top_k=wl.top_k, top_p=wl.top_p,
+              top_k_frac=wl.top_k_frac, volume_mask=wl.volume_mask,
+              fixed_shape=tuple(wl.fixed_shape), need_backward=False)
+    stats = {}
+    for thr in (0.0, 4.0, 0.0, 4.0, 0.0, 4.0):
+        prism.timing_enable(True)
+        prism.timing_read()
+        pl = prism.plan(x["q"], x["k"], x["v"], norm, cut_threshold=thr, **kw)
+        torch.cuda.synchronize()
+        st = prism.timing_read()
+        prism.timing_enable(False)
+        # (a plan without a pair capacity runs its stages twice: a counting
+        # pass, then the pass that fills the lists)
+        stats.setdefault(thr, []).append(st["plan.stats"][1] / st["plan.stats"][0])
+        pl.close()
+    t_cut = statistics.median(stats[4.0]) - statistics.median(stats[0.0])
+    cut_bytes = 2 * H_ * N * D * 2
+    return {"metric": "upstream kernels", "workload": wl.name, "n_audio": n_audio,
+            "av_norm": {"ms": round(t_av, 3), "tflops": round(flops / (t_av * 1e-3) / 1e12, 1),
+                        "frac_bf16_peak": round(flops / (t_av * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "bytes": av_bytes, "tbs": round(av_bytes / (t_av * 1e-3) / 1e12, 3),
+                        "runs_ms": [round(v, 3) for v in ms]},
+            "cuts": {"ms": round(t_cut, 3), "bytes": cut_bytes,
+                     "tbs": round(cut_bytes / (t_cut * 1e-3) / 1e12, 3) if t_cut > 0 else None,
+                     "frac_hbm_peak": round(cut_bytes / (t_cut * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                     if t_cut > 0 else None,
+                     "stats_stage_ms": {"without": [round(v, 3) for v in stats[0.0]],
+                                        "with": [round(v, 3) for v in stats[4.0]]}}}
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -472,8 +544,9 @@ def main():
                             os.path.join(ROOT, "profiles", f"kernels_{args.workload}_hbm.md"))
         return
     if args.summarize_trace:
+        name = args.trace_name or f"{args.workload}_kernel_trace"
         summarize_trace(args.summarize_trace, args.workload, args.cmd,
-                        os.path.join(ROOT, "profiles", f"{args.workload}_kernel_trace.md"))
+                        os.path.join(ROOT, "profiles", f"{name}.md"))
         return
     if args.summarize_stalls:
         summarize_stalls(*args.summarize_stalls, args.workload, args.cmd,
@@ -494,6 +567,9 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.upstream:
+        print(json.dumps(upstream(wl, dev)), flush=True)
+        return
     t0 = time.time()
     x = synth.make_inputs(wl, device=dev, with_grad=not args.fwd_only)
     torch.cuda.synchronize()

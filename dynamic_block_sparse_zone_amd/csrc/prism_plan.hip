@@ -733,63 +733,93 @@ __global__ __launch_bounds__(512) void k_relayout(
 // the integer dot products I_hh = hi.hi, I_x = hi_i.lo_j + lo_i.hi_j and
 // I_ll = lo.lo are exact on the bf16 MFMA (every partial sum is an integer
 // below 2^24), J = 2^16 I_hh + 2^8 I_x + I_ll is formed exactly (in fp64),
-// and s = fl32(fl32(J) 2^(Ei + Ej - 16)) * fl(1/sqrt D), J rounded once.  A block of 256 threads covers 128 x 128 scores, each wave
-// 64 x 64 as two 32-row halves.
+// and s = fl32(fl32(J) 2^(Ei + Ej - 16)) * fl(1/sqrt D), J rounded once.
+// A work-group of four waves covers 128 x 128 scores: the hi and lo grids of
+// its 128 key blocks are staged once in LDS (16-byte chunks swizzled by row,
+// so that 16 consecutive rows read at one chunk touch distinct banks), and
+// each wave holds its 32 query blocks' fragments in registers and walks the
+// four 32-key tiles.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_block_scores(
+__global__ __launch_bounds__(256, 2) void k_block_scores(
     const uint16_t* __restrict__ qgrid, const uint16_t* __restrict__ kgrid,
     const uint16_t* __restrict__ qlo, const uint16_t* __restrict__ klo,
     const int32_t* __restrict__ qexp, const int32_t* __restrict__ kexp, int64_t g0, int n,
     float cD, float* __restrict__ scores) {
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i0 = blockIdx.y * 128 + (wv >> 1) * 64;
-  const int j0 = blockIdx.x * 128 + (wv & 1) * 64;
+  constexpr int C = D / 8;    // 16-byte chunks per row
+  constexpr int KK = D / 16;  // MFMA steps over the channels
+  __shared__ uint4 ksh[128 * C], ksl[128 * C];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int hl = lane >> 5, l32 = lane & 31;
-  auto frag = [&](const uint16_t* base, int row, int kk) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (row < n) u = *(const uint4*)(base + (g0 + row) * D + kk * 16 + hl * 8);
-    return __builtin_bit_cast(bf16x8, u);
-  };
-  // one 32 x 32 tile at a time (48 accumulator registers, so that four waves
-  // fit a SIMD; the tile's Q and K fragments come from L2)
+  const int j0 = blockIdx.x * 128, i0 = blockIdx.y * 128 + wv * 32;
+  for (int idx = tid; idx < 128 * C; idx += 256) {
+    const int r = idx / C, c = idx % C;
+    uint4 vh = make_uint4(0, 0, 0, 0), vl = vh;
+    if (j0 + r < n) {
+      vh = *(const uint4*)(kgrid + (g0 + j0 + r) * D + c * 8);
+      vl = *(const uint4*)(klo + (g0 + j0 + r) * D + c * 8);
+    }
+    const int pc = r * C + (c ^ (r & (C - 1)));
+    ksh[pc] = vh;
+    ksl[pc] = vl;
+  }
+  // this wave's query blocks as MFMA A operands (row l32, channels
+  // 16kk + 8hl .. + 7) and the exponents of the rows this lane's outputs hold
+  const int ia = i0 + l32;
+  bf16x8 qh[KK], ql[KK];
 #pragma unroll
-  for (int a = 0; a < 2; a++)
+  for (int kk = 0; kk < KK; kk++) {
+    uint4 uh = make_uint4(0, 0, 0, 0), ul = uh;
+    if (ia < n) {
+      uh = *(const uint4*)(qgrid + (g0 + ia) * D + kk * 16 + hl * 8);
+      ul = *(const uint4*)(qlo + (g0 + ia) * D + kk * 16 + hl * 8);
+    }
+    qh[kk] = __builtin_bit_cast(bf16x8, uh);
+    ql[kk] = __builtin_bit_cast(bf16x8, ul);
+  }
+  int qe[16];
 #pragma unroll
-    for (int b = 0; b < 2; b++) {
-      f32x16 hh, hx, ll;
+  for (int r = 0; r < 16; r++) {
+    const int i = i0 + (r >> 2) * 8 + hl * 4 + (r & 3);
+    qe[r] = i < n ? qexp[g0 + i] : 0;
+  }
+  __syncthreads();
+  if (i0 >= n) return;
+  for (int b = 0; b < 4 && j0 + 32 * b < n; b++) {
+    const int jr = 32 * b + l32;  // the lane's key row in the staged tile
+    f32x16 hh, hx, ll;
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        hh[r] = 0.0f;
-        hx[r] = 0.0f;
-        ll[r] = 0.0f;
-      }
-      const int ia = i0 + a * 32 + l32, jb = j0 + b * 32 + l32;
+    for (int r = 0; r < 16; r++) {
+      hh[r] = 0.0f;
+      hx[r] = 0.0f;
+      ll[r] = 0.0f;
+    }
 #pragma unroll
-      for (int kk = 0; kk < D / 16; kk++) {
-        const bf16x8 qh = frag(qgrid, ia, kk), ql = frag(qlo, ia, kk);
-        const bf16x8 kh = frag(kgrid, jb, kk), kl = frag(klo, jb, kk);
-        hh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kh, hh, 0, 0, 0);
-        hx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kl, hx, 0, 0, 0);
-        hx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kh, hx, 0, 0, 0);
-        ll = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kl, ll, 0, 0, 0);
-      }
-      if (jb >= n) continue;
-      const int j = jb;
-      const int ej = kexp[g0 + j];
+    for (int kk = 0; kk < KK; kk++) {
+      const int pc = jr * C + ((2 * kk + hl) ^ (jr & (C - 1)));
+      const bf16x8 kh = __builtin_bit_cast(bf16x8, ksh[pc]);
+      const bf16x8 kl = __builtin_bit_cast(bf16x8, ksl[pc]);
+      hh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kh, hh, 0, 0, 0);
+      hx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[kk], kl, hx, 0, 0, 0);
+      hx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[kk], kh, hx, 0, 0, 0);
+      ll = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[kk], kl, ll, 0, 0, 0);
+    }
+    const int j = j0 + jr;
+    if (j >= n) continue;
+    const int ej = kexp[g0 + j];
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int i = i0 + a * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-        if (i < n) {
-          // J = 2^16 I_hh + 2^8 I_x + I_ll: each product is an integer below
-          // 2^25 held exactly in fp32, and |J| < 2^42, so the fp64 sum is J
-          // exactly and is rounded once to fp32
-          const double J = __builtin_fma((double)hh[r], 65536.0,
-                                         __builtin_fma((double)hx[r], 256.0, (double)ll[r]));
-          const float s = ldexpf((float)J, qexp[g0 + i] + ej - 16) * cD;
-          scores[(int64_t)i * n + j] = (s == 0.0f) ? 0.0f : s;
-        }
+    for (int r = 0; r < 16; r++) {
+      const int i = i0 + (r >> 2) * 8 + hl * 4 + (r & 3);
+      if (i < n) {
+        // J = 2^16 I_hh + 2^8 I_x + I_ll: each product is an integer below
+        // 2^25 held exactly in fp32, and |J| < 2^42, so the fp64 sum is J
+        // exactly and is rounded once to fp32
+        const double J = __builtin_fma((double)hh[r], 65536.0,
+                                       __builtin_fma((double)hx[r], 256.0, (double)ll[r]));
+        const float s = ldexpf((float)J, qe[r] + ej - 16) * cD;
+        scores[(int64_t)i * n + j] = (s == 0.0f) ? 0.0f : s;
       }
     }
+  }
 }
 
 // ============================================================ K6: selection
@@ -1896,8 +1926,14 @@ bool launch_sum_i64(const int64_t* in, int64_t n, int64_t* out, hipStream_t st) 
 // the zone, at least 2; 8 without a cut).
 //
 // One block of 256 threads per (frame t >= 1, head): frame t of head h is
-// the contiguous run of H*W*D elements at (h*N + t*H*W)*D.  fp64; each
-// thread sums a fixed strided set of elements in order, then a fixed tree.
+// the contiguous run of H*W*D elements at (h*N + t*H*W)*D.  Each thread reads
+// both frames in 16-byte vectors (a fixed strided set of them) and keeps four
+// fp64 partial sums, element e of a vector going to sum e % 4, in order; then
+// the four in order and a fixed tree over the threads.
+__device__ inline void energy_add(double (&s)[4], int k, float a, float b) {
+  const double d = (double)a - (double)b;
+  s[k] = s[k] + d * d;
+}
 template <int DT>
 __global__ __launch_bounds__(256) void k_frame_energy(const void* __restrict__ v, int64_t N,
                                                       int64_t HW, int D, int heads,
@@ -1906,20 +1942,37 @@ __global__ __launch_bounds__(256) void k_frame_energy(const void* __restrict__ v
   const int t = blockIdx.x + 1, h = blockIdx.y;
   const int64_t fe = HW * D;
   const int64_t cur = ((int64_t)h * N + (int64_t)t * HW) * D;
-  double s = 0.0;
-  for (int64_t i = threadIdx.x; i < fe; i += 256) {
-    double a, b;
-    if (DT == 1) {
-      a = (double)bf16_to_f32(((const uint16_t*)v)[cur + i]);
-      b = (double)bf16_to_f32(((const uint16_t*)v)[cur - fe + i]);
-    } else {
-      a = (double)((const float*)v)[cur + i];
-      b = (double)((const float*)v)[cur - fe + i];
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  if (DT == 1) {
+    // D is a multiple of 8, so each frame is a whole number of 16-byte vectors
+    const uint4* pa = (const uint4*)((const uint16_t*)v + cur);
+    const uint4* pb = (const uint4*)((const uint16_t*)v + cur - fe);
+    const int64_t nv = fe / 8;
+#pragma unroll 4
+    for (int64_t i = threadIdx.x; i < nv; i += 256) {
+      const uint4 x = pa[i], y = pb[i];
+      const uint32_t xa[4] = {x.x, x.y, x.z, x.w}, ya[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        energy_add(s, (2 * q) & 3, __uint_as_float(xa[q] << 16), __uint_as_float(ya[q] << 16));
+        energy_add(s, (2 * q + 1) & 3, __uint_as_float(xa[q] & 0xffff0000u),
+                   __uint_as_float(ya[q] & 0xffff0000u));
+      }
     }
-    const double d = a - b;
-    s = s + d * d;
+  } else {
+    const float4* pa = (const float4*)((const float*)v + cur);
+    const float4* pb = (const float4*)((const float*)v + cur - fe);
+    const int64_t nv = fe / 4;
+#pragma unroll 4
+    for (int64_t i = threadIdx.x; i < nv; i += 256) {
+      const float4 x = pa[i], y = pb[i];
+      energy_add(s, 0, x.x, y.x);
+      energy_add(s, 1, x.y, y.y);
+      energy_add(s, 2, x.z, y.z);
+      energy_add(s, 3, x.w, y.w);
+    }
   }
-  red[threadIdx.x] = s;
+  red[threadIdx.x] = ((s[0] + s[1]) + s[2]) + s[3];
   __syncthreads();
   for (int w = 128; w >= 1; w >>= 1) {
     if (threadIdx.x < w) red[threadIdx.x] = red[threadIdx.x] + red[threadIdx.x + w];

@@ -158,6 +158,22 @@ def test_block_scores_bit_exact(prism, orc):
             np.testing.assert_array_equal(s[i], orc.score_row(opl, h, int(i)))
 
 
+@pytest.mark.parametrize("name", ["check", "small"])
+def test_block_scores_every_row(prism, orc, name):
+    """Every score of one head (a block count that is not a multiple of the
+    kernel's 128 x 128 tiles, so the ragged last tiles are covered) equals
+    the oracle's row bit for bit."""
+    wl, pl, opl = _case(prism, orc, name)
+    h = wl.heads - 1
+    s = prism.block_scores(pl, h).cpu().numpy()
+    n = opl.nblk(h)
+    assert s.shape == (n, n)
+    if name == "small":
+        assert n % 128 != 0, n
+    for i in range(n):
+        np.testing.assert_array_equal(s[i], orc.score_row(opl, h, i))
+
+
 def test_plan_deterministic(prism):
     wl = synth.WORKLOADS["small"]
     dx = to_dev(synth.make_inputs(wl, device="cpu", with_grad=False), DEV)
