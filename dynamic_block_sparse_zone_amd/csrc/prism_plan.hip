@@ -1981,20 +1981,24 @@ __global__ __launch_bounds__(256) void k_frame_energy(const void* __restrict__ v
   if (threadIdx.x == 0) part[(int64_t)t * heads + h] = red[0];
 }
 
-// One thread: heads summed in order, the mean over frames, the cut
-// decisions and the per-row caps.
-__global__ void k_cuts(const double* __restrict__ part, int T, int heads, double denom,
-                       float kappa, double* __restrict__ energy, uint8_t* __restrict__ cuts,
-                       int32_t* __restrict__ zt_cap) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  double mean = 0.0;
-  energy[0] = 0.0;
-  for (int t = 1; t < T; t++) {
+// One block: thread t sums frame t's heads in order (frames t, t + 256, ...),
+// then thread 0 takes the mean over frames, the cut decisions and the
+// per-row caps.
+__global__ __launch_bounds__(256) void k_cuts(const double* __restrict__ part, int T, int heads,
+                                              double denom, float kappa,
+                                              double* __restrict__ energy,
+                                              uint8_t* __restrict__ cuts,
+                                              int32_t* __restrict__ zt_cap) {
+  for (int t = threadIdx.x; t < T; t += blockDim.x) {
     double e = 0.0;
-    for (int h = 0; h < heads; h++) e = e + part[(int64_t)t * heads + h];
+    if (t > 0)
+      for (int h = 0; h < heads; h++) e = e + part[(int64_t)t * heads + h];
     energy[t] = e / denom;
-    mean = mean + energy[t];
   }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  double mean = 0.0;
+  for (int t = 1; t < T; t++) mean = mean + energy[t];
   mean = T > 1 ? mean / (double)(T - 1) : 0.0;
   cuts[0] = 0;
   for (int t = 1; t < T; t++) cuts[t] = (kappa > 0.0f && energy[t] > (double)kappa * mean) ? 1 : 0;
@@ -2022,7 +2026,7 @@ bool launch_cuts(const PlanDev& P, const void* v, float kappa, hipStream_t st) {
                          P.cut_part);
   }
   const double denom = ((double)P.heads * (double)HW) * (double)P.D;
-  hipLaunchKernelGGL(k_cuts, dim3(1), dim3(64), 0, st, P.cut_part, P.T, P.heads, denom, kappa,
+  hipLaunchKernelGGL(k_cuts, dim3(1), dim3(256), 0, st, P.cut_part, P.T, P.heads, denom, kappa,
                      P.cut_energy, P.cuts, P.zt_cap);
   return hipGetLastError() == hipSuccess;
 }
