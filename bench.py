@@ -222,7 +222,19 @@ def summarize_mfma(csv_path, agent_csv, workload, cmds, out):
     print("\n".join(lines))
 
 
-def summarize_trace(db, workload, cmds, out):
+TRACE_WHAT = {
+    "step": "rocprofv3 `--kernel-trace --stats` over one bench step (after the small-grid "
+            "warm-up); durations from the trace's rocpd database.  The longest dispatch of "
+            "each attention kernel is the full-size one.",
+    "upstream": "rocprofv3 `--kernel-trace --stats` over `bench.py --upstream`: the A->V norm "
+                "producer (one warm-up call, three timed) and six plans without the backward "
+                "lists, three with shot-cut detection and three without (each plan runs its "
+                "stages twice: a counting pass, then the pass that fills the lists); durations "
+                "from the trace's rocpd database.",
+}
+
+
+def summarize_trace(db, workload, cmds, out, what="step"):
     """Per-kernel summary of a rocprofv3 --kernel-trace run (its rocpd
     SQLite output): the library's kernels with dispatch count, total and
     average duration, the longest dispatch and its launch shape."""
@@ -245,10 +257,8 @@ def summarize_trace(db, workload, cmds, out):
             a["max"] = dur
             a["shape"] = (gx, gy, wx, vg, ag, lds)
     total = sum(a["tot"] for a in agg.values())
-    lines = [f"# Kernel trace, {workload}", "",
-             "rocprofv3 `--kernel-trace --stats` over one bench step (after the small-grid "
-             "warm-up); durations from the trace's rocpd database.  The longest dispatch of "
-             "each attention kernel is the full-size one.", "",
+    lines = [f"# Kernel trace, {workload}" + ("" if what == "step" else f" ({what})"), "",
+             TRACE_WHAT[what], "",
              "Command (from /tmp, TMPDIR=/tmp):", "", *[f"    {c}" for c in cmds], "",
              "| kernel | dispatches | total ms | average ms | longest ms | % of library time | "
              "grid (x, y) | threads | VGPR | AGPR | LDS B |",
@@ -363,6 +373,8 @@ def parse():
                          "their JSON line and exit")
     ap.add_argument("--trace-name", default=None,
                     help="summary name for --summarize-trace (default <workload>_kernel_trace)")
+    ap.add_argument("--trace-what", default="step", choices=sorted(TRACE_WHAT),
+                    help="what the traced command ran: one bench step, or --upstream")
     ap.add_argument("--cmd", action="append", default=[],
                     help="profiling command lines to record in the summary")
     return ap.parse_args()
@@ -478,7 +490,8 @@ def upstream(wl, dev, n_audio=512, reps=3):
       norm written, K_a and V_a read once) against the HBM peak;
     * shot-cut detection (frame differences of V, per-zone caps): the plan's
       statistics stage with and without it, so the difference is the
-      detection's own time; algorithmic bytes 2 reads of V.
+      detection's own time; algorithmic bytes V once (each frame enters two
+      differences; the bytes the kernel issues, two reads of V, beside it).
     Median of `reps` runs each, HIP events on the stream the library
     launches on (torch's current stream)."""
     import statistics
@@ -521,13 +534,13 @@ def upstream(wl, dev, n_audio=512, reps=3):
         stats.setdefault(thr, []).append(st["plan.stats"][1] / st["plan.stats"][0])
         pl.close()
     t_cut = statistics.median(stats[4.0]) - statistics.median(stats[0.0])
-    cut_bytes = 2 * H_ * N * D * 2
+    cut_bytes = H_ * N * D * 2
     return {"metric": "upstream kernels", "workload": wl.name, "n_audio": n_audio,
             "av_norm": {"ms": round(t_av, 3), "tflops": round(flops / (t_av * 1e-3) / 1e12, 1),
                         "frac_bf16_peak": round(flops / (t_av * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                         "bytes": av_bytes, "tbs": round(av_bytes / (t_av * 1e-3) / 1e12, 3),
                         "runs_ms": [round(v, 3) for v in ms]},
-            "cuts": {"ms": round(t_cut, 3), "bytes": cut_bytes,
+            "cuts": {"ms": round(t_cut, 3), "bytes": cut_bytes, "issued_bytes": 2 * cut_bytes,
                      "tbs": round(cut_bytes / (t_cut * 1e-3) / 1e12, 3) if t_cut > 0 else None,
                      "frac_hbm_peak": round(cut_bytes / (t_cut * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
                      if t_cut > 0 else None,
@@ -546,7 +559,7 @@ def main():
     if args.summarize_trace:
         name = args.trace_name or f"{args.workload}_kernel_trace"
         summarize_trace(args.summarize_trace, args.workload, args.cmd,
-                        os.path.join(ROOT, "profiles", f"{name}.md"))
+                        os.path.join(ROOT, "profiles", f"{name}.md"), args.trace_what)
         return
     if args.summarize_stalls:
         summarize_stalls(*args.summarize_stalls, args.workload, args.cmd,

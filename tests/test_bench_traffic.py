@@ -156,3 +156,37 @@ def test_wave_utilisation_counts_idle_waves():
         heads = 1
 
     assert bench.wave_utilisation(FakePlan(), Wl(), (0,)) == {0: 0.5}
+
+
+def test_trace_summary_groups_the_librarys_kernels(tmp_path):
+    """The kernel-trace summary reads the rocpd database's kernels view:
+    the library's kernels by name (templates kept), their totals, average
+    and longest dispatch with its launch shape; everything else counted
+    apart; the header says what the traced command ran."""
+    import sqlite3
+    db = tmp_path / "run_results.db"
+    con = sqlite3.connect(db)
+    con.execute("create table kernels (name text, duration integer, grid_x integer, "
+                "grid_y integer, workgroup_x integer, vgpr_count integer, "
+                "accum_vgpr_count integer, lds_size integer)")
+    rows = [("void prism::k_frame_energy<1>(void const*, long)", 3_000_000, 18176, 40, 256, 28,
+             0, 2048),
+            ("void prism::k_frame_energy<1>(void const*, long)", 5_000_000, 18176, 40, 256, 28,
+             0, 2048),
+            ("prism::k_cuts(double const*, int)", 20_000, 256, 1, 256, 8, 0, 0),
+            ("at::native::elementwise_kernel", 7_000_000, 1, 1, 64, 4, 0, 0)]
+    con.executemany("insert into kernels values (?, ?, ?, ?, ?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    out = tmp_path / "trace.md"
+    bench.summarize_trace(str(db), "train2k", ["cmd one"], str(out), "upstream")
+    text = out.read_text()
+    assert text.startswith("# Kernel trace, train2k (upstream)")
+    assert bench.TRACE_WHAT["upstream"] in text
+    fe = [l for l in text.splitlines() if l.startswith("| `k_frame_energy<1>`")]
+    assert len(fe) == 1
+    cells = [c.strip() for c in fe[0].strip("|").split("|")]
+    assert cells[1:5] == ["2", "8.000", "4.000", "5.000"]
+    assert "Other (input generation, torch) kernels: 1 dispatches, 7.0 ms." in text
+    # the kernels' order: by total time
+    assert text.index("k_frame_energy") < text.index("k_cuts")
