@@ -493,7 +493,8 @@ def upstream(wl, dev, n_audio=512, reps=3):
       detection's own time; algorithmic bytes V once (each frame enters two
       differences; the bytes the kernel issues, two reads of V, beside it).
     Median of `reps` runs each, HIP events on the stream the library
-    launches on (torch's current stream)."""
+    launches on (torch's current stream).  Returns the figures and the
+    inputs (for the oracle's leg)."""
     import statistics
 
     import torch
@@ -535,7 +536,7 @@ def upstream(wl, dev, n_audio=512, reps=3):
         pl.close()
     t_cut = statistics.median(stats[4.0]) - statistics.median(stats[0.0])
     cut_bytes = H_ * N * D * 2
-    return {"metric": "upstream kernels", "workload": wl.name, "n_audio": n_audio,
+    return ({"metric": "upstream kernels", "workload": wl.name, "n_audio": n_audio,
             "av_norm": {"ms": round(t_av, 3), "tflops": round(flops / (t_av * 1e-3) / 1e12, 1),
                         "frac_bf16_peak": round(flops / (t_av * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                         "bytes": av_bytes, "tbs": round(av_bytes / (t_av * 1e-3) / 1e12, 3),
@@ -545,7 +546,45 @@ def upstream(wl, dev, n_audio=512, reps=3):
                      "frac_hbm_peak": round(cut_bytes / (t_cut * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
                      if t_cut > 0 else None,
                      "stats_stage_ms": {"without": [round(v, 3) for v in stats[0.0]],
-                                        "with": [round(v, 3) for v in stats[4.0]]}}}
+                                        "with": [round(v, 3) for v in stats[4.0]]}}},
+            (x, a))
+
+
+def upstream_cpu(x, a, wl, threads, av_tokens=8192, cut_heads=8):
+    """The oracle as it is beside the two upstream kernels, on bounded
+    samples: the A->V norm of `av_tokens` random tokens over all heads
+    (fp64), and the shot-cut energies of `cut_heads` heads (fp64 over every
+    frame)."""
+    import numpy as np
+    import torch
+
+    from dynamic_block_sparse_zone_amd import synth
+    from oracle import oracle as O
+
+    H_, N, D = x["q"].shape
+    n_audio = a["ka"].shape[1]
+    av_tokens, cut_heads = min(av_tokens, N), min(cut_heads, H_)
+    toks = np.sort(np.random.default_rng(5).choice(N, av_tokens, replace=False))
+    qs = synth.to_numpy_bits(x["q"][:, torch.from_numpy(toks).to(x["q"].device)])
+    ka, va = synth.to_numpy_bits(a["ka"]), synth.to_numpy_bits(a["va"])
+    t0 = time.perf_counter()
+    O.av_cross(qs, ka, va, np.arange(av_tokens))
+    t_av = time.perf_counter() - t0
+    av_flops = 4.0 * D * av_tokens * n_audio * H_
+    v = synth.to_numpy_bits(x["v"][:cut_heads])
+    cfg = O.Config(wl.T, wl.H, wl.W, cut_heads, D, cut_threshold=4.0)
+    t0 = time.perf_counter()
+    O.detect_cuts(v, cfg)
+    t_cut = time.perf_counter() - t0
+    cut_bytes = cut_heads * N * D * 2
+    return {"av_norm": {"value": round(av_flops / t_av / 1e12, 6), "unit": "TFLOP/s",
+                        "cores": min(threads, av_tokens), "kind": "oracle",
+                        "sample": f"fp64 oracle A->V norm of {av_tokens} random tokens over "
+                                  f"{H_} heads and {n_audio} audio tokens, {t_av:.1f} s"},
+            "cuts": {"value": round(cut_bytes / t_cut / 1e9, 3), "unit": "GB/s of V",
+                     "cores": min(threads, wl.T - 1), "kind": "oracle",
+                     "sample": f"fp64 oracle frame-difference energies of {cut_heads} of "
+                               f"{H_} heads, every frame, {t_cut:.1f} s"}}
 
 
 def main():
@@ -581,7 +620,11 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     if args.upstream:
-        print(json.dumps(upstream(wl, dev)), flush=True)
+        res, (x, a) = upstream(wl, dev)
+        if not args.no_cpu:
+            threads = int(os.environ.get("OMP_NUM_THREADS", 0) or os.cpu_count() or 1)
+            res["cpu_baseline"] = upstream_cpu(x, a, wl, threads)
+        print(json.dumps(res), flush=True)
         return
     t0 = time.time()
     x = synth.make_inputs(wl, device=dev, with_grad=not args.fwd_only)
