@@ -249,19 +249,30 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void k_attn_fwd_bf16(
 }
 
 // ---------------------------------------------------------------- fp32 path
-// Plain fp32 kernel (small problems, fp32 inputs): one thread per query row,
-// K/V tiles of 64 rows gathered into LDS through the block -> token map,
-// exact expf online softmax.
+// fp32 inputs (small problems): the same online softmax on the fp32 matrix
+// cores (v_mfma_f32_32x32x2_f32).  A work-group of two waves owns the 64
+// rows of one permuted query tile (32 rows per wave, its Q fragments in
+// registers); each 64-key tile of the row's blocks is gathered into LDS
+// through the block -> token map (rows padded by one word, so that the 32
+// lanes reading one channel of 32 keys touch distinct banks); per 32-key
+// half, S = Q K^T, then the row maxima and sums by lane shuffles within
+// each 32-lane half, and O += P V with P passed through LDS into the A
+// operand's layout.  Output layout of a 32 x 32 product: lane l holds column
+// l % 32 of rows 8 (r / 4) + 4 (l / 32) + r % 4, r = 0..15.
 template <int D>
-__global__ __launch_bounds__(64) void k_attn_fwd_f32(
+__global__ __launch_bounds__(128) void k_attn_fwd_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const uint8_t* __restrict__ shape_id, const int32_t* __restrict__ zone_base,
     const int64_t* __restrict__ blk_off, const int32_t* __restrict__ blk_org,
     const uint8_t* __restrict__ blk_shape, const int64_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, int H, int W, int Z, int64_t N, float scale,
     float* __restrict__ o, float* __restrict__ lse) {
-  __shared__ float Ks[64][D], Vs[64][D];
+  constexpr int DP = D + 1;  // padded LDS row
+  constexpr int NB = D / 32;  // 32-channel output blocks
+  __shared__ float Ks[64 * DP], Vs[64 * DP];
+  __shared__ float Ps[2][32 * 33];
   __shared__ int64_t rowtok[64];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int64_t tpH = N >> 6;
   const int h = (int)(blockIdx.x / tpH);
   const int64_t r0 = (blockIdx.x - (int64_t)h * tpH) << 6;
@@ -269,48 +280,96 @@ __global__ __launch_bounds__(64) void k_attn_fwd_f32(
   const Shape sh = d_shapes[shape_id[(int64_t)h * Z + m]];
   const int64_t hoff = blk_off[h];
   const int64_t g = hoff + zone_base[(int64_t)h * Z + m] + (int)(r0 & 511) / sh.volume;
-  const int64_t p = r0 + threadIdx.x;
-  const int64_t tok = token_of(sh, m, (int)(p & 511), H, W);
-  float qv[D], ov[D];
-  for (int c = 0; c < D; c++) {
-    qv[c] = q[((int64_t)h * N + tok) * D + c];
-    ov[c] = 0.0f;
+  // this wave's query rows as A operands: lane l holds row l % 32, channel
+  // 2 kk + l / 32 of step kk
+  const int64_t qtok = token_of(sh, m, (int)((r0 + 32 * wv + l32) & 511), H, W);
+  float qa[D / 2];
+#pragma unroll
+  for (int kk = 0; kk < D / 2; kk++) qa[kk] = q[((int64_t)h * N + qtok) * D + 2 * kk + hl];
+  f32x16 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[nb][r] = 0.0f;
+  // running maximum and sum of the rows this lane's registers hold
+  float mrun[16], lrun[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    mrun[r] = -INFINITY;
+    lrun[r] = 0.0f;
   }
-  float mrun = -INFINITY, lrun = 0.0f;
+  float* ps = Ps[wv];
   for (int64_t e = row_ptr[g]; e < row_ptr[g + 1]; e++) {
-    int j = col_idx[e];
+    const int j = col_idx[e];
     const uint32_t org = (uint32_t)blk_org[hoff + j];
     const int sid = block_shape_at(blk_shape, hoff + j);
-    int nt = d_shapes[sid].volume >> 6;
+    const int nt = d_shapes[sid].volume >> 6;
     for (int t = 0; t < nt; t++) {
+      __syncthreads();  // the previous tile's readers are done
+      if (tid < 64) rowtok[tid] = (int64_t)h * N + org + block_row_offset(sid, 64u * t + tid, H, W);
       __syncthreads();
-      rowtok[threadIdx.x] =
-          (int64_t)h * N + org + block_row_offset(sid, 64u * t + threadIdx.x, H, W);
-      __syncthreads();
-      for (int i = threadIdx.x; i < 64 * D; i += 64) {
-        Ks[i / D][i % D] = k[rowtok[i / D] * D + i % D];
-        Vs[i / D][i % D] = v[rowtok[i / D] * D + i % D];
+      for (int i = tid; i < 64 * D; i += 128) {
+        const int r = i / D, c = i % D;
+        Ks[r * DP + c] = k[rowtok[r] * D + c];
+        Vs[r * DP + c] = v[rowtok[r] * D + c];
       }
       __syncthreads();
-      for (int r = 0; r < 64; r++) {
-        float s = 0.0f;
-        for (int c = 0; c < D; c++) s = __builtin_fmaf(qv[c], Ks[r][c], s);
-        s *= scale;
-        if (s > mrun) {
-          float a = expf(mrun - s);
-          lrun *= a;
-          for (int c = 0; c < D; c++) ov[c] *= a;
-          mrun = s;
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++) {
+        // S = Q K^T over keys 32 kb .. 32 kb + 31: B operand lane l holds
+        // key 32 kb + l % 32, channel 2 kk + l / 32
+        f32x16 sc;
+#pragma unroll
+        for (int r = 0; r < 16; r++) sc[r] = 0.0f;
+        const float* kr = Ks + (32 * kb + l32) * DP + hl;
+#pragma unroll
+        for (int kk = 0; kk < D / 2; kk++)
+          sc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[kk], kr[2 * kk], sc, 0, 0, 0);
+        // online softmax per row: maxima and sums over the 32 lanes of a half
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const float sv = sc[r] * scale;
+          float mx = sv;
+#pragma unroll
+          for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+          const float mnew = fmaxf(mrun[r], mx);
+          const float alpha = mrun[r] == -INFINITY ? 0.0f : expf(mrun[r] - mnew);
+          const float pv = expf(sv - mnew);
+          float sum = pv;
+#pragma unroll
+          for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+          lrun[r] = lrun[r] * alpha + sum;
+          mrun[r] = mnew;
+#pragma unroll
+          for (int nb = 0; nb < NB; nb++) acc[nb][r] *= alpha;
+          ps[(8 * (r >> 2) + 4 * hl + (r & 3)) * 33 + l32] = pv;
         }
-        float pr = expf(s - mrun);
-        lrun += pr;
-        for (int c = 0; c < D; c++) ov[c] = __builtin_fmaf(pr, Vs[r][c], ov[c]);
+        __syncthreads();
+        // O += P V: A lane l holds row l % 32, key 2 kk + l / 32 of the half;
+        // B lane l holds key 32 kb + 2 kk + l / 32, channel 32 nb + l % 32
+#pragma unroll
+        for (int kk = 0; kk < 16; kk++) {
+          const float pa = ps[l32 * 33 + 2 * kk + hl];
+          const float* vr = Vs + (32 * kb + 2 * kk + hl) * DP + l32;
+#pragma unroll
+          for (int nb = 0; nb < NB; nb++)
+            acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa, vr[32 * nb], acc[nb], 0, 0, 0);
+        }
+        __syncthreads();  // P is rewritten by the next half
       }
     }
   }
-  float inv = lrun > 0.0f ? 1.0f / lrun : 0.0f;
-  for (int c = 0; c < D; c++) o[((int64_t)h * N + tok) * D + c] = ov[c] * inv;
-  lse[(int64_t)h * N + tok] = lrun > 0.0f ? mrun + logf(lrun) : -INFINITY;
+  // rows 8 (r / 4) + 4 hl + r % 4 of this wave's 32; lane l holds channel
+  // 32 nb + l % 32
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    const int i = 8 * (r >> 2) + 4 * hl + (r & 3);
+    const int64_t tok = token_of(sh, m, (int)((r0 + 32 * wv + i) & 511), H, W);
+    const float inv = lrun[r] > 0.0f ? 1.0f / lrun[r] : 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) o[((int64_t)h * N + tok) * D + 32 * nb + l32] = acc[nb][r] * inv;
+    if (l32 == 0) lse[(int64_t)h * N + tok] = lrun[r] > 0.0f ? mrun[r] + logf(lrun[r]) : -INFINITY;
+  }
 }
 
 bool launch_attn_fwd(const PlanDev& P, const void* q, const void* k, const void* v, void* o,
@@ -328,7 +387,7 @@ bool launch_attn_fwd(const PlanDev& P, const void* q, const void* k, const void*
                          P.blk_off, P.blk_org, P.blk_shape, P.row_ptr, P.col_idx, P.H, P.W,
                          P.Z, P.N, c_log2, (uint16_t*)o, lse);
   } else if (P.dtype == PRISM_F32 && (P.D == 64 || P.D == 128)) {
-    dim3 grid((unsigned)(P.heads * (P.N >> 6))), block(64);
+    dim3 grid((unsigned)(P.heads * (P.N >> 6))), block(128);
     float scale = (float)(1.0 / sqrt((double)P.D));
     if (P.D == 64)
       hipLaunchKernelGGL((k_attn_fwd_f32<64>), grid, block, 0, st, (const float*)q,

@@ -18,7 +18,7 @@ def prism():
 
 
 def run_fwd(prism, orc, name, sample=None, seed=0, **over):
-    wl = synth.WORKLOADS[name]
+    wl = synth.WORKLOADS[name] if isinstance(name, str) else name
     print(f"[fwd parity] workload={name} over={over}", flush=True)
     x = synth.make_inputs(wl, device="cpu", with_grad=False)
     dx = to_dev(x, DEV)
@@ -49,6 +49,16 @@ def run_fwd(prism, orc, name, sample=None, seed=0, **over):
 
 def test_fwd_tiny_fp32_full(prism, orc):
     wl, pl, g, r, gl, rl = run_fwd(prism, orc, "tiny")
+    np.testing.assert_allclose(g, r, atol=2e-5, rtol=1e-4)
+    np.testing.assert_allclose(gl, rl, atol=2e-5, rtol=1e-5)
+
+
+def test_fwd_fp32_mixed_volumes_d128(prism, orc):
+    """The fp32 path at head_dim 128 over blocks of all three volumes (the
+    structured check grid in fp32): several 64-key tiles per block and
+    rows whose lists span both halves of a tile."""
+    wl = synth.WORKLOADS["check"].with_(name="check_f32", dtype="f32")
+    wl_, pl, g, r, gl, rl = run_fwd(prism, orc, wl)
     np.testing.assert_allclose(g, r, atol=2e-5, rtol=1e-4)
     np.testing.assert_allclose(gl, rl, atol=2e-5, rtol=1e-5)
 
