@@ -1652,7 +1652,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select_emit(
     const int64_t* __restrict__ row_ptr, int64_t cap, const unsigned long long* __restrict__ volm,
     const uint8_t* __restrict__ blk_shape, int32_t* __restrict__ col_idx,
     int64_t* __restrict__ row_cost) {
-  __shared__ int32_t sout[kSelRegMax];
+  // block indices of a register-path row are below kSelRegMax <= 2^16: 16 bits
+  // each, so that 32 KB of LDS leaves room for four work-groups per CU
+  static_assert(kSelRegMax <= 65536, "16-bit list staging");
+  __shared__ uint16_t sout[kSelRegMax];
   __shared__ int sh[kSelThreads / 64];
   __shared__ int64_t sh_cost[kSelThreads / 64];
   const int i = blockIdx.x, tid = threadIdx.x;
@@ -1662,7 +1665,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_emit(
   int total;
   int pos = block_excl_scan_i32(__popcll(m), sh, &total);
   while (m) {
-    sout[pos++] = 64 * tid + __builtin_ctzll(m);
+    sout[pos++] = (uint16_t)(64 * tid + __builtin_ctzll(m));
     m &= m - 1;
   }
   __syncthreads();
