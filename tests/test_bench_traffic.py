@@ -190,3 +190,18 @@ def test_trace_summary_groups_the_librarys_kernels(tmp_path):
     assert "Other (input generation, torch) kernels: 1 dispatches, 7.0 ms." in text
     # the kernels' order: by total time
     assert text.index("k_frame_energy") < text.index("k_cuts")
+
+
+def test_upstream_oracle_leg_on_a_small_grid():
+    """The oracle's leg beside the upstream kernels runs on host copies of
+    bounded samples and reports a rate for each (CPU tensors stand in for
+    the device ones here)."""
+    from dynamic_block_sparse_zone_amd import synth
+    wl = synth.WORKLOADS["check"]
+    x = synth.make_inputs(wl, device="cpu", with_grad=False)
+    a = synth.make_audio(wl, 64, device="cpu")
+    res = bench.upstream_cpu(x, a, wl, threads=2, av_tokens=256, cut_heads=2)
+    assert res["av_norm"]["kind"] == res["cuts"]["kind"] == "oracle"
+    assert res["av_norm"]["value"] > 0 and res["cuts"]["value"] > 0
+    assert "256 random tokens" in res["av_norm"]["sample"]
+    assert "2 of 3 heads" in res["cuts"]["sample"]
